@@ -1,0 +1,136 @@
+"""Pins for the oracle's NVFP4 and FP8 pack (CPU only).
+
+Hand-worked examples (tests/golden/*_worked_example.txt) pin every step of
+the recipe including ties, saturation inside a block, zero blocks and a
+subnormal block scale; invariants that hold for any input pin the rest.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_quantized_skinny_qpn_amd import synth
+from golden_io import worked_example
+
+
+def _nib(codes_row):
+    out = []
+    for b in codes_row:
+        out += [int(b) & 0xF, int(b) >> 4]
+    return out
+
+
+def test_nvfp4_worked_example():
+    ex = worked_example("nvfp4_worked_example.txt")
+    w = np.array([ex["w"][r] for r in range(3)], dtype=np.float32)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    assert float(g) == ex["g"]
+    for r in range(3):
+        assert list(scales[r]) == ex["scales"][r], r
+        assert _nib(codes[r]) == ex["codes"][r], r
+
+
+def test_fp8_worked_example():
+    ex = worked_example("fp8_worked_example.txt")
+    w = np.array([ex["w"][r] for r in range(2)], dtype=np.float32)
+    codes, rs = oracle.pack_fp8(w)
+    for r in range(2):
+        assert float(rs[r]) == ex["scale"][r]
+        assert list(codes[r]) == ex["codes"][r], r
+
+
+def test_nvfp4_amax_block_gets_top_scale_and_code():
+    w = synth.weights(24, 96, seed=3)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    r, c = np.unravel_index(np.argmax(np.abs(w)), w.shape)
+    assert scales[r, c // 16] == 0x7E
+    nib = _nib(codes[r])[c]
+    assert nib == (0xF if w[r, c] < 0 else 0x7)
+    # every scale byte is a valid UE4M3 byte
+    assert scales.max() <= 0x7E
+
+
+def test_nvfp4_power_of_two_invariance():
+    w = synth.weights(16, 64, seed=5)
+    c0, s0, g0 = oracle.pack_nvfp4(w)
+    for j in (-20, -3, 1, 7, 30):
+        cj, sj, gj = oracle.pack_nvfp4(w * np.float32(2.0 ** j))
+        assert np.array_equal(c0, cj) and np.array_equal(s0, sj)
+        assert float(gj) == float(g0) * 2.0 ** j
+
+
+def test_fp8_power_of_two_invariance():
+    w = synth.weights(16, 64, seed=6)
+    c0, r0 = oracle.pack_fp8(w)
+    for j in (-20, -3, 1, 7, 30):
+        cj, rj = oracle.pack_fp8(w * np.float32(2.0 ** j))
+        assert np.array_equal(c0, cj)
+        assert np.array_equal(rj.astype(np.float64), r0.astype(np.float64) * 2.0 ** j)
+
+
+def test_nvfp4_zero_block_and_zero_tensor():
+    w = synth.weights(4, 64, seed=9)
+    w[1, 16:32] = 0.0
+    w[2, 0:16] = -0.0
+    codes, scales, g = oracle.pack_nvfp4(w)
+    assert scales[1, 1] == 0 and scales[2, 0] == 0
+    assert _nib(codes[1])[16:32] == [0] * 16
+    assert _nib(codes[2])[0:16] == [0] * 16
+    z = np.zeros((3, 32), np.float32)
+    cz, sz, gz = oracle.pack_nvfp4(z)
+    assert float(gz) == 0.0 and not cz.any() and not sz.any()
+
+
+def test_fp8_amax_element_and_zero_row():
+    w = synth.weights(8, 80, seed=11)
+    w[3] = 0.0
+    codes, rs = oracle.pack_fp8(w)
+    assert rs[3] == 0.0 and not codes[3].any()
+    for r in (0, 1, 2, 4, 5, 6, 7):
+        c = int(np.argmax(np.abs(w[r])))
+        assert codes[r, c] == (0xFE if w[r, c] < 0 else 0x7E)
+        assert rs[r] == np.float32(np.abs(w[r]).max() / np.float32(448.0))
+
+
+def test_nvfp4_reconstruction_error_bound():
+    # |w - w_hat| <= d * (half E2M1 spacing at |t|), where d = S*g; above 6
+    # (only after a downward-rounded block scale) it saturates by < d.
+    w = synth.weights(32, 128, seed=13)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    wh = oracle.dequant_nvfp4(codes, scales, g)
+    for r in range(32):
+        for b in range(8):
+            S = oracle.ue4m3_value(int(scales[r, b]))
+            d = float(np.float32(np.float32(S) * g))
+            for i in range(16):
+                k = b * 16 + i
+                t = abs(float(w[r, k])) / d
+                hs = 0.25 if t < 2 else (0.5 if t < 4 else 1.0)
+                assert abs(float(w[r, k]) - wh[r, k]) <= d * hs * (1 + 1e-6) + 1e-30
+
+
+def test_rows_pack_equals_whole_pack():
+    # packing a subset of rows with the tensor's own g equals the same rows of
+    # the whole-tensor pack (how full-size parity samples rows)
+    w = synth.weights(40, 64, seed=17)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    rows = [0, 7, 39]
+    c2, s2 = oracle.pack_nvfp4_rows(w[rows], g)
+    assert np.array_equal(c2, codes[rows]) and np.array_equal(s2, scales[rows])
+
+
+def test_degenerate_tiny_tensor_scale_underflows_to_zero():
+    # amax so small that amax/2688 underflows: g == 0, every code and scale 0
+    w = np.zeros((1, 16), np.float32)
+    w[0, 3] = np.float32(2.0 ** -149)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    assert float(g) == 0.0 and not codes.any() and not scales.any()
+
+
+def test_synth_chunks_equal_one_shot():
+    w = synth.weights(50, 48, seed=2)
+    parts = np.concatenate([c for _, c in synth.weight_chunks(50, 48, seed=2, rows_per_chunk=7)])
+    assert np.array_equal(w, parts)
+    rows = [0, 6, 7, 49]
+    assert np.array_equal(synth.weight_rows(50, 48, rows, seed=2, rows_per_chunk=7), w[rows])
+    x8 = synth.activations(8, 48, seed=2)
+    assert np.array_equal(synth.activations(3, 48, seed=2), x8[:3])
