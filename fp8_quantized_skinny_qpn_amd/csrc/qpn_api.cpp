@@ -1,0 +1,229 @@
+// qpn_api.cpp -- the C ABI declared in include/qpn.h: host-side argument
+// checks, plan selection and launches.  Every check runs before anything is
+// enqueued; nothing here allocates, copies, synchronises or prints.
+#include "qpn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "qpn_common.h"
+#include "qpn_internal.h"
+
+namespace {
+
+using namespace qpn;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool nv_shape_ok(int64_t n, int64_t k) {
+  return n >= 0 && k >= 0 && n <= kMaxN && k <= kMaxK && k % 16 == 0;
+}
+bool f8_shape_ok(int64_t n, int64_t k) {
+  return n >= 0 && k >= 0 && n <= kMaxN && k <= kMaxK && k % 8 == 0;
+}
+
+// Device check: the current device must be gfx950.  Cached per device id.
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+int g_ok[kMaxDevices];
+
+int device_check() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QPN_ERR_DEVICE;
+  std::call_once(g_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    g_ok[dev] = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+      g_ok[dev] = 1;
+  });
+  return g_ok[dev] ? QPN_OK : QPN_ERR_DEVICE;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QPN_OK : QPN_ERR_LAUNCH; }
+
+int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, const void* y,
+                       int m, int64_t n, int64_t k) {
+  if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
+  if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
+  if (m == 0 || n == 0) return QPN_OK;  // empty call: nothing is read or written
+  if (!packed || (!x && k > 0) || !y) return QPN_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 2)) return QPN_ERR_ALIGN;
+  return QPN_OK;
+}
+
+int gemm_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
+               int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = gemm_common_checks(fmt, packed, x, y, m, n, k);
+  if (rc != QPN_OK) return rc;
+  if (m == 0 || n == 0) return QPN_OK;
+  rc = device_check();
+  if (rc != QPN_OK) return rc;
+  GemmArgs a{packed, x, y, m, n, k, nullptr, stream};
+  return launch_status(launch_gemm(fmt, false, a, gemm_waves_per_panel(fmt, n, k)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qpn_status_string(int status) {
+  switch (status) {
+    case QPN_OK: return "QPN_OK";
+    case QPN_ERR_NULL: return "QPN_ERR_NULL: a required pointer is NULL";
+    case QPN_ERR_SHAPE: return "QPN_ERR_SHAPE: m, n or k outside the supported range";
+    case QPN_ERR_ALIGN: return "QPN_ERR_ALIGN: a pointer is not aligned as required";
+    case QPN_ERR_BUFFER: return "QPN_ERR_BUFFER: buffer smaller than required";
+    case QPN_ERR_DEVICE: return "QPN_ERR_DEVICE: current device is not a usable gfx950";
+    case QPN_ERR_LAUNCH: return "QPN_ERR_LAUNCH: kernel launch failed";
+    default: return "QPN: unknown status";
+  }
+}
+
+int qpn_layout_version(void) { return (int)kLayoutVersion; }
+
+size_t qpn_nvfp4_packed_bytes(int64_t n, int64_t k) {
+  if (!nv_shape_ok(n, k)) return 0;
+  return (size_t)nv_blob_bytes(n, k);
+}
+
+size_t qpn_fp8_packed_bytes(int64_t n, int64_t k) {
+  if (!f8_shape_ok(n, k)) return 0;
+  return (size_t)f8_blob_bytes(n, k);
+}
+
+size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
+  if (m < 0 || m > kMaxM) return (size_t)-1;
+  switch (op) {
+    case QPN_OP_GEMM_NVFP4: return nv_shape_ok(n, k) ? 0 : (size_t)-1;
+    case QPN_OP_GEMM_FP8: return f8_shape_ok(n, k) ? 0 : (size_t)-1;
+    case QPN_OP_LMHEAD_NVFP4:
+      if (!nv_shape_ok(n, k)) return (size_t)-1;
+      return (size_t)8 * (size_t)m * (size_t)panels_of(n);
+    default: return (size_t)-1;
+  }
+}
+
+int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups,
+                  int* waves_per_workgroup, int* prefetch_depth) {
+  if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
+  uint32_t fmt;
+  switch (op) {
+    case QPN_OP_GEMM_NVFP4:
+    case QPN_OP_LMHEAD_NVFP4:
+      if (!nv_shape_ok(n, k)) return QPN_ERR_SHAPE;
+      fmt = kFmtNvfp4;
+      break;
+    case QPN_OP_GEMM_FP8:
+      if (!f8_shape_ok(n, k)) return QPN_ERR_SHAPE;
+      fmt = kFmtFp8;
+      break;
+    default: return QPN_ERR_SHAPE;
+  }
+  if (workgroups) *workgroups = panels_of(n);
+  if (waves_per_workgroup) *waves_per_workgroup = gemm_waves_per_panel(fmt, n, k);
+  if (prefetch_depth) *prefetch_depth = gemm_prefetch_depth(fmt);
+  return QPN_OK;
+}
+
+int qpn_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, size_t packed_bytes,
+                   void* stream) {
+  if (!nv_shape_ok(n, k)) return QPN_ERR_SHAPE;
+  if (!packed || (!w && n * k > 0)) return QPN_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(w, 16)) return QPN_ERR_ALIGN;
+  if (packed_bytes < nv_blob_bytes(n, k)) return QPN_ERR_BUFFER;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_pack_nvfp4(w, n, k, packed, stream));
+}
+
+int qpn_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, size_t packed_bytes,
+                 void* stream) {
+  if (!f8_shape_ok(n, k)) return QPN_ERR_SHAPE;
+  if (!packed || (!w && n * k > 0)) return QPN_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(w, 16)) return QPN_ERR_ALIGN;
+  if (packed_bytes < f8_blob_bytes(n, k)) return QPN_ERR_BUFFER;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_pack_fp8(w, n, k, packed, stream));
+}
+
+int qpn_gemm_nvfp4(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
+                   int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_entry(kFmtNvfp4, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+}
+
+int qpn_gemm_fp8(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n, int64_t k,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_entry(kFmtFp8, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+}
+
+int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
+                     int m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (n < 1) return QPN_ERR_SHAPE;
+  int rc = gemm_common_checks(kFmtNvfp4, packed, x, logits, m, n, k);
+  if (rc != QPN_OK) return rc;
+  if (m == 0) return QPN_OK;
+  if (!argmax) return QPN_ERR_NULL;
+  if (!aligned(argmax, 4)) return QPN_ERR_ALIGN;
+  const size_t need = qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4, m, n, k);
+  if (!workspace) return QPN_ERR_NULL;
+  if (!aligned(workspace, 8)) return QPN_ERR_ALIGN;
+  if (workspace_bytes < need) return QPN_ERR_BUFFER;
+  rc = device_check();
+  if (rc != QPN_OK) return rc;
+  GemmArgs a{packed, x, logits, m, n, k, (uint64_t*)workspace, stream};
+  hipError_t e = launch_gemm(kFmtNvfp4, true, a, gemm_waves_per_panel(kFmtNvfp4, n, k));
+  if (e != hipSuccess) return QPN_ERR_LAUNCH;
+  return launch_status(
+      launch_argmax_finalize((const uint64_t*)workspace, panels_of(n), m, argmax, stream));
+}
+
+int qpn_debug_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,
+                           uint8_t* scales, float* g, void* stream) {
+  if (!nv_shape_ok(n, k)) return QPN_ERR_SHAPE;
+  if (!packed || !g || ((!codes || !scales) && n * k > 0)) return QPN_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(g, 4)) return QPN_ERR_ALIGN;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_unpack_nvfp4(packed, n, k, codes, scales, g, stream));
+}
+
+int qpn_debug_unpack_fp8(const void* packed, int64_t n, int64_t k, uint8_t* codes,
+                         float* row_scale, void* stream) {
+  if (!f8_shape_ok(n, k)) return QPN_ERR_SHAPE;
+  if (!packed || (!codes && n * k > 0) || (!row_scale && n > 0)) return QPN_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(row_scale, 4)) return QPN_ERR_ALIGN;
+  if (n == 0) return QPN_OK;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_unpack_fp8(packed, n, k, codes, row_scale, stream));
+}
+
+int qpn_debug_decode_nvfp4(const uint8_t* codes16, const uint8_t* scales2, int64_t count,
+                           uint16_t* out, void* stream) {
+  if (count < 0 || count > (int64_t(1) << 24)) return QPN_ERR_SHAPE;
+  if (count == 0) return QPN_OK;
+  if (!codes16 || !scales2 || !out) return QPN_ERR_NULL;
+  if (!aligned(out, 2)) return QPN_ERR_ALIGN;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_decode_nvfp4(codes16, scales2, count, out, stream));
+}
+
+int qpn_debug_decode_fp8(const uint8_t* codes16, int64_t count, uint16_t* out, void* stream) {
+  if (count < 0 || count > (int64_t(1) << 24)) return QPN_ERR_SHAPE;
+  if (count == 0) return QPN_OK;
+  if (!codes16 || !out) return QPN_ERR_NULL;
+  if (!aligned(out, 2)) return QPN_ERR_ALIGN;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_decode_fp8(codes16, count, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+"""Thin ctypes binding of libqpn.so (the C ABI in include/qpn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libqpn.so.  torch supplies device memory and the current stream.
+Importing this module loads the library and raises if it is not built; there
+is no fallback of any kind.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqpn.so")
+
+QPN_OK = 0
+OP_GEMM_NVFP4 = 1
+OP_GEMM_FP8 = 2
+OP_LMHEAD_NVFP4 = 3
+
+FMT_NVFP4 = "nvfp4"
+FMT_FP8 = "fp8"
+
+
+class QpnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m fp8_quantized_skinny_qpn_amd.build` "
+            "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    c = ctypes
+    vp, i64, sz, i32 = c.c_void_p, c.c_int64, c.c_size_t, c.c_int
+    sig = {
+        "qpn_status_string": ([i32], c.c_char_p),
+        "qpn_layout_version": ([], i32),
+        "qpn_nvfp4_packed_bytes": ([i64, i64], sz),
+        "qpn_fp8_packed_bytes": ([i64, i64], sz),
+        "qpn_workspace_bytes": ([i32, i32, i64, i64], sz),
+        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp], i32),
+        "qpn_pack_nvfp4": ([vp, i64, i64, vp, sz, vp], i32),
+        "qpn_pack_fp8": ([vp, i64, i64, vp, sz, vp], i32),
+        "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_gemm_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_lmhead_nvfp4": ([vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_debug_unpack_nvfp4": ([vp, i64, i64, vp, vp, vp, vp], i32),
+        "qpn_debug_unpack_fp8": ([vp, i64, i64, vp, vp, vp], i32),
+        "qpn_debug_decode_nvfp4": ([vp, vp, i64, vp, vp], i32),
+        "qpn_debug_decode_fp8": ([vp, i64, vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+# Symbols the C header declares (the CPU tests check that each one loads).
+EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
+            "qpn_fp8_packed_bytes", "qpn_workspace_bytes", "qpn_gemm_plan", "qpn_pack_nvfp4", "qpn_pack_fp8",
+            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_lmhead_nvfp4", "qpn_debug_unpack_nvfp4",
+            "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8")
+
+
+def status_string(rc: int) -> str:
+    return lib.qpn_status_string(int(rc)).decode()
+
+
+def check(rc: int):
+    if rc != QPN_OK:
+        raise QpnError(rc, status_string(rc))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def nvfp4_packed_bytes(n: int, k: int) -> int:
+    return int(lib.qpn_nvfp4_packed_bytes(n, k))
+
+
+def fp8_packed_bytes(n: int, k: int) -> int:
+    return int(lib.qpn_fp8_packed_bytes(n, k))
+
+
+def workspace_bytes(op: int, m: int, n: int, k: int) -> int:
+    return int(lib.qpn_workspace_bytes(op, m, n, k))
+
+
+def gemm_plan(op: int, m: int, n: int, k: int):
+    """(workgroups, waves_per_workgroup, prefetch_depth) the library launches."""
+    wg = ctypes.c_int64()
+    w = ctypes.c_int()
+    d = ctypes.c_int()
+    check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), ctypes.byref(w), ctypes.byref(d)))
+    return wg.value, w.value, d.value
+
+
+def kernel_name(fmt: str, n: int, k: int, lmhead: bool = False) -> str:
+    """Demangled name (template part) of the GEMM kernel a call launches."""
+    op = OP_LMHEAD_NVFP4 if lmhead else (OP_GEMM_NVFP4 if fmt == FMT_NVFP4 else OP_GEMM_FP8)
+    _, w, d = gemm_plan(op, 1, n, k)
+    f = 1 if fmt == FMT_NVFP4 else 2
+    return f"qpn::skinny_gemm_kernel<{f}u, {w}, {d}, {'true' if lmhead else 'false'}>"
+
+
+@dataclass
+class PackedWeight:
+    """A packed weight blob on the device plus the shape it was packed for."""
+    blob: torch.Tensor  # uint8, device
+    n: int
+    k: int
+    fmt: str
+
+    @property
+    def nbytes(self) -> int:
+        return self.blob.numel()
+
+    def clone(self) -> "PackedWeight":
+        return PackedWeight(self.blob.clone(), self.n, self.k, self.fmt)
+
+
+def _dev_f32(w):
+    if not (w.is_cuda and w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()):
+        raise ValueError("weights must be a contiguous 2-D float32 CUDA tensor")
+
+
+def pack_nvfp4(w: torch.Tensor, stream=None) -> PackedWeight:
+    _dev_f32(w)
+    n, k = w.shape
+    nb = nvfp4_packed_bytes(n, k)
+    if nb == 0:
+        raise QpnError(2, status_string(2))
+    blob = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    check(lib.qpn_pack_nvfp4(_ptr(w), n, k, _ptr(blob), nb, _stream(stream)))
+    return PackedWeight(blob, n, k, FMT_NVFP4)
+
+
+def pack_fp8(w: torch.Tensor, stream=None) -> PackedWeight:
+    _dev_f32(w)
+    n, k = w.shape
+    nb = fp8_packed_bytes(n, k)
+    if nb == 0:
+        raise QpnError(2, status_string(2))
+    blob = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    check(lib.qpn_pack_fp8(_ptr(w), n, k, _ptr(blob), nb, _stream(stream)))
+    return PackedWeight(blob, n, k, FMT_FP8)
+
+
+def _x_check(x, k):
+    if not (x.is_cuda and x.dtype == torch.float16 and x.dim() == 2 and x.is_contiguous()):
+        raise ValueError("activations must be a contiguous 2-D float16 CUDA tensor")
+    if x.shape[1] != k:
+        raise ValueError(f"activation K {x.shape[1]} does not match the packed K {k}")
+
+
+def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Y = X * What^T through qpn_gemm_nvfp4 / qpn_gemm_fp8."""
+    _x_check(x, pw.k)
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+    fn = lib.qpn_gemm_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_fp8
+    check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k, None, 0, _stream(stream)))
+    return out
+
+
+def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, workspace=None,
+                 stream=None):
+    """(logits fp16 [m, n], argmax int32 [m]) through qpn_lmhead_nvfp4."""
+    if pw.fmt != FMT_NVFP4:
+        raise ValueError("lm_head needs an NVFP4 blob")
+    _x_check(x, pw.k)
+    m = x.shape[0]
+    if logits is None:
+        logits = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+    if argmax is None:
+        argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
+    need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+    check(lib.qpn_lmhead_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax), m, pw.n, pw.k,
+                               _ptr(workspace), workspace.numel(), _stream(stream)))
+    return logits, argmax
+
+
+def debug_unpack_nvfp4(pw: PackedWeight, stream=None):
+    """Canonical (codes [n, k/2], scales [n, k/16], g) read back from the blob."""
+    dev = pw.blob.device
+    codes = torch.empty((pw.n, pw.k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((pw.n, pw.k // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty((1,), dtype=torch.float32, device=dev)
+    check(lib.qpn_debug_unpack_nvfp4(_ptr(pw.blob), pw.n, pw.k, _ptr(codes), _ptr(scales), _ptr(g),
+                                     _stream(stream)))
+    return codes, scales, g
+
+
+def debug_unpack_fp8(pw: PackedWeight, stream=None):
+    """Canonical (codes [n, k], row_scale [n]) read back from the blob."""
+    dev = pw.blob.device
+    codes = torch.empty((pw.n, pw.k), dtype=torch.uint8, device=dev)
+    rs = torch.empty((pw.n,), dtype=torch.float32, device=dev)
+    check(lib.qpn_debug_unpack_fp8(_ptr(pw.blob), pw.n, pw.k, _ptr(codes), _ptr(rs),
+                                   _stream(stream)))
+    return codes, rs
+
+
+def debug_decode_nvfp4(codes16: torch.Tensor, scales2: torch.Tensor, stream=None) -> torch.Tensor:
+    f = codes16.shape[0]
+    out = torch.empty((f, 32), dtype=torch.float16, device=codes16.device)
+    check(lib.qpn_debug_decode_nvfp4(_ptr(codes16), _ptr(scales2), f, _ptr(out), _stream(stream)))
+    return out
+
+
+def debug_decode_fp8(codes16: torch.Tensor, stream=None) -> torch.Tensor:
+    f = codes16.shape[0]
+    out = torch.empty((f, 16), dtype=torch.float16, device=codes16.device)
+    check(lib.qpn_debug_decode_fp8(_ptr(codes16), f, _ptr(out), _stream(stream)))
+    return out

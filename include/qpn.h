@@ -1,0 +1,195 @@
+/*
+ * qpn.h -- C ABI of the QPN weight-streaming skinny GEMM for MI355X (gfx950).
+ *
+ * The operation.  Decode steps of single-request speculative decoding
+ * multiply each projection's weights by a block of 1..8 FP16 activation rows
+ * (the target token plus up to 7 draft candidates checked in the same verify
+ * round).  The weights stay in their published compressed formats while they
+ * stream from HBM and are expanded to FP16 in registers, in small pieces,
+ * right before the matrix unit consumes them; there is no dequantise-first
+ * pass.  NVFP4 regions and FP8 regions each get their own path, activations
+ * are FP16, accumulation is FP32, outputs are FP16.  Sources:
+ *   taozi.news, "四张 2017 年 V100 跑通 Qwen 3 NVFP4 推理，性能追平 RTX 5090":
+ *     section "自研 QPN 内核：让 Volta 跑 NVFP4" (the kernel idea, the NVFP4
+ *     M=1 / M=8 and FP8 M=1..4 paths, the 4-bit lm_head, the 8-row verify
+ *     tile) and section "v1.1 的关键改进：保留官方混合精度分配" (FP4 regions
+ *     -> NVFP4 path, FP8 regions -> FP8 path, activations FP16);
+ *   aiwitness.kr, "VOLTA에서 NVFP4 구동! ...": section "내가 실제로 만든 것"
+ *     (weights stay compressed and are translated in registers) and the v1.1
+ *     section (the published FP4/FP8 assignment is preserved);
+ *   lcz.me, "前情提要 整台洋垃圾V100 16G雙卡": table
+ *     "NVFP4 （V100 sm_70 + E5-2686 v4）的支援狀況" (NVFP4 = E2M1 codes with
+ *     UE4M3 scales, decodable in software).
+ * The pages fix no bit layout, block size or rounding.  This library uses:
+ *   NVFP4: E2M1 codes, one UE4M3 scale per 16 consecutive K elements of a
+ *          row, one FP32 tensor scale g = amax / (6 * 448);
+ *   FP8:   E4M3 (OCP "FN": bias 7, max 448) codes, one FP32 scale per output
+ *          row s = row amax / 448;
+ *   both:  round to nearest, ties to the even code, saturating.
+ *
+ * Conventions for every call.
+ *   - W is [n, k] row-major FP32 (row = output channel).  X is [m, k]
+ *     row-major FP16, Y is [m, n] row-major FP16: Y = X * What^T.
+ *   - FP16 data is passed as uint16_t bit patterns.
+ *   - Pointers named w, packed, x, y, logits, argmax, workspace are DEVICE
+ *     pointers on the current HIP device.  `stream` is a hipStream_t (NULL =
+ *     the default stream).  All work is enqueued on that stream; no call
+ *     allocates, frees, copies to the host or synchronises.
+ *   - The caller owns every buffer.  A packed blob is opaque and versioned;
+ *     it records its own n, k and scales, so GEMM calls need no host reads.
+ *   - Calls that share a workspace must not overlap.
+ *   - Argument checks run on the host before anything is enqueued; on any
+ *     error nothing is launched.  Device faults surface, as usual for HIP,
+ *     at the caller's next synchronisation.  Nothing is printed and no C++
+ *     exception crosses the ABI.
+ *   - Shapes: 0 <= m <= 8, n >= 0, k >= 0; n <= 2^24, k <= 2^20.  NVFP4
+ *     needs k % 16 == 0, FP8 needs k % 8 == 0.  m == 0 or n == 0 is a valid
+ *     empty call (QPN_OK, nothing launched); k == 0 gives Y = 0.
+ *   - Alignment: packed 256 B, x 16 B, w 16 B, workspace 8 B, y and
+ *     logits 2 B, argmax 4 B.
+ *   - Inputs to pack must be finite; this is a precondition, not checked.
+ */
+#ifndef QPN_H
+#define QPN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define QPN_API __attribute__((visibility("default")))
+#else
+#define QPN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+#define QPN_OK 0
+#define QPN_ERR_NULL 1   /* a required pointer is NULL                      */
+#define QPN_ERR_SHAPE 2  /* m, n or k outside the documented range         */
+#define QPN_ERR_ALIGN 3  /* a pointer is not aligned as documented         */
+#define QPN_ERR_BUFFER 4 /* packed or workspace buffer smaller than needed */
+#define QPN_ERR_DEVICE 5 /* current device is not gfx950 or not usable     */
+#define QPN_ERR_LAUNCH 6 /* the HIP runtime rejected a kernel launch       */
+
+/* Formats, for qpn_workspace_bytes. */
+#define QPN_OP_GEMM_NVFP4 1
+#define QPN_OP_GEMM_FP8 2
+#define QPN_OP_LMHEAD_NVFP4 3
+
+/* Human-readable name of a status code (static string, never NULL). */
+QPN_API const char *qpn_status_string(int status);
+
+/* Version of the packed-blob layout this library reads and writes. */
+QPN_API int qpn_layout_version(void);
+
+/* Bytes a packed NVFP4 blob of an [n, k] weight occupies (header, codes and
+ * block scales, padded to whole tiles); 0 when (n, k) is not a valid NVFP4
+ * shape.  Pure host computation. */
+QPN_API size_t qpn_nvfp4_packed_bytes(int64_t n, int64_t k);
+
+/* Bytes a packed FP8 blob of an [n, k] weight occupies (header, row scales
+ * and codes, padded to whole tiles); 0 when (n, k) is not a valid FP8 shape.
+ * Pure host computation. */
+QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
+
+/* Workspace bytes a call of kind `op` (QPN_OP_*) with these sizes needs.
+ * The GEMM calls need none (0); the lm_head needs 8 * m * ceil(n / 16).
+ * Returns (size_t)-1 for an unknown op or invalid shape.  Pure host. */
+QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
+
+/* Launch geometry a call of kind `op` (QPN_OP_*) uses for (m, n, k): the
+ * number of workgroups (one per 16-row panel), wavefronts per workgroup (they
+ * split the panel's K range) and the k-steps each wavefront keeps in flight.
+ * A pure function of the shape, independent of any declared maximum.  Any
+ * output pointer may be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
+QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
+                          int *waves_per_workgroup, int *prefetch_depth);
+
+/* NVFP4 pack ("pure round" quantisation, lcz.me quantisation-option table,
+ * NVFP4-NVIDIA row; format per the lcz.me NVFP4 support table).
+ * w: device FP32 [n, k].  packed: device buffer of packed_bytes >=
+ * qpn_nvfp4_packed_bytes(n, k).  Computes, in FP32 with IEEE division:
+ *   amax = max|w|;  g = amax / 2688;
+ *   per 16-block of a row: sc = E4M3(nearest-even, saturating) of
+ *     (blockmax / 6) / g  (sc = 0 when g == 0);  S = value of sc;
+ *   codes = 0 when S == 0, else E2M1(nearest-even, saturating) of w / (S*g).
+ * Writes the whole blob (header, codes, scales, zeroed padding).  Three
+ * kernels on `stream`, no host synchronisation. */
+QPN_API int qpn_pack_nvfp4(const float *w, int64_t n, int64_t k, void *packed,
+                   size_t packed_bytes, void *stream);
+
+/* FP8 pack (taozi.news section "v1.1 的关键改进", FP8 regions kept as FP8).
+ * w: device FP32 [n, k].  Per row: s = max|w_row| / 448 (stored FP32);
+ * codes = 0 when s == 0, else E4M3(nearest-even, saturating) of w / s.
+ * Writes the whole blob.  One kernel plus a header kernel on `stream`. */
+QPN_API int qpn_pack_fp8(const float *w, int64_t n, int64_t k, void *packed,
+                 size_t packed_bytes, void *stream);
+
+/* QPN NVFP4 skinny GEMM (taozi.news section "自研 QPN 内核", the NVFP4 path
+ * at M=1 and M=8; aiwitness.kr section "내가 실제로 만든 것").
+ * Y[m, n] = FP16_RNE( sum_k X[m, k] * What[n, k] ), What = E2M1 * UE4M3 * g,
+ * with FP32 accumulation.  packed: blob from qpn_pack_nvfp4 for this (n, k).
+ * x: [m, k] FP16, y: [m, n] FP16.  workspace may be NULL (0 bytes needed).
+ * If the blob header does not describe an NVFP4 [n, k] weight the kernel
+ * writes FP16 NaN to every output instead of computing. */
+QPN_API int qpn_gemm_nvfp4(const void *packed, const uint16_t *x, uint16_t *y, int m,
+                   int64_t n, int64_t k, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* QPN FP8 skinny GEMM (taozi.news section "自研 QPN 内核", the FP8 M=1..4
+ * path; section "v1.1 的关键改进" for FP8 regions).
+ * Y[m, n] = FP16_RNE( s_n * sum_k X[m, k] * E4M3(code[n, k]) ), FP32
+ * accumulation.  Arguments and failure behaviour as qpn_gemm_nvfp4. */
+QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int m,
+                 int64_t n, int64_t k, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* NVFP4 lm_head with fused greedy argmax (taozi.news section "自研 QPN 内核",
+ * the native 4-bit lm_head; section "一些工程细节与长上下文发现", drafts
+ * proposed by greedy / local argmax).  Computes logits exactly as
+ * qpn_gemm_nvfp4 and, per row m, argmax[m] = the lowest index n whose FP16
+ * logit equals the row maximum (values compared as numbers: -0 == +0).
+ * n >= 1 is required.  workspace: >= qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4,
+ * m, n, k) bytes of device memory, contents ignored and overwritten.  Two
+ * kernels on `stream`. */
+QPN_API int qpn_lmhead_nvfp4(const void *packed, const uint16_t *x, uint16_t *logits,
+                     int32_t *argmax, int m, int64_t n, int64_t k,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* --- test exports: the device-side layout and decode, for parity checks --- */
+
+/* Canonical export of an NVFP4 blob: codes [n, k/2] (element 2j in the low
+ * nibble of byte j), scales [n, k/16], tensor scale g (1 float).  All three
+ * are device pointers.  Reads the blob with the same layout map the GEMM
+ * uses. */
+QPN_API int qpn_debug_unpack_nvfp4(const void *packed, int64_t n, int64_t k,
+                           uint8_t *codes, uint8_t *scales, float *g,
+                           void *stream);
+
+/* Canonical export of an FP8 blob: codes [n, k], row scales [n] FP32. */
+QPN_API int qpn_debug_unpack_fp8(const void *packed, int64_t n, int64_t k,
+                         uint8_t *codes, float *row_scale, void *stream);
+
+/* Runs the GEMM's own NVFP4 register decode on `count` fragments: fragment
+ * i is 16 code bytes codes16[16 i ..] (32 E2M1 codes, low nibble first) and
+ * 2 UE4M3 bytes scales2[2 i ..] (first for codes 0..15, second for 16..31).
+ * out[32 i + e] is the FP16 operand the matrix unit receives for code e,
+ * which equals E2M1(code) * UE4M3(scale) exactly.  Scale bytes must be
+ * <= 0x7E.  Device pointers. */
+QPN_API int qpn_debug_decode_nvfp4(const uint8_t *codes16, const uint8_t *scales2,
+                           int64_t count, uint16_t *out, void *stream);
+
+/* Runs the GEMM's own FP8 register decode: fragment i is 16 E4M3 bytes;
+ * out[16 i + e] is the FP16 operand for byte e, which equals E4M3(byte)
+ * exactly for every byte except the NaN codes 0x7F and 0xFF. */
+QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
+                         uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPN_H */

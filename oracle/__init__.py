@@ -66,8 +66,15 @@ def lib():
         L.qpn_oracle_argmax_f16.restype = None
         L.qpn_oracle_round_f16_array.argtypes = [c.c_void_p, c.c_int64, c.c_void_p]
         L.qpn_oracle_round_f16_array.restype = None
+        L.qpn_oracle_threads.argtypes = []
+        L.qpn_oracle_threads.restype = c.c_int
         _LIB = L
     return _LIB
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().qpn_oracle_threads())
 
 
 def _p(a):

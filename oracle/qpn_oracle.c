@@ -39,6 +39,7 @@
  * products); see the function comments for which pin covers what.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -452,6 +453,9 @@ ORACLE_API void qpn_oracle_argmax_f16(const uint16_t *logits, int m, int64_t n,
         out[mi] = (int32_t)best;
     }
 }
+
+/* Threads the OpenMP loops above run with (reported by the CPU baseline). */
+ORACLE_API int qpn_oracle_threads(void) { return omp_get_max_threads(); }
 
 /* Round an FP64 result array to FP16 bit patterns (the returned logits). */
 ORACLE_API void qpn_oracle_round_f16_array(const double *y, int64_t count,

@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and its host-side size queries and argument checks behave as
+include/qpn.h documents.  No kernel is launched by any test here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qpn.h")
+
+
+@pytest.fixture(scope="module")
+def qpn():
+    from fp8_quantized_skinny_qpn_amd import qpn as q
+    return q
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"QPN_API\s+[\w\s\*]*?\b(qpn_\w+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(qpn):
+    names = _declared()
+    assert len(names) == 15
+    lib = ctypes.CDLL(qpn.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(qpn.EXPORTED) == names
+
+
+def test_status_strings(qpn):
+    for rc in range(7):
+        s = qpn.status_string(rc)
+        assert s.startswith("QPN_")
+    assert "unknown" in qpn.status_string(99)
+    assert qpn.lib.qpn_layout_version() == 1
+
+
+def test_packed_sizes(qpn):
+    # header 256 B + ceil(n/16) panels * ceil(k/128) k-steps * 1152 B
+    assert qpn.nvfp4_packed_bytes(5120, 17408) == 256 + 320 * 136 * 1152
+    assert qpn.nvfp4_packed_bytes(17408, 5120) == 256 + 1088 * 40 * 1152
+    assert qpn.nvfp4_packed_bytes(151936, 5120) == 256 + 9496 * 40 * 1152
+    # the algorithmic bytes of the format (codes + scales + g) fit exactly
+    # when n % 16 == 0 and k % 128 == 0
+    for n, k in [(2048, 2048), (5120, 17408), (17408, 5120), (151936, 5120)]:
+        assert qpn.nvfp4_packed_bytes(n, k) - 256 == n * k // 2 + n * k // 16
+    assert qpn.nvfp4_packed_bytes(17, 16) == 256 + 2 * 1 * 1152
+    assert qpn.nvfp4_packed_bytes(0, 0) == 256
+    assert qpn.nvfp4_packed_bytes(16, 8) == 0       # k % 16 != 0
+    assert qpn.nvfp4_packed_bytes(-1, 16) == 0
+    assert qpn.nvfp4_packed_bytes(1 << 25, 16) == 0  # n too large
+    # FP8: header + 256-aligned row scales + ceil(n/16) * ceil(k/64) * 1024
+    assert qpn.fp8_packed_bytes(6144, 5120) == 256 + 6144 * 4 + 384 * 80 * 1024
+    assert qpn.fp8_packed_bytes(20, 8) == 256 + 256 + 2 * 1 * 1024
+    assert qpn.fp8_packed_bytes(16, 12) == 0
+
+
+def test_gemm_plan(qpn):
+    # one workgroup per 16-row panel; waves split K; a pure function of the shape
+    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)[0] == 1088
+    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)[0] == 320
+    for m in (1, 4, 8):
+        assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, 5120, 17408) == qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)
+    for op, n, k in [(1, 17408, 5120), (1, 5120, 17408), (2, 6144, 5120), (3, 151936, 5120), (1, 17, 16)]:
+        wg, w, d = qpn.gemm_plan(op, 8, n, k)
+        assert w in (1, 2, 4, 8, 16) and d >= 1
+    with pytest.raises(qpn.QpnError):
+        qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 16, 24)
+
+
+def test_workspace_sizes(qpn):
+    assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 5120, 17408) == 0
+    assert qpn.workspace_bytes(qpn.OP_GEMM_FP8, 4, 5120, 5120) == 0
+    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 8, 151936, 5120) == 8 * 8 * 9496
+    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 1, 17, 16) == 8 * 2
+    big = ctypes.c_size_t(-1).value
+    assert qpn.workspace_bytes(99, 1, 16, 16) == big
+    assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 9, 16, 16) == big
+
+
+# Argument checks.  Pointers are plain integers the library never dereferences
+# because every call below fails a host-side check first.
+A256 = 0x10000
+A16 = 0x10010
+ODD = 0x10001
+
+
+def _gemm(qpn, fn, packed, x, y, m, n, k):
+    return fn(ctypes.c_void_p(packed), ctypes.c_void_p(x), ctypes.c_void_p(y), m, n, k, None, 0,
+              None)
+
+
+@pytest.mark.parametrize("fname", ["qpn_gemm_nvfp4", "qpn_gemm_fp8"])
+def test_gemm_argument_errors(qpn, fname):
+    fn = getattr(qpn.lib, fname)
+    assert _gemm(qpn, fn, 0, A16, A16, 1, 16, 16) == 1          # null packed
+    assert _gemm(qpn, fn, A256, 0, A16, 1, 16, 16) == 1         # null x
+    assert _gemm(qpn, fn, A256, A16, 0, 1, 16, 16) == 1         # null y
+    assert _gemm(qpn, fn, A256, A16, A16, 9, 16, 16) == 2       # m > 8
+    assert _gemm(qpn, fn, A256, A16, A16, -1, 16, 16) == 2
+    assert _gemm(qpn, fn, A256, A16, A16, 1, 16, 12) == 2       # k not a multiple of 16 / 8
+    assert _gemm(qpn, fn, A256, A16, A16, 1, -3, 16) == 2
+    assert _gemm(qpn, fn, A256, A16, A16, 1, 1 << 25, 16) == 2
+    assert _gemm(qpn, fn, A256, A16, A16, 1, 16, 1 << 21) == 2
+    assert _gemm(qpn, fn, A16, A16, A16, 1, 16, 16) == 3        # packed not 256-aligned
+    assert _gemm(qpn, fn, A256, A16 + 8, A16, 1, 16, 16) == 3   # x not 16-aligned
+    assert _gemm(qpn, fn, A256, A16, ODD, 1, 16, 16) == 3       # y not 2-aligned
+    # empty calls succeed without launching anything
+    assert _gemm(qpn, fn, A256, A16, A16, 0, 16, 16) == 0
+    assert _gemm(qpn, fn, A256, A16, A16, 3, 0, 16) == 0
+
+
+def test_lmhead_argument_errors(qpn):
+    L = qpn.lib
+    v = ctypes.c_void_p
+
+    def call(packed=A256, x=A16, lg=A16, am=A16, m=1, n=16, k=16, ws=A16, wsb=64):
+        return L.qpn_lmhead_nvfp4(v(packed), v(x), v(lg), v(am), m, n, k, v(ws), wsb, None)
+
+    assert call(am=0) == 1
+    assert call(ws=0) == 1
+    assert call(n=0) == 2
+    assert call(am=A16 + 2) == 3
+    assert call(ws=A16 + 4) == 3
+    assert call(wsb=8 * 1 * 1 - 1) == 4                       # workspace too small
+    assert call(m=8, n=160, wsb=8 * 8 * 10 - 8) == 4
+    assert call(m=0) == 0
+
+
+def test_pack_argument_errors(qpn):
+    L = qpn.lib
+    v = ctypes.c_void_p
+    need = qpn.nvfp4_packed_bytes(32, 64)
+    assert L.qpn_pack_nvfp4(v(A16), 32, 64, v(0), need, None) == 1
+    assert L.qpn_pack_nvfp4(v(0), 32, 64, v(A256), need, None) == 1
+    assert L.qpn_pack_nvfp4(v(A16), 32, 40, v(A256), need, None) == 2
+    assert L.qpn_pack_nvfp4(v(A16 + 4), 32, 64, v(A256), need, None) == 3
+    assert L.qpn_pack_nvfp4(v(A16), 32, 64, v(A256 + 128), need, None) == 3
+    assert L.qpn_pack_nvfp4(v(A16), 32, 64, v(A256), need - 1, None) == 4
+    need8 = qpn.fp8_packed_bytes(32, 64)
+    assert L.qpn_pack_fp8(v(A16), 32, 64, v(A256), need8 - 1, None) == 4
+    assert L.qpn_pack_fp8(v(A16), 32, 60, v(A256), need8, None) == 2
+
+
+def test_debug_argument_errors(qpn):
+    L = qpn.lib
+    v = ctypes.c_void_p
+    assert L.qpn_debug_decode_nvfp4(v(0), v(A16), 4, v(A16), None) == 1
+    assert L.qpn_debug_decode_nvfp4(v(A16), v(A16), -1, v(A16), None) == 2
+    assert L.qpn_debug_decode_fp8(v(A16), 0, v(A16), None) == 0
+    assert L.qpn_debug_unpack_nvfp4(v(A256), 16, 24, v(A16), v(A16), v(A16), None) == 2
+    assert L.qpn_debug_unpack_fp8(v(A16), 16, 16, v(A16), v(A16), None) == 3
+
+
+def test_valid_call_without_gpu_reports_device_error(qpn):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    fn = qpn.lib.qpn_gemm_nvfp4
+    assert _gemm(qpn, fn, A256, A16, A16, 1, 16, 16) == 5

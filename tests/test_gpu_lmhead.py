@@ -1,0 +1,137 @@
+"""NVFP4 lm_head with fused argmax against the oracle.
+
+Logits: the GEMM parity bar.  Argmax: bit-exact against the oracle's lowest
+index of the FP16-rounded FP64 logits, with one allowance for a property of
+the arithmetic, not of the code: when two candidates' FP64 logits round to
+FP16 values within the FP32 accumulation error of each other, the GPU's own
+FP16 logits may legitimately order them differently.  Such a row must still
+pick a candidate within 2 FP16 ulps of the true maximum and must equal the
+lowest-index argmax of the GPU's own returned logits; any other mismatch
+fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_quantized_skinny_qpn_amd import synth
+from gpu_util import dev, host, log, need_gpu, parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp16(v):
+    v = abs(float(v))
+    if v < 2.0 ** -14:
+        return 2.0 ** -24
+    return 2.0 ** (np.floor(np.log2(v)) - 10)
+
+
+def _check_argmax(am_gpu, logits_gpu, y_ref, what):
+    lg = np.asarray(logits_gpu)
+    # self-consistency: the returned index is the lowest argmax of the returned logits
+    assert np.array_equal(am_gpu, np.argmax(lg, axis=1).astype(np.int32)), f"{what}: self"
+    am_ref = oracle.argmax_f16(oracle.round_f16(y_ref))
+    ambiguous = 0
+    for mi in range(y_ref.shape[0]):
+        a, b = int(am_gpu[mi]), int(am_ref[mi])
+        if a == b:
+            continue
+        top = float(y_ref[mi, b])
+        assert top - float(y_ref[mi, a]) <= 2 * _ulp16(top), \
+            f"{what}: row {mi} GPU {a} ({y_ref[mi, a]!r}) vs oracle {b} ({top!r})"
+        ambiguous += 1
+    assert ambiguous <= max(1, y_ref.shape[0] // 4), f"{what}: {ambiguous} ambiguous rows"
+    gap = []
+    for mi in range(y_ref.shape[0]):
+        srt = np.sort(oracle.round_f16(y_ref[mi:mi + 1])[0].astype(np.float64))
+        gap.append((srt[-1] - srt[-2]) / _ulp16(srt[-1]))
+    log(f"{what}: top-2 gap in fp16 ulps per row {['%.1f' % g for g in gap]}, ambiguous {ambiguous}")
+
+
+@pytest.mark.parametrize("n,k", [(1000, 256), (4099, 1024), (160, 5120)])
+def test_lmhead_small(n, k):
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=n)
+    x = synth.activations(8, k, seed=n)
+    pw = qpn.pack_nvfp4(dev(w))
+    codes, scales, g = oracle.pack_nvfp4(w)
+    for m in (1, 3, 8):
+        log(f"lmhead {n}x{k} m={m}")
+        lg, am = qpn.lmhead_nvfp4(pw, dev(x[:m]))
+        lg, am = host(lg), host(am)
+        y_ref = oracle.gemm_nvfp4(codes, scales, g, x[:m])
+        parity(lg, y_ref, f"lmhead {n}x{k} m={m}")
+        _check_argmax(am, lg, y_ref, f"lmhead {n}x{k} m={m}")
+        # the GEMM entry point returns the same logits
+        assert np.array_equal(host(qpn.gemm(pw, dev(x[:m]))).view(np.uint16), lg.view(np.uint16))
+
+
+def test_lmhead_duplicate_rows_tie_to_lowest_index():
+    qpn = need_gpu()
+    n, k = 777, 512
+    w = synth.weights(n, k, seed=12)
+    x = synth.activations(8, k, seed=12)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    best = np.argmax(oracle.gemm_nvfp4(codes, scales, g, x), axis=1)
+    # copy each row's winner to one earlier and one later position
+    for mi, b in enumerate(best[:4]):
+        lo, hi = int(b) // 2, min(n - 1, int(b) + 300 + mi)
+        w[lo] = w[b]
+        w[hi] = w[b]
+    lg, am = qpn.lmhead_nvfp4(qpn.pack_nvfp4(dev(w)), dev(x))
+    lg, am = host(lg), host(am)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
+    _check_argmax(am, lg, y_ref, "duplicates")
+    for mi, b in enumerate(best[:4]):
+        lo = int(b) // 2
+        assert lg[mi, lo].view(np.uint16) == lg[mi, b].view(np.uint16)
+
+
+def test_lmhead_one_hot_many_exact_ties():
+    qpn = need_gpu()
+    n, k = 3000, 128
+    w = synth.weights(n, k, seed=21)
+    x = np.zeros((8, k), np.float16)
+    for i in range(8):
+        x[i, 9 * i + 3] = 1.0
+    lg, am = qpn.lmhead_nvfp4(qpn.pack_nvfp4(dev(w)), dev(x))
+    lg, am = host(lg), host(am)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
+    # a column of What takes few distinct values, so the max repeats
+    assert all((y_ref[i] == y_ref[i].max()).sum() > 1 for i in range(8))
+    assert np.array_equal(am, oracle.argmax_f16(oracle.round_f16(y_ref)))
+
+
+def test_lmhead_negative_zero_equals_zero():
+    qpn = need_gpu()
+    n, k = 64, 32
+    w = -np.abs(synth.weights(n, k, seed=5))
+    w[10, :] = 0.0          # logit exactly +0 (or -0 through the sign of the sum)
+    w[40, :] = 0.0
+    x = np.abs(synth.activations(2, k, seed=5)).astype(np.float16)
+    lg, am = qpn.lmhead_nvfp4(qpn.pack_nvfp4(dev(w)), dev(x))
+    assert list(host(am)) == [10, 10]
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_lmhead_full_vocab(m):
+    qpn = need_gpu()
+    n, k = 151936, 5120
+    log(f"lmhead full {n}x{k} m={m}: drawing weights")
+    w = synth.weights(n, k, seed=0)
+    x = synth.activations(8, k, seed=0)[:m]
+    pw = qpn.pack_nvfp4(dev(w))
+    lg, am = qpn.lmhead_nvfp4(pw, dev(x))
+    lg, am = host(lg), host(am)
+    del pw
+    torch.cuda.empty_cache()
+    log("lmhead full: oracle pack + FP64 GEMM")
+    codes, scales, g = oracle.pack_nvfp4(w)
+    del w
+    y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
+    rows = np.random.default_rng(0).choice(n, 4096, replace=False)
+    parity(lg[:, rows], y_ref[:, rows], f"lmhead full m={m} (sampled logits)")
+    _check_argmax(am, lg, y_ref, f"lmhead full m={m}")
