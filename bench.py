@@ -287,6 +287,24 @@ def main():
             extra[f"{name}_M{m}"] = {"us_median": round(med, 3), "GBps": round(b / med / 1e3, 1),
                                      "pct_hbm_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBPS, 1)}
 
+    # measured read ceiling: the same nontemporal 16-byte loads streaming a
+    # 2 GiB buffer (far larger than the 256 MB Infinity Cache)
+    ceil_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        qpn.debug_read_ceiling(ceil_buf, sink)
+    ce = []
+    for _ in range(5):
+        e0 = _record()
+        qpn.debug_read_ceiling(ceil_buf, sink)
+        e1 = _record()
+        ce.append((e0, e1))
+    torch.cuda.synchronize()
+    ceil_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ce]))
+    read_ceiling = ceil_buf.numel() / ceil_us / 1e3
+    del ceil_buf
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -306,6 +324,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 1),
+        "read_ceiling_GBps": round(read_ceiling, 1),
+        "pct_read_ceiling": round(100 * value / read_ceiling, 1),
         "config": {
             "workload": "nvfp4_skinny_gemm K5120->N17408 and K17408->N5120, M in {1,4,8}",
             "calls_per_step": len(shapes) * len(HEADLINE_M),

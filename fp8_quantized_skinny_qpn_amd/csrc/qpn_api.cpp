@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "qpn_common.h"
@@ -44,6 +45,20 @@ int device_check() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QPN_OK : QPN_ERR_LAUNCH; }
 
+// Plan override for A/B measurements (qpn_debug_set_plan): 0 = automatic,
+// 1 = per-lane activation loads with `g_plan_arg` wavefronts per panel,
+// 2 = LDS-streamed activations with stream plan `g_plan_arg`.
+std::atomic<int> g_plan_kernel{0};
+std::atomic<int> g_plan_arg{0};
+
+hipError_t dispatch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a) {
+  const int kern = g_plan_kernel.load(std::memory_order_relaxed);
+  const int arg = g_plan_arg.load(std::memory_order_relaxed);
+  if (kern == 1) return launch_gemm(fmt, argmax, a, arg);
+  if (kern == 2) return launch_stream(fmt, argmax, a, arg);
+  return launch_gemm(fmt, argmax, a, gemm_waves_per_panel(fmt, a.n, a.k));
+}
+
 int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, const void* y,
                        int m, int64_t n, int64_t k) {
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
@@ -64,7 +79,7 @@ int gemm_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y,
   rc = device_check();
   if (rc != QPN_OK) return rc;
   GemmArgs a{packed, x, y, m, n, k, nullptr, stream};
-  return launch_status(launch_gemm(fmt, false, a, gemm_waves_per_panel(fmt, n, k)));
+  return launch_status(dispatch_gemm(fmt, false, a));
 }
 
 }  // namespace
@@ -178,7 +193,7 @@ int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, in
   rc = device_check();
   if (rc != QPN_OK) return rc;
   GemmArgs a{packed, x, logits, m, n, k, (uint64_t*)workspace, stream};
-  hipError_t e = launch_gemm(kFmtNvfp4, true, a, gemm_waves_per_panel(kFmtNvfp4, n, k));
+  hipError_t e = dispatch_gemm(kFmtNvfp4, true, a);
   if (e != hipSuccess) return QPN_ERR_LAUNCH;
   return launch_status(
       launch_argmax_finalize((const uint64_t*)workspace, panels_of(n), m, argmax, stream));
@@ -210,7 +225,7 @@ int qpn_debug_decode_nvfp4(const uint8_t* codes16, const uint8_t* scales2, int64
   if (count < 0 || count > (int64_t(1) << 24)) return QPN_ERR_SHAPE;
   if (count == 0) return QPN_OK;
   if (!codes16 || !scales2 || !out) return QPN_ERR_NULL;
-  if (!aligned(out, 2)) return QPN_ERR_ALIGN;
+  if (!aligned(out, 16)) return QPN_ERR_ALIGN;
   int rc = device_check();
   if (rc != QPN_OK) return rc;
   return launch_status(launch_decode_nvfp4(codes16, scales2, count, out, stream));
@@ -220,10 +235,26 @@ int qpn_debug_decode_fp8(const uint8_t* codes16, int64_t count, uint16_t* out, v
   if (count < 0 || count > (int64_t(1) << 24)) return QPN_ERR_SHAPE;
   if (count == 0) return QPN_OK;
   if (!codes16 || !out) return QPN_ERR_NULL;
-  if (!aligned(out, 2)) return QPN_ERR_ALIGN;
+  if (!aligned(out, 16)) return QPN_ERR_ALIGN;
   int rc = device_check();
   if (rc != QPN_OK) return rc;
   return launch_status(launch_decode_fp8(codes16, count, out, stream));
+}
+
+int qpn_debug_set_plan(int kernel, int arg) {
+  if (kernel < 0 || kernel > 2) return QPN_ERR_SHAPE;
+  g_plan_kernel.store(kernel, std::memory_order_relaxed);
+  g_plan_arg.store(arg, std::memory_order_relaxed);
+  return QPN_OK;
+}
+
+int qpn_debug_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return QPN_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return QPN_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QPN_ERR_ALIGN;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_read_ceiling(buf, (int64_t)(bytes / 16), sink, stream));
 }
 
 }  // extern "C"

@@ -80,71 +80,112 @@ __global__ __launch_bounds__(kLanes * W) void skinny_gemm_kernel(
     uint64_t* __restrict__ keys) {
   using F = Fmt<FMT>;
   constexpr int G = F::kGroups;
+  constexpr int R = D + 1;  // ring slots: one being consumed, D in flight
   const int lane = threadIdx.x & (kLanes - 1);
-  const int wave = threadIdx.x / kLanes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int64_t p = blockIdx.x;
-  const int64_t J = (k + F::kKStep - 1) / F::kKStep;
-  const int row = lane & 15;  // weight row in the panel / activation column
+  const int J = (int)((k + F::kKStep - 1) / F::kKStep);  // k-steps, last may be partial
+  const int Jfull = (int)(k / F::kKStep);                // full k-steps
+  const int row = lane & 15;  // weight row in the panel / activation row (B column)
   const int kg = lane >> 4;   // K group of this lane inside a k-step
 
   const BlobHeader* hdr = reinterpret_cast<const BlobHeader*>(blob);
   const bool valid = hdr->magic == kMagic && hdr->format == FMT &&
                      hdr->layout_version == kLayoutVersion && hdr->n == n && hdr->k == k;
 
-  const uint8_t* chunks = blob + (FMT == kFmtNvfp4 ? (uint64_t)kHeaderBytes : f8_codes_offset(n)) +
-                          (uint64_t)p * J * F::kChunk;
-  const bool xlane = row < m;
-  const uint16_t* xrow = x + (int64_t)(xlane ? row : 0) * k;
+  const uint8_t* pbase = blob + (FMT == kFmtNvfp4 ? (uint64_t)kHeaderBytes : f8_codes_offset(n)) +
+                         (uint64_t)p * (uint64_t)J * F::kChunk;
+
+  // Activations through a raw buffer resource covering exactly x[m, k]:
+  // lanes whose row is >= m fall outside it and read zeros, so every load is
+  // unconditional (no lane branches, static wait counts).  The lane part of
+  // the offset is fixed; the k-step part is a scalar offset.
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, (short)0, (int)((int64_t)m * k * 2), 0x00020000);
+  const int xlane_off = (int)(((int64_t)row * k + kg * (F::kKStep / 4)) * 2);
 
   float4v acc = {0.f, 0.f, 0.f, 0.f};
 
-  if (valid) {
-    const int64_t j0 = J * wave / W;
-    const int64_t j1 = J * (wave + 1) / W;
+  auto issue = [&](int j, WStep& w, XStep<G>& xs) {
+    const uint8_t* ch = pbase + (uint32_t)(j * F::kChunk);
+    w.codes = load_nt_16(ch + 16 * lane);
+    if constexpr (FMT == kFmtNvfp4)
+      w.scales = *reinterpret_cast<const uint16_t*>(ch + kNvCodeBytes + 2 * lane);
+    const int soff = j * F::kKStep * 2;
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+      xs.b[t] = __builtin_bit_cast(
+          half8, __builtin_amdgcn_raw_buffer_load_b128(xres, xlane_off + 16 * t, soff, 0));
+  };
 
-    auto issue = [&](int64_t j, WStep& w, XStep<G>& xs) {
-      const uint8_t* ch = chunks + (uint64_t)j * F::kChunk;
+  auto compute = [&](const WStep& w, const XStep<G>& xs) {
+    half8 a[G];
+    if constexpr (FMT == kFmtNvfp4)
+      decode_nvfp4_fragment(w.codes, w.scales, a);
+    else
+      decode_fp8_fragment(w.codes, a);
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], xs.b[t], acc, 0, 0, 0);
+  };
+
+  if (valid) {
+    // This wavefront's full k-steps [j0, j1).
+    const int j0 = (int)((int64_t)Jfull * wave / W);
+    const int j1 = (int)((int64_t)Jfull * (wave + 1) / W);
+    const int nsteps = j1 - j0;
+    WStep ws[R];
+    XStep<G> xs[R];
+    if (nsteps >= D + R) {
+      // Prologue, steady state and drain.  The steady loop issues k-step
+      // j+i+D into the slot freed by k-step j+i-1 and then consumes k-step
+      // j+i; every load in it is unconditional.
+#pragma unroll
+      for (int i = 0; i < D; ++i) issue(j0 + i, ws[i], xs[i]);
+      int j = j0;
+      for (; j + D + R <= j1; j += R) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          // scheduling fences keep the issue-ahead order: the scheduler would
+          // otherwise hoist later slots' decode and shorten the prefetch
+          issue(j + i + D, ws[(i + D) % R], xs[(i + D) % R]);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(ws[i], xs[i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < D + R - 1; ++i) {
+        if (j + i + D < j1) issue(j + i + D, ws[(i + D) % R], xs[(i + D) % R]);
+        if (j + i < j1) compute(ws[i % R], xs[i % R]);
+      }
+    } else {
+      // Short range: batches of R k-steps, issued together then consumed.
+      for (int j = j0; j < j1; j += R) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (j + i < j1) issue(j + i, ws[i], xs[i]);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (j + i < j1) compute(ws[i], xs[i]);
+      }
+    }
+    // A partial last k-step (k not a multiple of the k-step) goes to the last
+    // wavefront; its K positions past k read zero activations.
+    if (J > Jfull && wave == W - 1) {
+      const uint8_t* ch = pbase + (uint32_t)(Jfull * F::kChunk);
+      WStep w;
+      XStep<G> xt;
       w.codes = load_nt_16(ch + 16 * lane);
       if constexpr (FMT == kFmtNvfp4)
         w.scales = *reinterpret_cast<const uint16_t*>(ch + kNvCodeBytes + 2 * lane);
-      const int64_t kx = j * F::kKStep + kg * (F::kKStep / 4);
 #pragma unroll
       for (int t = 0; t < G; ++t) {
-        const int64_t kk = kx + 8 * t;
-        if (xlane && kk < k)
-          xs.b[t] = *reinterpret_cast<const half8*>(xrow + kk);
-        else
-          xs.b[t] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+        const int64_t kk = (int64_t)Jfull * F::kKStep + kg * (F::kKStep / 4) + 8 * t;
+        const int off = kk < k ? (int)(((int64_t)row * k + kk) * 2) : 0x7FFFFFF0;
+        xt.b[t] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
       }
-    };
-
-    auto compute = [&](const WStep& w, const XStep<G>& xs) {
-      half8 a[G];
-      if constexpr (FMT == kFmtNvfp4)
-        decode_nvfp4_fragment(w.codes, w.scales, a);
-      else
-        decode_fp8_fragment(w.codes, a);
-#pragma unroll
-      for (int t = 0; t < G; ++t)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], xs.b[t], acc, 0, 0, 0);
-    };
-
-    // Ring of D + 1 k-step slots: while slot i is consumed, the D k-steps
-    // after it are in flight.  The loop body is unrolled over the ring so
-    // every slot index is static.
-    constexpr int R = D + 1;
-    WStep ws[R];
-    XStep<G> xs[R];
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-      if (j0 + i < j1) issue(j0 + i, ws[i], xs[i]);
-
-    for (int64_t j = j0; j < j1; j += R) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if (j + i + D < j1) issue(j + i + D, ws[(i + D) % R], xs[(i + D) % R]);
-        if (j + i < j1) compute(ws[i], xs[i]);
-      }
+      compute(w, xt);
     }
   }
 

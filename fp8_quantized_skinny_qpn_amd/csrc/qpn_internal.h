@@ -25,6 +25,7 @@ int gemm_waves_per_panel(uint32_t fmt, int64_t n, int64_t k);
 int gemm_prefetch_depth(uint32_t fmt);
 
 hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, int waves);
+hipError_t launch_stream(uint32_t fmt, bool argmax, const GemmArgs& a, int plan);
 hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t panels, int m, int32_t* argmax,
                                   void* stream);
 
@@ -38,5 +39,6 @@ hipError_t launch_unpack_fp8(const void* packed, int64_t n, int64_t k, uint8_t* 
 hipError_t launch_decode_nvfp4(const uint8_t* codes16, const uint8_t* scales2, int64_t count,
                                uint16_t* out, void* stream);
 hipError_t launch_decode_fp8(const uint8_t* codes16, int64_t count, uint16_t* out, void* stream);
+hipError_t launch_read_ceiling(const void* buf, int64_t count16, uint32_t* sink, void* stream);
 
 }  // namespace qpn

@@ -273,8 +273,8 @@ __global__ __launch_bounds__(256) void decode_nvfp4_kernel(const uint8_t* __rest
   const uint32_t sc2 = (uint32_t)scales2[2 * i] | ((uint32_t)scales2[2 * i + 1] << 8);
   half8 a[4];
   decode_nvfp4_fragment(c, sc2, a);
-  for (int t = 0; t < 4; ++t)
-    for (int e = 0; e < 8; ++e) out[32 * i + 8 * t + e] = __builtin_bit_cast(uint16_t, a[t][e]);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + 32 * i);
+  for (int t = 0; t < 4; ++t) dst[t] = __builtin_bit_cast(u32x4, a[t]);
 }
 
 __global__ __launch_bounds__(256) void decode_fp8_kernel(const uint8_t* __restrict__ codes16,
@@ -289,8 +289,30 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(const uint8_t* __restri
   }
   half8 a[2];
   decode_fp8_fragment(c, a);
-  for (int t = 0; t < 2; ++t)
-    for (int e = 0; e < 8; ++e) out[16 * i + 8 * t + e] = __builtin_bit_cast(uint16_t, a[t][e]);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + 16 * i);
+  for (int t = 0; t < 2; ++t) dst[t] = __builtin_bit_cast(u32x4, a[t]);
+}
+
+// Plain streaming read of `count16` 16-byte words (nontemporal, 8 loads in
+// flight per thread, grid-stride), folded with XOR into one word per block:
+// the measured read ceiling the GEMM kernels are compared with.
+__global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4* __restrict__ buf,
+                                                           int64_t count16,
+                                                           uint32_t* __restrict__ sink) {
+  u32x4 acc = {0, 0, 0, 0};
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 7 * stride < count16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < count16; i += stride) acc ^= __builtin_nontemporal_load(buf + i);
+  uint32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int o = 32; o > 0; o >>= 1) r ^= __shfl_xor(r, o, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, r);
 }
 
 inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
@@ -345,6 +367,12 @@ hipError_t launch_decode_nvfp4(const uint8_t* codes16, const uint8_t* scales2, i
                                uint16_t* out, void* stream) {
   hipLaunchKernelGGL(decode_nvfp4_kernel, dim3(blocks_for(count)), dim3(256), 0,
                      (hipStream_t)stream, codes16, scales2, count, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_ceiling(const void* buf, int64_t count16, uint32_t* sink, void* stream) {
+  hipLaunchKernelGGL(read_ceiling_kernel, dim3(2048), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, count16, sink);
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ def _load():
         "qpn_debug_unpack_fp8": ([vp, i64, i64, vp, vp, vp], i32),
         "qpn_debug_decode_nvfp4": ([vp, vp, i64, vp, vp], i32),
         "qpn_debug_decode_fp8": ([vp, i64, vp, vp], i32),
+        "qpn_debug_read_ceiling": ([vp, sz, vp, vp], i32),
+        "qpn_debug_set_plan": ([i32, i32], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -67,7 +69,8 @@ lib = _load()
 EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_fp8_packed_bytes", "qpn_workspace_bytes", "qpn_gemm_plan", "qpn_pack_nvfp4", "qpn_pack_fp8",
             "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_lmhead_nvfp4", "qpn_debug_unpack_nvfp4",
-            "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8")
+            "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",
+            "qpn_debug_read_ceiling", "qpn_debug_set_plan")
 
 
 def status_string(rc: int) -> str:
@@ -231,3 +234,14 @@ def debug_decode_fp8(codes16: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty((f, 16), dtype=torch.float16, device=codes16.device)
     check(lib.qpn_debug_decode_fp8(_ptr(codes16), f, _ptr(out), _stream(stream)))
     return out
+
+
+def debug_read_ceiling(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """One streaming read of `buf` (the measured read ceiling kernel)."""
+    check(lib.qpn_debug_read_ceiling(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                     _stream(stream)))
+
+
+def debug_set_plan(kernel: int, arg: int = 0):
+    """Force the kernel family / plan of later calls (0 = automatic)."""
+    check(lib.qpn_debug_set_plan(int(kernel), int(arg)))

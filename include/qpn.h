@@ -178,15 +178,33 @@ QPN_API int qpn_debug_unpack_fp8(const void *packed, int64_t n, int64_t k,
  * 2 UE4M3 bytes scales2[2 i ..] (first for codes 0..15, second for 16..31).
  * out[32 i + e] is the FP16 operand the matrix unit receives for code e,
  * which equals E2M1(code) * UE4M3(scale) exactly.  Scale bytes must be
- * <= 0x7E.  Device pointers. */
+ * <= 0x7E.  Device pointers; out must be 16-byte aligned. */
 QPN_API int qpn_debug_decode_nvfp4(const uint8_t *codes16, const uint8_t *scales2,
                            int64_t count, uint16_t *out, void *stream);
 
 /* Runs the GEMM's own FP8 register decode: fragment i is 16 E4M3 bytes;
  * out[16 i + e] is the FP16 operand for byte e, which equals E4M3(byte)
- * exactly for every byte except the NaN codes 0x7F and 0xFF. */
+ * exactly for every byte except the NaN codes 0x7F and 0xFF.  out must be
+ * 16-byte aligned. */
 QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
                          uint16_t *out, void *stream);
+
+/* Diagnostic: forces the kernel family and plan of every later GEMM and
+ * lm_head call in this process, for A/B timing of the designs on identical
+ * inputs.  kernel 0 restores the automatic choice; kernel 1 selects per-lane
+ * activation loads with `arg` wavefronts per 16-row panel (1, 2, 4, 8, 16);
+ * kernel 2 selects LDS-streamed activations with stream plan `arg` (1..8).
+ * An unknown plan makes later calls fail with QPN_ERR_LAUNCH.  Not for
+ * concurrent use with other calls. */
+QPN_API int qpn_debug_set_plan(int kernel, int arg);
+
+/* Diagnostic: reads `bytes` (a multiple of 16) of device memory at `buf`
+ * once with the same nontemporal 16-byte loads the GEMM kernels use and
+ * XORs a meaningless fold into *sink.  Timing it gives the measured HBM read
+ * ceiling that bandwidth is also reported against, as the taozi.news and
+ * aiwitness.kr pages report theirs against a measured read-only limit. */
+QPN_API int qpn_debug_read_ceiling(const void *buf, size_t bytes, uint32_t *sink,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(qpn):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 17
     lib = ctypes.CDLL(qpn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -154,6 +154,9 @@ def test_debug_argument_errors(qpn):
     assert L.qpn_debug_decode_fp8(v(A16), 0, v(A16), None) == 0
     assert L.qpn_debug_unpack_nvfp4(v(A256), 16, 24, v(A16), v(A16), v(A16), None) == 2
     assert L.qpn_debug_unpack_fp8(v(A16), 16, 16, v(A16), v(A16), None) == 3
+    assert L.qpn_debug_read_ceiling(v(A16), 24, v(A16), None) == 2
+    assert L.qpn_debug_read_ceiling(v(A16 + 4), 32, v(A16), None) == 3
+    assert L.qpn_debug_decode_fp8(v(A16), 4, v(A16 + 2), None) == 3
 
 
 def test_valid_call_without_gpu_reports_device_error(qpn):
