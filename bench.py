@@ -8,12 +8,23 @@ C ABI.  Weights are synthetic N(0, 0.02) packed on the GPU; every call reads a
 different packed copy (>= 1 GiB of copies per shape) so the 256 MB Infinity
 Cache cannot serve the weights.  Inputs are resident in HBM before timing.
 
+The launches of the timed region are recorded once into a HIP graph (through
+torch.cuda.CUDAGraph, on the stream the library launches on) and replayed, so
+host launch overhead stays out of the measurement; the graph holds exactly
+`--steps` steps.
+
 value = algorithmic weight bytes of one step (codes + UE4M3 scales + the
-4-byte tensor scale of each call) / time of one step, in GB/s (1e9 B/s).
-The roofline object reports the dominant kernel: its per-launch algorithmic
-bytes over its average launch duration, timed live with HIP events on the
-stream the kernels run on.  The CPU baseline times the FP64 oracle on a
-bounded row sample of the same six calls.
+4-byte tensor scale of each call) / wall time of one step, in GB/s (1e9 B/s).
+
+roofline: the dominant kernel (largest share of the step).  Its average
+launch duration is timed with HIP events around a graph of back-to-back
+launches of that call (rotating copies) on the launch stream; achieved =
+its algorithmic bytes per launch / that average.  traffic comes from the
+committed rocprofv3 PMC summary when it matches the current kernel source.
+
+cpu_baseline: the FP64 oracle (test infrastructure, C with OpenMP over rows)
+computing one complete headline step (all six calls, every row), repeated
+until about ten seconds of CPU time have been spent.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
 """
@@ -33,6 +44,7 @@ sys.path.insert(0, HERE)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, decimal GB/s
 ROTATE_BYTES = 1 << 30          # >= 1 GiB of distinct packed copies per shape
 METRIC = "effective weight GB/s and % of HBM peak, NVFP4 & FP8 skinny GEMM at M=1/8"
+BATCH = 44                      # launches per per-call timing graph (2 rotations)
 
 HEADLINE = [  # (name, n, k, format)
     ("gate_up_K5120_N17408", 17408, 5120, "nvfp4"),
@@ -42,12 +54,10 @@ HEADLINE_M = (1, 4, 8)
 
 EXTRA = [  # measured only with --extra (the other configurations' timings)
     ("cfg1_K2048_N2048", 2048, 2048, "nvfp4", (1,)),
-    ("fp8_K5120_N6144", 6144, 5120, "fp8", (1, 2, 4)),
-    ("fp8_K5120_N5120", 5120, 5120, "fp8", (1, 2, 4)),
+    ("fp8_K5120_N6144", 6144, 5120, "fp8", (1, 2, 4, 8)),
+    ("fp8_K5120_N5120", 5120, 5120, "fp8", (1, 2, 4, 8)),
     ("layer_qkv_fp8_K5120_N7168", 7168, 5120, "fp8", (8,)),
-    ("layer_o_fp8_K5120_N5120", 5120, 5120, "fp8", (8,)),
     ("layer_gateup_nvfp4_K5120_N34816", 34816, 5120, "nvfp4", (8,)),
-    ("layer_down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4", (8,)),
 ]
 LMHEAD = ("lmhead_nvfp4_K5120_N151936", 151936, 5120)
 
@@ -84,7 +94,6 @@ class Shape:
         self.xm = {m: self.x[:m].contiguous() for m in ms}
         self.bytes = algo_bytes(n, k, fmt)
         self.i = 0
-        self.waves = None
 
     def next_copy(self):
         pw = self.copies[self.i]
@@ -92,67 +101,74 @@ class Shape:
         return pw
 
 
-def run_step(qpn, shapes, events=None):
+def one_step(qpn, shapes):
     """One pass: every (shape, M) call once, each on the next rotated copy."""
     for s in shapes:
         for m in s.ms:
-            pw = s.next_copy()
-            if events is not None:
-                events[(s.name, m)][0].append(_record())
-            qpn.gemm(pw, s.xm[m], out=s.y[m])
-            if events is not None:
-                events[(s.name, m)][1].append(_record())
+            qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m])
 
 
-_torch = None
+def capture(torch, fn):
+    """Record the launches fn() makes into a graph (on torch's capture stream,
+    which is the stream the library launches on)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
-def _record():
-    e = _torch.cuda.Event(enable_timing=True)
-    e.record()
-    return e
+def time_graph(torch, g, reps):
+    """Per-replay times (s) of graph g, measured with HIP events on the stream
+    the graph is replayed on."""
+    out = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e-3)
+    return out
 
 
-def cpu_baseline(shapes, budget_s=12.0):
-    """FP64 oracle on a bounded row sample of the same calls (CPU leg only)."""
+def time_call(qpn, torch, s, m, batch=BATCH, reps=5):
+    """Average launch time (s) of one (shape, M) call in back-to-back graphs."""
+    g = capture(torch, lambda: [qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m]) for _ in range(batch)])
+    g.replay()
+    torch.cuda.synchronize()
+    per = [t / batch for t in time_graph(torch, g, reps)]
+    del g
+    return per
+
+
+def cpu_baseline(min_seconds=10.0):
+    """FP64 oracle computing whole headline steps (CPU leg only)."""
     import oracle
     from fp8_quantized_skinny_qpn_amd import synth
-    threads = oracle.threads()
-    # calibrate rows per call so the whole sample takes about budget_s seconds
-    total_t, total_b, sample = 0.0, 0, []
-    rows_per_call = 64
-    s0 = shapes[0]
-    rows = np.arange(rows_per_call)
-    w = synth.weight_rows(s0.n, s0.k, rows, seed=0)
-    g = np.float32(1e-4)
-    c, sc = oracle.pack_nvfp4_rows(w, g)
-    x = synth.activations(8, s0.k, seed=0)
-    t = time.perf_counter()
-    oracle.gemm_nvfp4(c, sc, g, x)
-    dt = time.perf_counter() - t
-    per_mac = dt / (rows_per_call * s0.k * 8)
-    macs_total = sum(s.k * m for s in shapes for m in s.ms)
-    rows_per_call = int(max(16, min(4096, budget_s / (per_mac * macs_total))))
-    for s in shapes:
-        rows = np.arange(rows_per_call) * (s.n // rows_per_call)
-        w = synth.weight_rows(s.n, s.k, rows, seed=0)
-        g, _ = oracle.nvfp4_tensor_scale(w)  # scale of the sample; timing depends on bytes only
-        c, sc = oracle.pack_nvfp4_rows(w, g)
-        for m in s.ms:
-            x = synth.activations(8, s.k, seed=0)[:m]
-            t = time.perf_counter()
-            oracle.gemm_nvfp4(c, sc, g, x)
-            total_t += time.perf_counter() - t
-            total_b += algo_bytes(rows_per_call, s.k, "nvfp4") - 4
+    packed = []
+    for name, n, k, _ in HEADLINE:
+        w = synth.weights(n, k, seed=0)
+        codes, scales, g = oracle.pack_nvfp4(w)
+        del w
+        packed.append((name, n, k, codes, scales, g, synth.activations(8, k, seed=0)))
+    steps, total_t = 0, 0.0
+    while total_t < min_seconds or steps == 0:
+        for name, n, k, codes, scales, g, x8 in packed:
+            for m in HEADLINE_M:
+                t = time.perf_counter()
+                oracle.gemm_nvfp4(codes, scales, g, x8[:m])
+                total_t += time.perf_counter() - t
+        steps += 1
+    step_bytes = sum(algo_bytes(n, k, "nvfp4") for _, n, k, *_ in packed) * len(HEADLINE_M)
     return {
-        "value": round(total_b / total_t / 1e9, 6),
+        "value": round(step_bytes * steps / total_t / 1e9, 6),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": (f"FP64 oracle GEMM (qpn_oracle_gemm_nvfp4, OpenMP over rows) on {rows_per_call} "
-                   f"evenly spaced rows of each of the 6 headline calls "
-                   f"({', '.join(s.name for s in shapes)} x M={list(HEADLINE_M)}); "
-                   f"{total_t:.1f} s of CPU time; GB/s over the sampled rows' weight bytes"),
+        "sample": (f"{steps} complete headline step(s) (6 calls, every row) on the FP64 oracle "
+                   f"(C, OpenMP over rows), {total_t:.1f} s of wall time; packing untimed"),
     }
 
 
@@ -172,10 +188,24 @@ def traffic_for(kernel_name):
     return ent.get("bytes_per_launch")
 
 
+def read_ceiling(qpn, torch):
+    """Measured read ceiling: nontemporal 16-byte loads streaming a 2 GiB
+    buffer (far larger than the 256 MB Infinity Cache)."""
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        qpn.debug_read_ceiling(buf, sink)
+    g = capture(torch, lambda: qpn.debug_read_ceiling(buf, sink))
+    ts = time_graph(torch, g, 7)
+    del g, buf
+    torch.cuda.empty_cache()
+    return (2 << 30) / float(np.median(ts)) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--extra", action="store_true", help="also time the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -188,8 +218,6 @@ def main():
         sys.exit(2)
 
     import torch
-    global _torch
-    _torch = torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -197,66 +225,58 @@ def main():
 
     log("setting up headline shapes")
     shapes = [Shape(qpn, torch, name, n, k, fmt, HEADLINE_M) for name, n, k, fmt in HEADLINE]
+    for _ in range(2):
+        one_step(qpn, shapes)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        run_step(qpn, shapes)
-    torch.cuda.synchronize()
-
-    # timed region: exactly `steps` steps, synchronised on both sides, with
-    # an event pair around every launch
-    events = {(s.name, m): ([], []) for s in shapes for m in s.ms}
+    # warmup and timed graphs hold exactly W and K steps
+    g_warm = capture(torch, lambda: [one_step(qpn, shapes) for _ in range(max(1, args.warmup))])
+    g_timed = capture(torch, lambda: [one_step(qpn, shapes) for _ in range(args.steps)])
+    if args.warmup > 0:
+        g_warm.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step(qpn, shapes, events)
+    g_timed.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
+    del g_warm, g_timed
     step_s = (t1 - t0) / args.steps
     step_bytes = sum(s.bytes * len(s.ms) for s in shapes)
     value = step_bytes / step_s / 1e9
 
-    breakdown = {}
-    per_kernel = {}
+    # per-call launch times
+    breakdown, per_kernel = {}, {}
     for s in shapes:
         for m in s.ms:
-            st, en = events[(s.name, m)]
-            us = [a.elapsed_time(b) * 1e3 for a, b in zip(st, en)]
-            med = float(np.median(us))
-            kname = qpn.kernel_name(s.fmt, s.n, s.k, lmhead=False)
+            per = time_call(qpn, torch, s, m)
+            med = float(np.median(per))
+            kname = qpn.kernel_name(s.fmt, m, s.n, s.k, lmhead=False)
             breakdown[f"{s.name}_M{m}"] = {
-                "kernel": kname, "us_median": round(med, 3),
-                "us_p10": round(float(np.percentile(us, 10)), 3),
-                "us_p90": round(float(np.percentile(us, 90)), 3),
-                "GBps": round(s.bytes / med / 1e3, 1),
-                "pct_hbm_peak": round(100 * s.bytes / med / 1e3 / HBM_PEAK_GBPS, 1),
+                "kernel": kname, "us": round(med * 1e6, 3),
+                "us_min": round(min(per) * 1e6, 3), "us_max": round(max(per) * 1e6, 3),
+                "GBps": round(s.bytes / med / 1e9, 1),
+                "pct_hbm_peak": round(100 * s.bytes / med / 1e9 / HBM_PEAK_GBPS, 1),
                 "weight_bytes": s.bytes, "rotated_copies": len(s.copies),
             }
-            k = per_kernel.setdefault(kname, {"us": [], "bytes": s.bytes})
-            k["us"] += us
-    dom = max(per_kernel, key=lambda kn: sum(per_kernel[kn]["us"]))
+            k = per_kernel.setdefault(kname, {"t": [], "bytes": s.bytes, "calls": []})
+            k["t"] += per
+            k["calls"].append(f"{s.name}_M{m}")
+    dom = max(per_kernel, key=lambda kn: float(np.mean(per_kernel[kn]["t"])) * len(per_kernel[kn]["calls"]))
     dk = per_kernel[dom]
-    avg_us = float(np.mean(dk["us"]))
-    achieved = dk["bytes"] / avg_us / 1e3
-    traffic = traffic_for(dom)
+    avg_s = float(np.mean(dk["t"]))
+    achieved = dk["bytes"] / avg_s / 1e9
 
     extra = {}
     if args.extra:
         for name, n, k, fmt, ms in EXTRA:
             log(f"extra: {name}")
             sh = Shape(qpn, torch, name, n, k, fmt, ms)
-            ev = {(name, m): ([], []) for m in ms}
-            for _ in range(5):
-                run_step(qpn, [sh])
-            for _ in range(50):
-                run_step(qpn, [sh], ev)
-            torch.cuda.synchronize()
             for m in ms:
-                us = [a.elapsed_time(b) * 1e3 for a, b in zip(*ev[(name, m)])]
-                med = float(np.median(us))
-                extra[f"{name}_M{m}"] = {"us_median": round(med, 3), "GBps": round(sh.bytes / med / 1e3, 1),
-                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e3 / HBM_PEAK_GBPS, 1)}
+                per = time_call(qpn, torch, sh, m)
+                med = float(np.median(per))
+                extra[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k), "us": round(med * 1e6, 3),
+                                         "GBps": round(sh.bytes / med / 1e9, 1),
+                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
             del sh
             torch.cuda.empty_cache()
         from fp8_quantized_skinny_qpn_amd import synth
@@ -274,41 +294,22 @@ def main():
             lg = torch.empty((m, n), dtype=torch.float16, device="cuda")
             am = torch.empty((m,), dtype=torch.int32, device="cuda")
             ws = torch.empty(qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, m, n, k), dtype=torch.uint8, device="cuda")
-            us = []
-            for it in range(40):
-                e0 = _record()
-                qpn.lmhead_nvfp4(copies[it % 3], xm, lg, am, ws)
-                e1 = _record()
-                if it >= 10:
-                    us.append((e0, e1))
-            torch.cuda.synchronize()
-            t = [a.elapsed_time(bb) * 1e3 for a, bb in us]
-            med = float(np.median(t))
-            extra[f"{name}_M{m}"] = {"us_median": round(med, 3), "GBps": round(b / med / 1e3, 1),
-                                     "pct_hbm_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBPS, 1)}
+            qpn.lmhead_nvfp4(copies[0], xm, lg, am, ws)
+            g = capture(torch, lambda: [qpn.lmhead_nvfp4(copies[i % 3], xm, lg, am, ws) for i in range(12)])
+            per = [t / 12 for t in time_graph(torch, g, 5)]
+            del g
+            med = float(np.median(per))
+            extra[f"{name}_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
+                                     "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
+        del copies, pw
+        torch.cuda.empty_cache()
 
-    # measured read ceiling: the same nontemporal 16-byte loads streaming a
-    # 2 GiB buffer (far larger than the 256 MB Infinity Cache)
-    ceil_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    for _ in range(2):
-        qpn.debug_read_ceiling(ceil_buf, sink)
-    ce = []
-    for _ in range(5):
-        e0 = _record()
-        qpn.debug_read_ceiling(ceil_buf, sink)
-        e1 = _record()
-        ce.append((e0, e1))
-    torch.cuda.synchronize()
-    ceil_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ce]))
-    read_ceiling = ceil_buf.numel() / ceil_us / 1e3
-    del ceil_buf
-    torch.cuda.empty_cache()
+    ceiling = read_ceiling(qpn, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(shapes)
+        cpu = cpu_baseline()
 
     out = {
         "metric": METRIC,
@@ -324,8 +325,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 1),
-        "read_ceiling_GBps": round(read_ceiling, 1),
-        "pct_read_ceiling": round(100 * value / read_ceiling, 1),
+        "read_ceiling_GBps": round(ceiling, 1),
+        "pct_read_ceiling": round(100 * value / ceiling, 1),
         "config": {
             "workload": "nvfp4_skinny_gemm K5120->N17408 and K17408->N5120, M in {1,4,8}",
             "calls_per_step": len(shapes) * len(HEADLINE_M),
@@ -333,19 +334,22 @@ def main():
             "activations": "fp16 N(0,1), seed 0",
             "step_weight_bytes": step_bytes,
             "rotated_copies_per_shape": [len(s.copies) for s in shapes],
-            "waves_per_panel": {s.name: qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, s.n, s.k)[1] for s in shapes},
+            "timing": "HIP graph of exactly `steps` steps, replayed once between device synchronisations",
+            "plans": {f"{s.name}_M{m}": qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, s.n, s.k).__dict__
+                      for s in shapes for m in s.ms},
         },
         "roofline": {
             "bound": "hbm",
             "kernel": dom,
+            "calls": dk["calls"],
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
+            "traffic": traffic_for(dom),
             "algorithmic_bytes_per_launch": dk["bytes"],
-            "avg_launch_us": round(avg_us, 3),
-            "launches_timed": len(dk["us"]),
+            "avg_launch_us": round(avg_s * 1e6, 3),
+            "launches_timed": len(dk["t"]) * BATCH,
         },
         "cpu_baseline": cpu,
         "breakdown": breakdown,

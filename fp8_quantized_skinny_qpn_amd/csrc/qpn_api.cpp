@@ -45,18 +45,11 @@ int device_check() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QPN_OK : QPN_ERR_LAUNCH; }
 
-// Plan override for A/B measurements (qpn_debug_set_plan): 0 = automatic,
-// 1 = per-lane activation loads with `g_plan_arg` wavefronts per panel,
-// 2 = LDS-streamed activations with stream plan `g_plan_arg`.
-std::atomic<int> g_plan_kernel{0};
-std::atomic<int> g_plan_arg{0};
+// Plan override for A/B measurements (qpn_debug_set_plan): 0 = automatic.
+std::atomic<int> g_plan{0};
 
 hipError_t dispatch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a) {
-  const int kern = g_plan_kernel.load(std::memory_order_relaxed);
-  const int arg = g_plan_arg.load(std::memory_order_relaxed);
-  if (kern == 1) return launch_gemm(fmt, argmax, a, arg);
-  if (kern == 2) return launch_stream(fmt, argmax, a, arg);
-  return launch_gemm(fmt, argmax, a, gemm_waves_per_panel(fmt, a.n, a.k));
+  return launch_gemm(fmt, argmax, a, g_plan.load(std::memory_order_relaxed));
 }
 
 int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, const void* y,
@@ -123,8 +116,9 @@ size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
   }
 }
 
-int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups,
-                  int* waves_per_workgroup, int* prefetch_depth) {
+int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
+                  int* panels_per_workgroup, int* prefetch_depth, int* lds_slots,
+                  int* activation_rows) {
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
   uint32_t fmt;
   switch (op) {
@@ -139,9 +133,15 @@ int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups,
       break;
     default: return QPN_ERR_SHAPE;
   }
-  if (workgroups) *workgroups = panels_of(n);
-  if (waves_per_workgroup) *waves_per_workgroup = gemm_waves_per_panel(fmt, n, k);
-  if (prefetch_depth) *prefetch_depth = gemm_prefetch_depth(fmt);
+  const int forced = g_plan.load(std::memory_order_relaxed);
+  GemmPlan pl;
+  if (!gemm_plan_info(forced > 0 ? forced : gemm_auto_plan(fmt, m, n, k), &pl)) return QPN_ERR_SHAPE;
+  if (workgroups) *workgroups = (panels_of(n) + pl.panels_per_workgroup - 1) / pl.panels_per_workgroup;
+  if (waves_per_panel) *waves_per_panel = pl.waves_per_panel;
+  if (panels_per_workgroup) *panels_per_workgroup = pl.panels_per_workgroup;
+  if (prefetch_depth) *prefetch_depth = pl.depth;
+  if (lds_slots) *lds_slots = gemm_ring_slots(fmt, pl.waves_per_panel, m, pl.lds_slots);
+  if (activation_rows) *activation_rows = gemm_activation_rows(m);
   return QPN_OK;
 }
 
@@ -241,16 +241,16 @@ int qpn_debug_decode_fp8(const uint8_t* codes16, int64_t count, uint16_t* out, v
   return launch_status(launch_decode_fp8(codes16, count, out, stream));
 }
 
-int qpn_debug_set_plan(int kernel, int arg) {
-  if (kernel < 0 || kernel > 2) return QPN_ERR_SHAPE;
-  g_plan_kernel.store(kernel, std::memory_order_relaxed);
-  g_plan_arg.store(arg, std::memory_order_relaxed);
+int qpn_debug_set_plan(int plan) {
+  GemmPlan pl;
+  if (plan != 0 && !gemm_plan_info(plan, &pl)) return QPN_ERR_SHAPE;
+  g_plan.store(plan, std::memory_order_relaxed);
   return QPN_OK;
 }
 
 int qpn_debug_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink) return QPN_ERR_NULL;
-  if (bytes == 0 || bytes % 16 != 0) return QPN_ERR_SHAPE;
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40)) return QPN_ERR_SHAPE;
   if (!aligned(buf, 16) || !aligned(sink, 4)) return QPN_ERR_ALIGN;
   int rc = device_check();
   if (rc != QPN_OK) return rc;

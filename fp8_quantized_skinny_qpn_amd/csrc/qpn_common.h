@@ -1,7 +1,7 @@
 // qpn_common.h -- packed-blob layout and device helpers shared by the QPN
 // kernels (pack, GEMM, lm_head, debug exports).
 //
-// Packed layout v1 (designed for CDNA4; the pages fix no layout: the taozi.news
+// Packed layout v2 (designed for CDNA4; the pages fix no layout: the taozi.news
 // page, section "自研 QPN 内核", only asks that weights stay compressed in HBM
 // and are expanded in registers in small pieces).
 //
@@ -11,6 +11,12 @@
 //   bytes one wavefront fetches with a single 16-byte-per-lane load, so each
 //   load instruction reads 1 KiB of contiguous codes.
 //
+//   Chunks are stored step-major: chunk (p, j) is number j * P + p, so the
+//   chunks of one k-step of all panels are adjacent.  Workgroups that work
+//   on neighbouring panels at the same pace then read neighbouring bytes;
+//   a panel-major order (each panel's K run contiguous) measured up to 30%
+//   slower on gfx950 for the same bytes.
+//
 //   Lane l of a wavefront owns row (l & 15) of the panel and K group (l >> 4).
 //
 //   NVFP4, k-step = 128 K elements, chunk = 1152 bytes:
@@ -19,11 +25,12 @@
 //         nibble first;
 //     bytes [1024 + 2 l, 1024 + 2 l + 2): the two UE4M3 scales of those 32
 //         codes (first for e < 16).
-//     Chunk (p, j) starts at 256 + (p * J + j) * 1152, J = ceil(k / 128).
+//     Chunk (p, j) starts at 256 + (j * P + p) * 1152, J = ceil(k / 128).
 //   FP8, k-step = 64 K elements, chunk = 1024 bytes:
 //     bytes [16 l, 16 l + 16): the 16 E4M3 codes of row 16p + (l & 15) at
 //         K = 64 j + 16 (l >> 4) + e, code e in byte e;
-//     row scales: float[16 P] at byte 256; chunks start at codes_offset.
+//     row scales: float[16 P] at byte 256; chunk (p, j) starts at
+//     codes_offset + (j * P + p) * 1024.
 //   Rows past n and K past k are padding: zero codes and zero scales.
 #pragma once
 
@@ -34,7 +41,7 @@
 namespace qpn {
 
 constexpr uint32_t kMagic = 0x314E5051u;  // "QPN1" little-endian
-constexpr uint32_t kLayoutVersion = 1;
+constexpr uint32_t kLayoutVersion = 2;
 constexpr uint32_t kFmtNvfp4 = 1;
 constexpr uint32_t kFmtFp8 = 2;
 
@@ -74,6 +81,11 @@ static_assert(sizeof(BlobHeader) == kHeaderBytes, "header is 256 bytes");
 __host__ __device__ inline int64_t panels_of(int64_t n) { return (n + kPanelRows - 1) / kPanelRows; }
 __host__ __device__ inline int64_t nv_ksteps_of(int64_t k) { return (k + kNvKStep - 1) / kNvKStep; }
 __host__ __device__ inline int64_t f8_ksteps_of(int64_t k) { return (k + kF8KStep - 1) / kF8KStep; }
+
+// Index of chunk (panel p, k-step j) among the P * J chunks (step-major).
+__host__ __device__ inline uint64_t chunk_index(int64_t p, int64_t j, int64_t P) {
+  return (uint64_t)j * (uint64_t)P + (uint64_t)p;
+}
 
 __host__ __device__ inline uint64_t nv_blob_bytes(int64_t n, int64_t k) {
   return (uint64_t)kHeaderBytes + (uint64_t)panels_of(n) * nv_ksteps_of(k) * kNvChunkBytes;

@@ -17,15 +17,33 @@ struct GemmArgs {
   void* stream;
 };
 
-// Wavefronts per 16-row panel chosen for an (n, k) call; a pure function of
-// the shape, so launch geometry never depends on anything else.
-int gemm_waves_per_panel(uint32_t fmt, int64_t n, int64_t k);
+// One compiled GEMM configuration: W compute wavefronts per 16-row panel,
+// G panels per workgroup (plus one loader wavefront), D k-step windows of
+// weight loads in flight per wavefront, NB activation windows in the LDS ring.
+struct GemmPlan {
+  int waves_per_panel;
+  int panels_per_workgroup;
+  int depth;
+  int lds_slots;
+};
 
-// k-steps each wavefront keeps in flight (a compile-time constant per format).
-int gemm_prefetch_depth(uint32_t fmt);
+// The plan used when none is forced: a pure function of the call's shape,
+// so launch geometry never depends on anything else.
+int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k);
 
-hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, int waves);
-hipError_t launch_stream(uint32_t fmt, bool argmax, const GemmArgs& a, int plan);
+// Activation rows staged per LDS window for m rows (1, 2, 4 or 8).
+int gemm_activation_rows(int m);
+
+// Activation ring slots a plan with `slots` gets for m rows (fewer when its
+// windows are wide).
+int gemm_ring_slots(uint32_t fmt, int waves_per_panel, int m, int slots);
+
+// Plan `id` (1-based) of the compiled table; false if there is none.
+bool gemm_plan_info(int id, GemmPlan* out);
+
+// Launch the GEMM (and, with `argmax`, the per-panel argmax keys) with plan
+// `plan`, or the automatic plan when `plan` is 0.
+hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, int plan);
 hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t panels, int m, int32_t* argmax,
                                   void* stream);
 

@@ -43,7 +43,7 @@ def _load():
         "qpn_nvfp4_packed_bytes": ([i64, i64], sz),
         "qpn_fp8_packed_bytes": ([i64, i64], sz),
         "qpn_workspace_bytes": ([i32, i32, i64, i64], sz),
-        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp], i32),
+        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp], i32),
         "qpn_pack_nvfp4": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_pack_fp8": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
@@ -54,7 +54,7 @@ def _load():
         "qpn_debug_decode_nvfp4": ([vp, vp, i64, vp, vp], i32),
         "qpn_debug_decode_fp8": ([vp, i64, vp, vp], i32),
         "qpn_debug_read_ceiling": ([vp, sz, vp, vp], i32),
-        "qpn_debug_set_plan": ([i32, i32], i32),
+        "qpn_debug_set_plan": ([i32], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -104,21 +104,37 @@ def workspace_bytes(op: int, m: int, n: int, k: int) -> int:
     return int(lib.qpn_workspace_bytes(op, m, n, k))
 
 
-def gemm_plan(op: int, m: int, n: int, k: int):
-    """(workgroups, waves_per_workgroup, prefetch_depth) the library launches."""
+@dataclass(frozen=True)
+class Plan:
+    """Launch plan of one call, as the library reports it."""
+    workgroups: int
+    waves_per_panel: int
+    panels_per_workgroup: int
+    prefetch_depth: int
+    lds_slots: int
+    activation_rows: int
+
+    @property
+    def waves_per_workgroup(self) -> int:
+        return self.waves_per_panel * self.panels_per_workgroup + 1
+
+
+def gemm_plan(op: int, m: int, n: int, k: int) -> Plan:
+    """The launch plan the library uses for a call of kind `op`."""
     wg = ctypes.c_int64()
-    w = ctypes.c_int()
-    d = ctypes.c_int()
-    check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), ctypes.byref(w), ctypes.byref(d)))
-    return wg.value, w.value, d.value
+    outs = [ctypes.c_int() for _ in range(5)]
+    check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *[ctypes.byref(o) for o in outs]))
+    return Plan(wg.value, *[o.value for o in outs])
 
 
-def kernel_name(fmt: str, n: int, k: int, lmhead: bool = False) -> str:
+def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:
     """Demangled name (template part) of the GEMM kernel a call launches."""
     op = OP_LMHEAD_NVFP4 if lmhead else (OP_GEMM_NVFP4 if fmt == FMT_NVFP4 else OP_GEMM_FP8)
-    _, w, d = gemm_plan(op, 1, n, k)
+    pl = gemm_plan(op, m, n, k)
     f = 1 if fmt == FMT_NVFP4 else 2
-    return f"qpn::skinny_gemm_kernel<{f}u, {w}, {d}, {'true' if lmhead else 'false'}>"
+    return (f"qpn::skinny_gemm_kernel<{f}u, {pl.waves_per_panel}, {pl.panels_per_workgroup}, "
+            f"{pl.prefetch_depth}, {pl.lds_slots}, {pl.activation_rows}, "
+            f"{'true' if lmhead else 'false'}>")
 
 
 @dataclass
@@ -242,6 +258,6 @@ def debug_read_ceiling(buf: torch.Tensor, sink: torch.Tensor, stream=None):
                                      _stream(stream)))
 
 
-def debug_set_plan(kernel: int, arg: int = 0):
-    """Force the kernel family / plan of later calls (0 = automatic)."""
-    check(lib.qpn_debug_set_plan(int(kernel), int(arg)))
+def debug_set_plan(plan: int):
+    """Force the launch plan of later calls (0 = automatic)."""
+    check(lib.qpn_debug_set_plan(int(plan)))

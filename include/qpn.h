@@ -100,13 +100,18 @@ QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
  * Returns (size_t)-1 for an unknown op or invalid shape.  Pure host. */
 QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
 
-/* Launch geometry a call of kind `op` (QPN_OP_*) uses for (m, n, k): the
- * number of workgroups (one per 16-row panel), wavefronts per workgroup (they
- * split the panel's K range) and the k-steps each wavefront keeps in flight.
- * A pure function of the shape, independent of any declared maximum.  Any
- * output pointer may be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
+/* Launch plan a call of kind `op` (QPN_OP_*) uses for (m, n, k): the number
+ * of workgroups; the compute wavefronts per 16-row panel (they interleave
+ * the panel's k-steps); the panels per workgroup (a workgroup also has one
+ * wavefront that stages activations in LDS); the k-steps each compute
+ * wavefront keeps in flight; the activation windows in the LDS ring; and
+ * the activation rows staged per window (1, 2, 4 or 8 >= m).  A pure
+ * function of the shape (and of a plan forced with qpn_debug_set_plan),
+ * independent of any declared maximum.  Any output pointer may be NULL.
+ * Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
-                          int *waves_per_workgroup, int *prefetch_depth);
+                          int *waves_per_panel, int *panels_per_workgroup,
+                          int *prefetch_depth, int *lds_slots, int *activation_rows);
 
 /* NVFP4 pack ("pure round" quantisation, lcz.me quantisation-option table,
  * NVFP4-NVIDIA row; format per the lcz.me NVFP4 support table).
@@ -189,20 +194,20 @@ QPN_API int qpn_debug_decode_nvfp4(const uint8_t *codes16, const uint8_t *scales
 QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
                          uint16_t *out, void *stream);
 
-/* Diagnostic: forces the kernel family and plan of every later GEMM and
- * lm_head call in this process, for A/B timing of the designs on identical
- * inputs.  kernel 0 restores the automatic choice; kernel 1 selects per-lane
- * activation loads with `arg` wavefronts per 16-row panel (1, 2, 4, 8, 16);
- * kernel 2 selects LDS-streamed activations with stream plan `arg` (1..8).
- * An unknown plan makes later calls fail with QPN_ERR_LAUNCH.  Not for
- * concurrent use with other calls. */
-QPN_API int qpn_debug_set_plan(int kernel, int arg);
+/* Diagnostic: forces the launch plan (wavefronts per panel, panels per
+ * workgroup, prefetch depth; ids 1..8) of every later GEMM and lm_head call
+ * in this process, for A/B timing of configurations on identical inputs.
+ * 0 restores the automatic choice.  Returns QPN_ERR_SHAPE for an unknown id
+ * (nothing changes).  Not for concurrent use with other calls. */
+QPN_API int qpn_debug_set_plan(int plan);
 
-/* Diagnostic: reads `bytes` (a multiple of 16) of device memory at `buf`
- * once with the same nontemporal 16-byte loads the GEMM kernels use and
- * XORs a meaningless fold into *sink.  Timing it gives the measured HBM read
- * ceiling that bandwidth is also reported against, as the taozi.news and
- * aiwitness.kr pages report theirs against a measured read-only limit. */
+/* Diagnostic: reads `bytes` (a multiple of 16, at most 2^40) of device
+ * memory at `buf` once with the same nontemporal 16-byte loads the GEMM
+ * kernels use; *sink is written only if a fold of the data equals a fixed
+ * constant (so the loads cannot be elided).  Timing it gives the measured
+ * HBM read ceiling that bandwidth is also reported against, as the
+ * taozi.news and aiwitness.kr pages report theirs against a measured
+ * read-only limit. */
 QPN_API int qpn_debug_read_ceiling(const void *buf, size_t bytes, uint32_t *sink,
                                    void *stream);
 

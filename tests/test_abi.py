@@ -36,7 +36,7 @@ def test_status_strings(qpn):
         s = qpn.status_string(rc)
         assert s.startswith("QPN_")
     assert "unknown" in qpn.status_string(99)
-    assert qpn.lib.qpn_layout_version() == 1
+    assert qpn.lib.qpn_layout_version() == 2
 
 
 def test_packed_sizes(qpn):
@@ -60,16 +60,32 @@ def test_packed_sizes(qpn):
 
 
 def test_gemm_plan(qpn):
-    # one workgroup per 16-row panel; waves split K; a pure function of the shape
-    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)[0] == 1088
-    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)[0] == 320
-    for m in (1, 4, 8):
-        assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, 5120, 17408) == qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)
-    for op, n, k in [(1, 17408, 5120), (1, 5120, 17408), (2, 6144, 5120), (3, 151936, 5120), (1, 17, 16)]:
-        wg, w, d = qpn.gemm_plan(op, 8, n, k)
-        assert w in (1, 2, 4, 8, 16) and d >= 1
+    # workgroups cover the 16-row panels; a pure function of the shape
+    for op, m, n, k in [(1, 1, 17408, 5120), (1, 8, 17408, 5120), (1, 4, 5120, 17408),
+                        (2, 2, 6144, 5120), (3, 8, 151936, 5120), (1, 3, 17, 16), (2, 7, 24, 8)]:
+        pl = qpn.gemm_plan(op, m, n, k)
+        panels = -(-n // 16)
+        assert pl.workgroups == -(-panels // pl.panels_per_workgroup)
+        assert pl.waves_per_panel in (1, 2, 4, 8) and pl.panels_per_workgroup >= 1
+        assert 2 <= pl.waves_per_workgroup <= 16
+        assert pl.prefetch_depth >= 1 and pl.lds_slots >= 2
+        assert pl.activation_rows in (1, 2, 4, 8) and pl.activation_rows >= m
+        assert pl.activation_rows < 2 * m or m == 0
+        assert pl == qpn.gemm_plan(op, m, n, k)
+        name = qpn.kernel_name(qpn.FMT_NVFP4 if op != 2 else qpn.FMT_FP8, m, n, k, lmhead=op == 3)
+        assert name.startswith("qpn::skinny_gemm_kernel<") and name.endswith(">")
     with pytest.raises(qpn.QpnError):
         qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 16, 24)
+    with pytest.raises(qpn.QpnError):
+        qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 9, 16, 32)
+
+
+def test_plan_override_rejects_unknown_ids(qpn):
+    with pytest.raises(qpn.QpnError):
+        qpn.debug_set_plan(10 ** 6)
+    with pytest.raises(qpn.QpnError):
+        qpn.debug_set_plan(-1)
+    qpn.debug_set_plan(0)
 
 
 def test_workspace_sizes(qpn):

@@ -140,3 +140,24 @@ def test_lmhead_full_vocab(m):
     rows = np.random.default_rng(0).choice(n, 4096, replace=False)
     parity(lg[:, rows], y_ref[:, rows], f"lmhead full m={m} (sampled logits)")
     _check_argmax(am, lg, y_ref, f"lmhead full m={m}")
+
+
+@pytest.mark.parametrize("plan", list(range(1, 9)))
+def test_lmhead_every_plan(plan):
+    qpn = need_gpu()
+    n, k = 4099, 1040
+    w = synth.weights(n, k, seed=plan)
+    x = synth.activations(8, k, seed=plan)
+    codes, scales, g = oracle.pack_nvfp4(w)
+    try:
+        qpn.debug_set_plan(plan)
+        pw = qpn.pack_nvfp4(dev(w))
+        for m in (1, 2, 5, 8):
+            log(f"lmhead plan {plan} {n}x{k} m={m}")
+            lg, am = qpn.lmhead_nvfp4(pw, dev(x[:m]))
+            lg, am = host(lg), host(am)
+            y_ref = oracle.gemm_nvfp4(codes, scales, g, x[:m])
+            parity(lg, y_ref, f"lmhead plan {plan} m={m}")
+            _check_argmax(am, lg, y_ref, f"lmhead plan {plan} m={m}")
+    finally:
+        qpn.debug_set_plan(0)
