@@ -93,6 +93,10 @@ class Shape:
         self.y = {m: torch.empty((m, n), dtype=torch.float16, device="cuda") for m in ms}
         self.xm = {m: self.x[:m].contiguous() for m in ms}
         self.bytes = algo_bytes(n, k, fmt)
+        op = qpn.OP_GEMM_NVFP4 if fmt == "nvfp4" else qpn.OP_GEMM_FP8
+        # split-K workspace, zero-filled once (the library keeps it zeroed)
+        self.ws = torch.zeros(max(256, max(qpn.workspace_bytes(op, m, n, k) for m in ms)),
+                              dtype=torch.uint8, device="cuda")
         self.i = 0
 
     def next_copy(self):
@@ -105,7 +109,7 @@ def one_step(qpn, shapes):
     """One pass: every (shape, M) call once, each on the next rotated copy."""
     for s in shapes:
         for m in s.ms:
-            qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m])
+            qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws)
 
 
 def capture(torch, fn):
@@ -135,7 +139,7 @@ def time_graph(torch, g, reps):
 
 def time_call(qpn, torch, s, m, batch=BATCH, reps=5):
     """Average launch time (s) of one (shape, M) call in back-to-back graphs."""
-    g = capture(torch, lambda: [qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m]) for _ in range(batch)])
+    g = capture(torch, lambda: [qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws) for _ in range(batch)])
     g.replay()
     torch.cuda.synchronize()
     per = [t / batch for t in time_graph(torch, g, reps)]
@@ -293,7 +297,7 @@ def main():
             xm = x8[:m].contiguous()
             lg = torch.empty((m, n), dtype=torch.float16, device="cuda")
             am = torch.empty((m,), dtype=torch.int32, device="cuda")
-            ws = torch.empty(qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, m, n, k), dtype=torch.uint8, device="cuda")
+            ws = torch.zeros(qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, m, n, k), dtype=torch.uint8, device="cuda")
             qpn.lmhead_nvfp4(copies[0], xm, lg, am, ws)
             g = capture(torch, lambda: [qpn.lmhead_nvfp4(copies[i % 3], xm, lg, am, ws) for i in range(12)])
             per = [t / 12 for t in time_graph(torch, g, 5)]

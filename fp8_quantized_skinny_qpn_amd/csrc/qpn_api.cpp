@@ -48,9 +48,12 @@ int launch_status(hipError_t e) { return e == hipSuccess ? QPN_OK : QPN_ERR_LAUN
 // Plan override for A/B measurements (qpn_debug_set_plan): 0 = automatic.
 std::atomic<int> g_plan{0};
 
-hipError_t dispatch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a) {
-  return launch_gemm(fmt, argmax, a, g_plan.load(std::memory_order_relaxed));
-}
+int forced_plan() { return g_plan.load(std::memory_order_relaxed); }
+
+// Bytes of lm_head argmax keys at the start of its workspace, and where the
+// split-K area starts after them.
+size_t lmhead_keys_bytes(int m, int64_t n) { return (size_t)8 * (size_t)m * (size_t)panels_of(n); }
+size_t lmhead_split_offset(int m, int64_t n) { return (lmhead_keys_bytes(m, n) + 255) / 256 * 256; }
 
 int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, const void* y,
                        int m, int64_t n, int64_t k) {
@@ -64,15 +67,17 @@ int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, cons
 
 int gemm_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
                int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int rc = gemm_common_checks(fmt, packed, x, y, m, n, k);
   if (rc != QPN_OK) return rc;
   if (m == 0 || n == 0) return QPN_OK;
+  if (workspace && !aligned(workspace, 8)) return QPN_ERR_ALIGN;
   rc = device_check();
   if (rc != QPN_OK) return rc;
-  GemmArgs a{packed, x, y, m, n, k, nullptr, stream};
-  return launch_status(dispatch_gemm(fmt, false, a));
+  GemmLaunch l;
+  const int lr = gemm_launch_for(fmt, m, n, k, forced_plan(), workspace ? workspace_bytes : 0, 0, &l);
+  if (lr != kGemmLaunchOk) return lr == kGemmNoWorkspace ? QPN_ERR_BUFFER : QPN_ERR_SHAPE;
+  GemmArgs a{packed, x, y, m, n, k, nullptr, workspace, stream};
+  return launch_status(launch_gemm(fmt, false, a, l));
 }
 
 }  // namespace
@@ -106,18 +111,31 @@ size_t qpn_fp8_packed_bytes(int64_t n, int64_t k) {
 
 size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
   if (m < 0 || m > kMaxM) return (size_t)-1;
+  uint32_t fmt;
   switch (op) {
-    case QPN_OP_GEMM_NVFP4: return nv_shape_ok(n, k) ? 0 : (size_t)-1;
-    case QPN_OP_GEMM_FP8: return f8_shape_ok(n, k) ? 0 : (size_t)-1;
+    case QPN_OP_GEMM_NVFP4:
     case QPN_OP_LMHEAD_NVFP4:
       if (!nv_shape_ok(n, k)) return (size_t)-1;
-      return (size_t)8 * (size_t)m * (size_t)panels_of(n);
+      fmt = kFmtNvfp4;
+      break;
+    case QPN_OP_GEMM_FP8:
+      if (!f8_shape_ok(n, k)) return (size_t)-1;
+      fmt = kFmtFp8;
+      break;
     default: return (size_t)-1;
   }
+  if (m == 0 || n == 0) return 0;
+  const bool lm = op == QPN_OP_LMHEAD_NVFP4;
+  GemmLaunch l;
+  if (gemm_launch_for(fmt, m, n, k, forced_plan(), (size_t)-1, lm ? lmhead_split_offset(m, n) : 0,
+                      &l) != kGemmLaunchOk)
+    return (size_t)-1;
+  if (l.splits <= 1) return lm ? lmhead_keys_bytes(m, n) : 0;
+  return l.ws_needed;
 }
 
 int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
-                  int* panels_per_workgroup, int* prefetch_depth, int* lds_slots,
+                  int* panels_per_workgroup, int* prefetch_depth, int* splits,
                   int* activation_rows) {
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
   uint32_t fmt;
@@ -133,14 +151,16 @@ int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int*
       break;
     default: return QPN_ERR_SHAPE;
   }
-  const int forced = g_plan.load(std::memory_order_relaxed);
-  GemmPlan pl;
-  if (!gemm_plan_info(forced > 0 ? forced : gemm_auto_plan(fmt, m, n, k), &pl)) return QPN_ERR_SHAPE;
-  if (workgroups) *workgroups = (panels_of(n) + pl.panels_per_workgroup - 1) / pl.panels_per_workgroup;
-  if (waves_per_panel) *waves_per_panel = pl.waves_per_panel;
-  if (panels_per_workgroup) *panels_per_workgroup = pl.panels_per_workgroup;
-  if (prefetch_depth) *prefetch_depth = pl.depth;
-  if (lds_slots) *lds_slots = gemm_ring_slots(fmt, pl.waves_per_panel, m, pl.lds_slots);
+  const bool lm = op == QPN_OP_LMHEAD_NVFP4;
+  GemmLaunch l;
+  if (gemm_launch_for(fmt, m, n, k, forced_plan(), (size_t)-1, lm ? lmhead_split_offset(m, n) : 0,
+                      &l) != kGemmLaunchOk)
+    return QPN_ERR_SHAPE;
+  if (workgroups) *workgroups = l.groups * l.splits;
+  if (waves_per_panel) *waves_per_panel = l.waves_per_panel;
+  if (panels_per_workgroup) *panels_per_workgroup = l.panels_per_workgroup;
+  if (prefetch_depth) *prefetch_depth = l.depth;
+  if (splits) *splits = l.splits;
   if (activation_rows) *activation_rows = gemm_activation_rows(m);
   return QPN_OK;
 }
@@ -186,17 +206,20 @@ int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, in
   if (m == 0) return QPN_OK;
   if (!argmax) return QPN_ERR_NULL;
   if (!aligned(argmax, 4)) return QPN_ERR_ALIGN;
-  const size_t need = qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4, m, n, k);
   if (!workspace) return QPN_ERR_NULL;
   if (!aligned(workspace, 8)) return QPN_ERR_ALIGN;
-  if (workspace_bytes < need) return QPN_ERR_BUFFER;
+  if (workspace_bytes < lmhead_keys_bytes(m, n)) return QPN_ERR_BUFFER;
   rc = device_check();
   if (rc != QPN_OK) return rc;
-  GemmArgs a{packed, x, logits, m, n, k, (uint64_t*)workspace, stream};
-  hipError_t e = dispatch_gemm(kFmtNvfp4, true, a);
+  GemmLaunch l;
+  const int lr = gemm_launch_for(kFmtNvfp4, m, n, k, forced_plan(), workspace_bytes,
+                                 lmhead_split_offset(m, n), &l);
+  if (lr != kGemmLaunchOk) return lr == kGemmNoWorkspace ? QPN_ERR_BUFFER : QPN_ERR_SHAPE;
+  GemmArgs a{packed, x, logits, m, n, k, (uint64_t*)workspace, workspace, stream};
+  hipError_t e = launch_gemm(kFmtNvfp4, true, a, l);
   if (e != hipSuccess) return QPN_ERR_LAUNCH;
   return launch_status(
-      launch_argmax_finalize((const uint64_t*)workspace, panels_of(n), m, argmax, stream));
+      launch_argmax_finalize((uint64_t*)workspace, panels_of(n), m, argmax, stream));
 }
 
 int qpn_debug_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,

@@ -11,33 +11,40 @@
 // the MFMA is used because it does the K-reduction across lanes for free and
 // leaves the VALU to the decode.
 //
-// Why this shape (CDNA4 specifics):
-//   * Vector memory loads of one wavefront complete in order.  If a compute
-//     wavefront also loaded activations, every wait for activation data would
-//     also wait for all weight loads issued before it and the weight prefetch
-//     would collapse.  So the compute wavefronts issue weight loads only; the
-//     activations are staged into LDS by one extra wavefront per workgroup and
-//     read back with ds_read (a separate counter).
-//   * Every activation row is needed by every 16-row panel.  Staging it once
-//     per workgroup into LDS replaces per-panel, per-lane activation loads
-//     (which cost more L2->CU bytes than the weights themselves at M = 8).
-//   * Weight loads go through buffer descriptors: 32-bit offsets, and, being
-//     memory intrinsics, they keep program order in the load queue, so every
-//     wait count the compiler derives is exact.
+// Work split.  A workgroup owns G consecutive 16-row panels and one of S
+// contiguous K ranges ("splits") of them.  Each panel is worked on by W
+// wavefronts that interleave the split's k-steps (wavefront w takes local
+// k-steps w, w + W, ...).
 //
-// Schedule.  A workgroup owns G consecutive 16-row panels.  Each panel is
-// worked on by W compute wavefronts that interleave its k-steps: "window" c is
-// k-steps [cW, cW + W), and wavefront w of the panel consumes k-step cW + w.
-// The loader wavefront writes window c's activations into LDS ring slot
-// c % NB, NB - 1 windows ahead, with direct-to-LDS buffer loads whose
-// out-of-range lanes (rows >= m, K >= k) deliver zeros.  One s_barrier per
-// window hands a filled slot to the compute wavefronts and a drained one back
-// to the loader.  The compute wavefronts keep D windows of weight loads in
-// flight (5 VGPRs per k-step); past their last k-step they keep issuing
-// loads through a descriptor of size zero (no memory access, zeros back)
-// instead of branching, so every wait count is static.  Partial tiles of a
-// panel's W wavefronts are summed through LDS in a fixed order, so results
-// are deterministic and independent of where a row sits in the matrix.
+// Why this shape (CDNA4 specifics):
+//   * Every activation row is needed by every panel.  The workgroup stages
+//     its split's activation slice X[:, K range] into LDS once, with
+//     direct-to-LDS buffer loads spread over all its wavefronts, and all G
+//     panels read it from there (ds_read, a separate counter from the weight
+//     loads).  Activation traffic from L2 is (panels / G) * M * K * 2 bytes,
+//     so at M = 8 G is raised to keep it well below the weight bytes.
+//   * Vector memory loads of one wavefront complete in order.  The
+//     activation loads are issued before the weight prefetch, so waiting for
+//     them never waits for weights; after one barrier the main loop has no
+//     barriers and no activation loads at all.
+//   * Weight loads go through one buffer descriptor per chunk: 32-bit
+//     offsets, and, being memory intrinsics, they keep program order in the
+//     load queue, so every wait count the compiler derives is exact.  Past
+//     its last k-step a wavefront keeps issuing loads through a descriptor
+//     of size zero (no memory access, zeros back) instead of branching, so
+//     the ring of D loads in flight has static slots and static waits.
+//   * When S > 1, each workgroup writes its FP32 partial tiles to the
+//     workspace and bumps its panel group's counter; the last to arrive sums
+//     the S partials in split order and writes the FP16 result.  Partials
+//     and counters use device-scope relaxed atomics (write-through stores and
+//     coherent loads), ordered by waiting for the stores before the counter
+//     update: no whole-cache write-back or invalidate is needed.
+//
+// The partial tiles of a panel's W wavefronts are summed through LDS in a
+// fixed order and splits in split order, so results are deterministic and
+// independent of where a row sits in the matrix.
+#include <algorithm>
+
 #include "qpn_common.h"
 #include "qpn_internal.h"
 
@@ -108,126 +115,149 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 
 }  // namespace
 
-// Bytes of one LDS activation window (padded to whole 1 KiB loader loads).
-template <uint32_t FMT, int W, int MB>
-constexpr int window_bytes() {
-  return ((W * (Fmt<FMT>::kKStep / 8) * MB + 63) / 64) * 1024;
-}
+// Split-K arguments of one launch (all unused when splits == 1).
+struct SplitArgs {
+  int splits;            // S: K ranges per panel group
+  int split_steps;       // k-steps per K range (the last may be shorter)
+  float* partial;        // [S][groups][G][64 lanes][4] FP32 partial tiles
+  uint32_t* counters;    // [groups] arrivals; zero between calls
+};
 
-template <uint32_t FMT, int W, int G, int D, int NB, int MB, bool ARGMAX>
-__global__ __launch_bounds__(kLanes * (G * W + 1)) void skinny_gemm_kernel(
+template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX>
+__global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
     const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-    int m, int64_t n, int64_t k, uint64_t* __restrict__ keys) {
+    int m, int64_t n, int64_t k, SplitArgs sp, uint64_t* __restrict__ keys) {
   using F = Fmt<FMT>;
   constexpr int KS = F::kKStep;
   constexpr int GR = F::kGroups;
-  constexpr int NCW = G * W;                      // compute wavefronts
-  constexpr int UNITS = W * (KS / 8) * MB;        // 16-byte activation units per window
-  constexpr int LPW = (UNITS + 63) / 64;          // loader loads per window
-  constexpr int WINB = LPW * 1024;
-  constexpr int R = D + 1;                        // weight ring slots
-  static_assert(NB >= 2, "ring needs two slots");
-  static_assert(NCW + 1 <= 16, "at most 16 wavefronts");
-  static_assert((NB - 2) * LPW < 64, "loader wait count");
+  constexpr int NW = G * W;                          // wavefronts
+  constexpr int LPS = FMT == kFmtNvfp4 ? 2 : 1;      // weight loads per k-step
+  constexpr int R = D + 1;                           // weight ring slots
+  constexpr int XSTEP = (KS / 8) * MB;               // 16-byte activation units per k-step
+  static_assert(NW <= 16, "at most 16 wavefronts");
+  static_assert(D * LPS < 64, "wait count");
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int lane = threadIdx.x & (kLanes - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int64_t P = panels_of(n);
   const int J = (int)((k + KS - 1) / KS);
+  const int S = sp.splits;
+  const int grp = (int)(blockIdx.x / S);
+  const int split = (int)(blockIdx.x % S);
+  const int j0 = split * sp.split_steps;                       // first k-step of the range
+  const int nj = max(0, min(J - j0, sp.split_steps));          // k-steps in the range
 
-  const BlobHeader* hdr = reinterpret_cast<const BlobHeader*>(blob);
-  const bool valid = hdr->magic == kMagic && hdr->format == FMT &&
-                     hdr->layout_version == kLayoutVersion && hdr->n == n && hdr->k == k;
-  // Windows of real work, padded to whole weight-ring cycles so the compute
-  // loop body is straight-line with static ring slots (and so exact wait
-  // counts).  Padded windows cost a barrier and an out-of-range load; the
-  // loader does nothing in them.  Every wavefront of the workgroup runs the
-  // same number of windows, hence of barriers.
-  const int nwin = valid ? (J + W - 1) / W : 0;
-  const int nwin_pad = ((nwin + R - 1) / R) * R;
+  const int gi = wv / W;  // panel of this wavefront inside the workgroup
+  const int w = wv % W;   // its interleave position
+  // panel group grp owns panels [grp * P / groups, (grp + 1) * P / groups):
+  // G or fewer, spread evenly so that every workgroup has about the same work
+  const int64_t groups = gridDim.x / S;
+  const int64_t pbeg = (int64_t)grp * P / groups;
+  const int64_t pend = (int64_t)(grp + 1) * P / groups;
+  const int64_t p = pbeg + gi;
+  const bool active = p < pend;
+  const int row = lane & 15, kg = lane >> 4;
 
-  if (wv == NCW) {
-    // ---------------- loader wavefront ----------------
+  // ---- 0. header and FP8 row scales: loaded now, used in the epilogue, so
+  // their latency overlaps the stream instead of adding to the tail ----
+  // (vector loads: they join the in-order load queue ahead of the activation
+  // loads and are covered by the same wait; scalar loads would be waited for
+  // together with the kernel arguments, before anything else is issued)
+  const __amdgpu_buffer_rsrc_t hres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, kHeaderBytes, kRsrcFlags);
+  const u32x4 hd0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, 0, 0, 0));
+  const u32x4 hd1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, 16, 0, 0));
+  const uint32_t hd2 = __builtin_amdgcn_raw_buffer_load_b32(hres, 48, 0, 0);
+  float4v row_scale = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (FMT == kFmtFp8) {
+    // rows 16 p + 4 (lane >> 4) + v; the padded scale area holds 16 P floats
+    const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + kHeaderBytes), (short)0, (int)(P * kPanelRows * 4), kRsrcFlags);
+    const int64_t r0 = (active ? p : 0) * kPanelRows + 4 * (lane >> 4);
+    row_scale = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rres, (int)(r0 * 4), 0, 0));
+  }
+  asm volatile("" ::: "memory");
+
+  // ---- 1. activation slice -> LDS (issued first: see the header) ----
+  // Unit u (16 bytes) = ((jl * GR + t) * 4 + kg) * MB + mm holds
+  // X[mm][K .. K + 8), K = (j0 + jl) * KS + kg * KS / 4 + 8 t; load q of the
+  // slice fills units [64 q, 64 q + 64).  Rows >= m and K outside the range
+  // read zeros (out-of-range buffer offsets).  Offsets stay below 2^25.
+  {
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrcFlags);
-    // Load q, lane l fills 16-byte unit u = 64 q + l of a window:
-    // u = ((jw * GR + t) * 4 + kg) * MB + mm  (step-in-window jw, MFMA group t,
-    // K group kg, activation row mm), at K = window start + koff.
-    // K positions stay below 2^21 and byte offsets below 2^25: 32-bit math.
-    const int kk = (int)k;
-    int rowoff[LPW], koff[LPW];
-#pragma unroll
-    for (int q = 0; q < LPW; ++q) {
+    const int units = nj * XSTEP;
+    const int nq = (units + 63) / 64;
+    for (int q = wv; q < nq; q += NW) {
       const int u = q * 64 + lane;
       const int mm = u % MB;
       const int rest = u / MB;
-      koff[q] = (rest / (4 * GR)) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
-      // rows >= m and padding units never address the buffer: push their K
-      // position out of range instead
-      rowoff[q] = mm * kk * 2;
-      if (!(u < UNITS && mm < m)) koff[q] = 1 << 24;
+      const int jl = rest / (4 * GR);
+      const int kpos = (j0 + jl) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
+      const bool ok = u < units && mm < m && kpos < k;
+      const int off = ok ? (int)(((int64_t)mm * k + kpos) * 2) : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)(smem + q * 1024), 16, off, 0, 0, 0);
     }
-    auto issue_window = [&](int c) {
-      uint8_t* slot = smem + (c % NB) * WINB;
-      const int kbase = c * W * KS;  // first K of the window
-#pragma unroll
-      for (int q = 0; q < LPW; ++q) {
-        // K past k (ragged tail, padded windows) reads zeros: out of range
-        const int kpos = kbase + koff[q];
-        const int off = kpos < kk ? rowoff[q] + 2 * kpos : 0x7FFFFFF0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xres, (__attribute__((address_space(3))) void*)(slot + q * 1024), 16, off, 0, 0, 0);
-      }
-    };
-#pragma unroll
-    for (int c = 0; c < NB - 1; ++c) issue_window(c);
-    wait_vmcnt<(NB - 2) * LPW>();
-    bare_barrier();  // window 0 is in LDS
-    for (int c = 0; c < nwin; ++c) {
-      issue_window(c + NB - 1);  // into the slot drained in window c - 1
-      wait_vmcnt<(NB - 2) * LPW>();
-      bare_barrier();  // window c + 1 is in LDS; window c is consumed
-    }
-    for (int c = nwin; c < nwin_pad; ++c) bare_barrier();
-    wait_vmcnt<0>();
-    bare_barrier();  // no LDS writes in flight any more
-    bare_barrier();  // partial tiles written
-    return;
   }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---------------- compute wavefronts ----------------
-  const int gi = wv / W;  // panel of this wavefront inside the workgroup
-  const int w = wv % W;   // its position inside each window
-  const int64_t p = (int64_t)blockIdx.x * G + gi;
-  const bool active = p < P;
-  const int row = lane & 15, kg = lane >> 4;
-  // chunk (p, s) = codes + (s * P + p) * chunk bytes (step-major layout)
+  // ---- 2. weight prefetch ----
+  // chunk (p, j) = codes + (j * P + p) * chunk bytes (step-major layout)
   const uint8_t* cbase = blob + (FMT == kFmtNvfp4 ? (uint64_t)kHeaderBytes : f8_codes_offset(n)) +
                          (uint64_t)(active ? p : 0) * F::kChunk;
   const uint64_t sstride = (uint64_t)P * F::kChunk;
-  // this wavefront's k-steps are w, w + W, ...; its last valid one:
-  const int slast = (J > w) ? w + ((J - 1 - w) / W) * W : 0;
-  const bool any_step = active && J > w;
+  // this wavefront's local k-steps: w + c W for c < nc
+  const int nc = (active && nj > w) ? (nj - w + W - 1) / W : 0;
+  const int nc_pad = ((nc + R - 1) / R) * R;
 
   // One descriptor per load, covering exactly its chunk; past the end of the
   // wavefront's k-steps the descriptor has size zero (no memory access).
   auto issue = [&](int c, WFrag& f) {
-    const int s = c * W + w;
-    const bool ok = s <= slast;
+    const bool ok = c < nc;
+    const int jg = j0 + c * W + w;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(cbase + (uint64_t)s * sstride), (short)0, ok ? F::kChunk : 0, kRsrcFlags);
+        (void*)(cbase + (uint64_t)(ok ? jg : 0) * sstride), (short)0, ok ? F::kChunk : 0,
+        kRsrcFlags);
     // aux 2: nontemporal (streamed once)
     f.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 2));
     if constexpr (FMT == kFmtNvfp4)
       f.scales = __builtin_amdgcn_raw_buffer_load_b16(r, kNvCodeBytes + 2 * lane, 0, 0);
   };
 
+  WFrag ring[R];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    issue(i, ring[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // this wavefront's activation loads (older than the D weight steps) are
+  // in LDS; after the barrier everyone's are
+  wait_vmcnt<D * LPS>();
+  bare_barrier();
+  // the header loads were older than the activation loads: they are in
+  // (BlobHeader: magic, format, layout_version, reserved, n, k, ..., tensor_scale at 48)
+  const uint32_t h_magic = __builtin_amdgcn_readfirstlane(hd0[0]);
+  const uint32_t h_format = __builtin_amdgcn_readfirstlane(hd0[1]);
+  const uint32_t h_version = __builtin_amdgcn_readfirstlane(hd0[2]);
+  const int64_t h_n = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
+                                __builtin_amdgcn_readfirstlane(hd1[0]));
+  const int64_t h_k = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[3]) << 32) |
+                                __builtin_amdgcn_readfirstlane(hd1[2]));
+  const float h_scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(hd2));
+  const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
+                     h_n == n && h_k == k;
+
+  // ---- 3. stream ----
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   // activation operand for this lane: row min(row, MB-1) (columns >= m are
-  // discarded by the epilogue), K group kg, own step jw = w of the window
+  // discarded by the epilogue), K group kg, local step w + c W
   const int xrow = row < MB ? row : MB - 1;
-  const int xoff0 = (((w * GR) * 4 + kg) * MB + xrow) * 16;
+  const uint8_t* xlane = smem + ((w * GR * 4 + kg) * MB + xrow) * 16;
+  constexpr int XC = W * GR * 4 * MB * 16;  // LDS bytes per interleave round
 
   auto compute = [&](int c, const WFrag& f) {
     half8 a[GR];
@@ -235,7 +265,7 @@ __global__ __launch_bounds__(kLanes * (G * W + 1)) void skinny_gemm_kernel(
       decode_nvfp4_fragment(f.codes, (uint32_t)f.scales, a);
     else
       decode_fp8_fragment(f.codes, a);
-    const uint8_t* xs = smem + (c % NB) * WINB + xoff0;
+    const uint8_t* xs = xlane + c * XC;
 #pragma unroll
     for (int t = 0; t < GR; ++t) {
       const half8 b = *reinterpret_cast<const half8*>(xs + t * 4 * MB * 16);
@@ -243,59 +273,87 @@ __global__ __launch_bounds__(kLanes * (G * W + 1)) void skinny_gemm_kernel(
     }
   };
 
-  WFrag ring[R];
-  if (any_step) {
+  // At least one ring cycle runs even when this wavefront has no k-steps, so
+  // the prologue loads are used on every path and stay ahead of the barrier.
+  int c0 = 0;
+  do {
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      issue(i, ring[i]);
+    for (int i = 0; i < R; ++i) {
+      const int c = c0 + i;
+      issue(c + D, ring[(i + D) % R]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c < nc) compute(c, ring[i]);  // no loads inside: waits unaffected
       __builtin_amdgcn_sched_barrier(0);
     }
-    bare_barrier();  // window 0 ready
-    for (int c0 = 0; c0 < nwin_pad; c0 += R) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int c = c0 + i;
-        issue(c + D, ring[(i + D) % R]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c * W + w < J) compute(c, ring[i]);  // no loads inside: waits unaffected
-        __builtin_amdgcn_sched_barrier(0);
-        bare_barrier();
-      }
-    }
-  } else {
-    bare_barrier();
-    for (int c = 0; c < nwin_pad; ++c) bare_barrier();
-  }
-  bare_barrier();  // loader drained: LDS is free for the reduction
+    c0 += R;
+  } while (c0 < nc_pad);
 
-  // Fixed-order sum of the W partial tiles of each panel.
+  // ---- 4. fixed-order sum of the W partial tiles of each panel ----
+  wait_vmcnt<0>();  // surplus (size-zero) loads retired before the wavefront ends
+  bare_barrier();   // every wavefront is done reading activations
   float4v* red = reinterpret_cast<float4v*>(smem);
   if constexpr (W > 1) red[wv * kLanes + lane] = acc;
-  wait_lgkmcnt0();  // this wavefront's partial tile has reached LDS
+  wait_lgkmcnt0();
   bare_barrier();
-  if (w != 0 || !active) return;
+  const bool lead = w == 0;  // this wavefront holds its panel's tile below
   if constexpr (W > 1) {
-    acc = red[(gi * W) * kLanes + lane];
+    if (lead) {
+      acc = red[(gi * W) * kLanes + lane];
 #pragma unroll
-    for (int i = 1; i < W; ++i) acc += red[(gi * W + i) * kLanes + lane];
+      for (int i = 1; i < W; ++i) acc += red[(gi * W + i) * kLanes + lane];
+    }
   }
 
-  // Epilogue.  Lane holds D[i][j] for j = lane & 15 (activation row) and
-  // i = 4 (lane >> 4) + v (panel row).
+  // ---- 5. split-K: partial tiles, arrival count, last arriver sums ----
+  if (S > 1) {
+    float* mine = sp.partial + ((((int64_t)split * groups + grp) * G + gi) * kLanes + lane) * 4;
+    if (lead) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        __hip_atomic_store(mine + v, acc[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmcnt<0>();  // this wavefront's partial stores are complete at device scope
+    bare_barrier();
+    uint32_t* arrived = reinterpret_cast<uint32_t*>(smem);
+    if (wv == 0 && lane == 0) {
+      const uint32_t before =
+          __hip_atomic_fetch_add(sp.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the last arrival also re-arms the counter for the next call
+      if (before == (uint32_t)(S - 1))
+        __hip_atomic_store(sp.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *arrived = before;
+    }
+    wait_lgkmcnt0();
+    bare_barrier();
+    if (*arrived != (uint32_t)(S - 1)) return;  // uniform over the workgroup
+    if (lead) {
+      const int64_t per_split = groups * G * kLanes * 4;
+      float* first = sp.partial + ((((int64_t)grp) * G + gi) * kLanes + lane) * 4;
+      acc = float4v{0.f, 0.f, 0.f, 0.f};
+      for (int sx = 0; sx < S; ++sx) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[v] += __hip_atomic_load(first + sx * per_split + v, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // this is the only reader: clear the partials so the workspace is all
+      // zeros again when the call ends (whatever layout the next call uses)
+      for (int sx = 0; sx < S; ++sx)
+        *reinterpret_cast<float4v*>(first + sx * per_split) = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (!lead || !active) return;
+
+  // ---- 6. epilogue.  Lane holds D[i][j] for j = lane & 15 (activation
+  // row) and i = 4 (lane >> 4) + v (panel row). ----
   const int mcol = lane & 15;
   const int64_t n0 = p * kPanelRows + 4 * (lane >> 4);
   uint16_t h[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t nn = n0 + v;
-    float s = 0.f;  // the blob is only read past its header when the header matched
-    if (valid) {
-      if constexpr (FMT == kFmtNvfp4)
-        s = hdr->tensor_scale;
-      else
-        s = nn < n ? reinterpret_cast<const float*>(blob + kHeaderBytes)[nn] : 0.f;
-    }
-    _Float16 o = valid ? (_Float16)(s * acc[v]) : (_Float16)__builtin_nanf("");
+    const float sc = FMT == kFmtNvfp4 ? h_scale : row_scale[v];
+    _Float16 o = valid ? (_Float16)(sc * acc[v]) : (_Float16)__builtin_nanf("");
     h[v] = __builtin_bit_cast(uint16_t, o);
     if (mcol < m && nn < n) y[(int64_t)mcol * n + nn] = h[v];
   }
@@ -321,7 +379,7 @@ __global__ __launch_bounds__(kLanes * (G * W + 1)) void skinny_gemm_kernel(
 }
 
 // Final argmax: one block per activation row reduces that row's panel keys.
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __restrict__ keys,
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(uint64_t* __restrict__ keys,
                                                               int64_t panels,
                                                               int32_t* __restrict__ argmax) {
   __shared__ uint64_t part[256];
@@ -329,6 +387,7 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __
   uint64_t best = 0;
   for (int64_t i = threadIdx.x; i < panels; i += 256) {
     uint64_t kv = keys[(int64_t)mi * panels + i];
+    keys[(int64_t)mi * panels + i] = 0;  // leave the workspace all zeros
     best = kv > best ? kv : best;
   }
   part[threadIdx.x] = best;
@@ -348,62 +407,72 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __
 // ---------------------------------------------------------------------------
 namespace {
 
-// Ring slots actually used: the loader's wait count (vmcnt) is 6 bits wide,
-// so wide windows (many loads each) get fewer slots.
-constexpr int ring_slots_of(int kstep, int W, int MB, int NB) {
-  const int lpw = (W * (kstep / 8) * MB + 63) / 64;
-  return (NB - 2) * lpw < 64 ? NB : 2 + 63 / lpw;
+// Activation bytes one k-step of a slice occupies in LDS.
+int x_step_bytes(uint32_t fmt, int m) {
+  return (fmt == kFmtNvfp4 ? kNvKStep : kF8KStep) * gemm_activation_rows(m) * 2;
 }
 
-template <uint32_t FMT, int W, int G, int D, int NB0, int MB, bool ARGMAX>
-hipError_t launch_t(const GemmArgs& a) {
-  constexpr int NB = ring_slots_of(Fmt<FMT>::kKStep, W, MB, NB0);
-  constexpr int WINB = window_bytes<FMT, W, MB>();
-  size_t lds = (size_t)NB * WINB;
-  const size_t red = (size_t)G * W * kLanes * 16;
-  if (lds < red) lds = red;
-  const int64_t wgs = (panels_of(a.n) + G - 1) / G;
-  hipLaunchKernelGGL((skinny_gemm_kernel<FMT, W, G, D, NB, MB, ARGMAX>), dim3((unsigned)wgs),
-                     dim3(kLanes * (G * W + 1)), lds, (hipStream_t)a.stream,
-                     (const uint8_t*)a.packed, a.x, a.y, a.m, a.n, a.k, a.keys);
+// LDS activation budget per workgroup: two workgroups fit in the 160 KiB of a CU.
+constexpr int kSliceBudget = 80 * 1024;
+// Wanted workgroups per launch: one per CU or more.
+constexpr int64_t kMinWorkgroups = 256;
+
+template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX>
+hipError_t launch_t(const GemmArgs& a, const GemmLaunch& l) {
+  const int xbytes = ((l.split_steps * (Fmt<FMT>::kKStep / 8) * MB + 63) / 64) * 1024;
+  const int red = G * W * kLanes * 16;
+  const size_t lds = (size_t)(xbytes > red ? xbytes : red);
+  SplitArgs sp{l.splits, l.split_steps, nullptr, nullptr};
+  if (l.splits > 1) {
+    sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
+    sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
+  }
+  hipLaunchKernelGGL((skinny_gemm_kernel<FMT, W, G, D, MB, ARGMAX>),
+                     dim3((unsigned)(l.groups * l.splits)), dim3(kLanes * G * W), lds,
+                     (hipStream_t)a.stream, (const uint8_t*)a.packed, a.x, a.y, a.m, a.n, a.k, sp,
+                     a.keys);
   return hipGetLastError();
 }
 
-template <uint32_t FMT, int W, int G, int D, int NB, bool ARGMAX>
-hipError_t launch_mb(const GemmArgs& a) {
+template <uint32_t FMT, int W, int G, int D, bool ARGMAX>
+hipError_t launch_mb(const GemmArgs& a, const GemmLaunch& l) {
   switch (gemm_activation_rows(a.m)) {
-    case 1: return launch_t<FMT, W, G, D, NB, 1, ARGMAX>(a);
-    case 2: return launch_t<FMT, W, G, D, NB, 2, ARGMAX>(a);
-    case 4: return launch_t<FMT, W, G, D, NB, 4, ARGMAX>(a);
-    default: return launch_t<FMT, W, G, D, NB, 8, ARGMAX>(a);
+    case 1: return launch_t<FMT, W, G, D, 1, ARGMAX>(a, l);
+    case 2: return launch_t<FMT, W, G, D, 2, ARGMAX>(a, l);
+    case 4: return launch_t<FMT, W, G, D, 4, ARGMAX>(a, l);
+    default: return launch_t<FMT, W, G, D, 8, ARGMAX>(a, l);
   }
 }
 
-// The compiled plans: (W, G, D, NB).
+// The compiled plans: (W, G, D).
 constexpr GemmPlan kPlans[] = {
-    {0, 0, 0, 0},  // 0: automatic
-    {4, 1, 4, 8},  // 1
-    {4, 2, 4, 4},  // 2
-    {4, 3, 4, 8},  // 3
-    {4, 2, 4, 6},  // 4
-    {8, 1, 4, 8},  // 5
-    {2, 4, 4, 8},  // 6
-    {4, 2, 6, 4},  // 7
-    {4, 1, 6, 8},  // 8
+    {0, 0, 0},    // 0: automatic
+    {4, 1, 4},    // 1
+    {4, 1, 10},   // 2
+    {8, 1, 5},    // 3
+    {8, 1, 9},    // 4
+    {3, 5, 4},    // 5
+    {3, 5, 14},   // 6
+    {8, 2, 9},    // 7
+    {4, 4, 10},   // 8
+    {16, 1, 9},   // 9
+    {4, 2, 10},   // 10
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
 template <uint32_t FMT, bool ARGMAX>
-hipError_t launch_plan(const GemmArgs& a, int id) {
-  switch (id) {
-    case 1: return launch_mb<FMT, 4, 1, 4, 8, ARGMAX>(a);
-    case 2: return launch_mb<FMT, 4, 2, 4, 4, ARGMAX>(a);
-    case 3: return launch_mb<FMT, 4, 3, 4, 8, ARGMAX>(a);
-    case 4: return launch_mb<FMT, 4, 2, 4, 6, ARGMAX>(a);
-    case 5: return launch_mb<FMT, 8, 1, 4, 8, ARGMAX>(a);
-    case 6: return launch_mb<FMT, 2, 4, 4, 8, ARGMAX>(a);
-    case 7: return launch_mb<FMT, 4, 2, 6, 4, ARGMAX>(a);
-    case 8: return launch_mb<FMT, 4, 1, 6, 8, ARGMAX>(a);
+hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
+  switch (l.plan) {
+    case 1: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
+    case 2: return launch_mb<FMT, 4, 1, 10, ARGMAX>(a, l);
+    case 3: return launch_mb<FMT, 8, 1, 5, ARGMAX>(a, l);
+    case 4: return launch_mb<FMT, 8, 1, 9, ARGMAX>(a, l);
+    case 5: return launch_mb<FMT, 3, 5, 4, ARGMAX>(a, l);
+    case 6: return launch_mb<FMT, 3, 5, 14, ARGMAX>(a, l);
+    case 7: return launch_mb<FMT, 8, 2, 9, ARGMAX>(a, l);
+    case 8: return launch_mb<FMT, 4, 4, 10, ARGMAX>(a, l);
+    case 9: return launch_mb<FMT, 16, 1, 9, ARGMAX>(a, l);
+    case 10: return launch_mb<FMT, 4, 2, 10, ARGMAX>(a, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -412,26 +481,22 @@ hipError_t launch_plan(const GemmArgs& a, int id) {
 
 int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
 
-// Automatic plan: a pure function of (format, m, n, k).  Measured on
-// MI355X (kernel durations, 17408x5120 and 5120x17408 NVFP4):
-//   m <= 2: one panel per workgroup and an 8-window activation ring (the
-//     loader's activation loads queue behind the weight misses of its CU,
-//     so the ring must be about as deep as the weight prefetch);
-//   m <= 4: two panels per workgroup share each staged activation window;
-//   m >  4: staging the activations is the bottleneck (every workgroup reads
-//     all of X), so panels per workgroup go up as far as the panel count
-//     still gives about one workgroup per CU or more.
+// Automatic plan: a pure function of (format, m, n, k).  From kernel-duration
+// sweeps on MI355X (NVFP4 17408x5120 and 5120x17408, FP8 6144x5120, warm
+// clocks):
+//   m <= 2: one panel per workgroup, four wavefronts interleaving its
+//     k-steps; activations are a few KiB and cost little.
+//   m >  2: every workgroup reads all of its activation slice from L2, and
+//     all workgroups read the same lines, so the slice traffic must be cut:
+//     one workgroup per CU, each owning up to five panels (three wavefronts
+//     per panel) that share one staged slice.  FP8 at m > 4 does best with
+//     two panels per workgroup and a deep (10 k-step) prefetch.
 int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
-  (void)fmt;
+  (void)n;
   (void)k;
   if (m <= 2) return 1;
-  if (m <= 4) return 4;
-  return panels_of(n) >= 768 ? 3 : 2;
-}
-
-int gemm_ring_slots(uint32_t fmt, int waves_per_panel, int m, int slots) {
-  const int ks = fmt == kFmtNvfp4 ? kNvKStep : kF8KStep;
-  return ring_slots_of(ks, waves_per_panel, gemm_activation_rows(m), slots);
+  if (fmt == kFmtFp8) return m <= 4 ? 1 : 10;
+  return 5;
 }
 
 bool gemm_plan_info(int id, GemmPlan* out) {
@@ -440,15 +505,63 @@ bool gemm_plan_info(int id, GemmPlan* out) {
   return true;
 }
 
-hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, int plan) {
-  const int id = plan > 0 ? plan : gemm_auto_plan(fmt, a.m, a.n, a.k);
-  if (fmt == kFmtNvfp4)
-    return argmax ? launch_plan<kFmtNvfp4, true>(a, id) : launch_plan<kFmtNvfp4, false>(a, id);
-  if (argmax) return hipErrorInvalidValue;
-  return launch_plan<kFmtFp8, false>(a, id);
+// Splits for a plan: the fewest K ranges whose activation slice fits the LDS
+// budget, then more (while each wavefront keeps >= 2 k-steps per range) until
+// there are at least kMinWorkgroups workgroups.  Splits > 1 need workspace;
+// with less of it the launch uses fewer splits, down to the fewest that fit
+// LDS (kGemmNoWorkspace when even those do not fit the workspace).
+int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t ws_bytes,
+                    size_t ws_offset, GemmLaunch* out) {
+  GemmPlan pl;
+  const int id = plan > 0 ? plan : gemm_auto_plan(fmt, m, n, k);
+  if (!gemm_plan_info(id, &pl)) return kGemmBadPlan;
+  const int64_t P = panels_of(n);
+  const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
+  // Panel groups per K range: enough to give every CU a workgroup when the
+  // panel count allows it, with at most G panels each (spread evenly).
+  int64_t groups = (P + pl.panels_per_workgroup - 1) / pl.panels_per_workgroup;
+  const int64_t xs = x_step_bytes(fmt, m);
+  auto steps_of = [&](int64_t s) { return J > 0 ? (J + s - 1) / s : 1; };
+  // fewest splits whose slice fits the budget
+  int64_t smin = J > 0 ? (J * xs + kSliceBudget - 1) / kSliceBudget : 1;
+  if (smin < 1) smin = 1;
+  if (smin > J && J > 0) smin = J;
+  int64_t S = smin;
+  // spreading panels thinner costs nothing; splitting K more costs a fixup
+  if (groups * S < kMinWorkgroups)
+    groups = std::min<int64_t>(P, (kMinWorkgroups + S - 1) / S);
+  if (groups < 1) groups = 1;
+  while (groups * S < kMinWorkgroups && (J + S) / (S + 1) >= 2 * pl.waves_per_panel) ++S;
+  auto need = [&](int64_t s) -> size_t {
+    if (s <= 1) return 0;
+    const size_t counters = ((size_t)groups * 4 + 255) / 256 * 256;
+    return counters + (size_t)s * groups * pl.panels_per_workgroup * kLanes * 16;
+  };
+  while (S > smin && ws_offset + need(S) > ws_bytes) --S;
+  if (S > 1 && ws_offset + need(S) > ws_bytes) return kGemmNoWorkspace;
+  const int64_t steps = steps_of(S);
+  S = J > 0 ? (J + steps - 1) / steps : 1;  // drop empty trailing ranges
+  out->plan = id;
+  out->waves_per_panel = pl.waves_per_panel;
+  out->panels_per_workgroup = pl.panels_per_workgroup;
+  out->depth = pl.depth;
+  out->groups = groups;
+  out->splits = (int)S;
+  out->split_steps = (int)steps;
+  out->ws_counters_offset = ws_offset;
+  out->ws_partial_offset = ws_offset + (((size_t)groups * 4 + 255) / 256 * 256);
+  out->ws_needed = ws_offset + need(S);
+  return kGemmLaunchOk;
 }
 
-hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t panels, int m, int32_t* argmax,
+hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmLaunch& l) {
+  if (fmt == kFmtNvfp4)
+    return argmax ? launch_plan<kFmtNvfp4, true>(a, l) : launch_plan<kFmtNvfp4, false>(a, l);
+  if (argmax) return hipErrorInvalidValue;
+  return launch_plan<kFmtFp8, false>(a, l);
+}
+
+hipError_t launch_argmax_finalize(uint64_t* keys, int64_t panels, int m, int32_t* argmax,
                                   void* stream) {
   hipLaunchKernelGGL(argmax_finalize_kernel, dim3(m), dim3(256), 0, (hipStream_t)stream, keys,
                      panels, argmax);

@@ -14,37 +14,53 @@ struct GemmArgs {
   int64_t n;
   int64_t k;
   uint64_t* keys;  // lm_head only: [m, panels] argmax keys
+  void* ws;        // caller workspace (split-K partials and counters), may be NULL
   void* stream;
 };
 
-// One compiled GEMM configuration: W compute wavefronts per 16-row panel,
-// G panels per workgroup (plus one loader wavefront), D k-step windows of
-// weight loads in flight per wavefront, NB activation windows in the LDS ring.
+// One compiled GEMM configuration: W wavefronts per 16-row panel, G panels
+// per workgroup, D k-steps of weight loads in flight per wavefront.
 struct GemmPlan {
   int waves_per_panel;
   int panels_per_workgroup;
   int depth;
-  int lds_slots;
 };
 
-// The plan used when none is forced: a pure function of the call's shape,
-// so launch geometry never depends on anything else.
-int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k);
+// Everything one launch needs: the plan plus its K split and workspace use.
+struct GemmLaunch {
+  int plan;
+  int waves_per_panel;
+  int panels_per_workgroup;
+  int depth;
+  int64_t groups;       // workgroups per K range
+  int splits;           // K ranges (workgroups = groups * splits)
+  int split_steps;      // k-steps per K range
+  size_t ws_counters_offset;
+  size_t ws_partial_offset;
+  size_t ws_needed;     // bytes of workspace this launch uses (from offset 0)
+};
 
-// Activation rows staged per LDS window for m rows (1, 2, 4 or 8).
+// Activation rows staged per LDS slice for m rows (1, 2, 4 or 8).
 int gemm_activation_rows(int m);
 
-// Activation ring slots a plan with `slots` gets for m rows (fewer when its
-// windows are wide).
-int gemm_ring_slots(uint32_t fmt, int waves_per_panel, int m, int slots);
+// The plan used when none is forced: a pure function of the call's shape.
+int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k);
 
 // Plan `id` (1-based) of the compiled table; false if there is none.
 bool gemm_plan_info(int id, GemmPlan* out);
 
-// Launch the GEMM (and, with `argmax`, the per-panel argmax keys) with plan
-// `plan`, or the automatic plan when `plan` is 0.
-hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, int plan);
-hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t panels, int m, int32_t* argmax,
+// The launch for plan `plan` (0 = automatic) given `ws_bytes` of workspace
+// whose first `ws_offset` bytes are taken; a pure function of its arguments.
+constexpr int kGemmLaunchOk = 0;
+constexpr int kGemmBadPlan = 1;       // unknown plan id
+constexpr int kGemmNoWorkspace = 2;   // K must be split and the workspace is too small
+int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t ws_bytes,
+                    size_t ws_offset, GemmLaunch* out);
+
+// Launch the GEMM (and, with `argmax`, the per-panel argmax keys).
+hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmLaunch& l);
+
+hipError_t launch_argmax_finalize(uint64_t* keys, int64_t panels, int m, int32_t* argmax,
                                   void* stream);
 
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream);

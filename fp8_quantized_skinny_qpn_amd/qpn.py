@@ -111,16 +111,17 @@ class Plan:
     waves_per_panel: int
     panels_per_workgroup: int
     prefetch_depth: int
-    lds_slots: int
+    splits: int
     activation_rows: int
 
     @property
     def waves_per_workgroup(self) -> int:
-        return self.waves_per_panel * self.panels_per_workgroup + 1
+        return self.waves_per_panel * self.panels_per_workgroup
 
 
 def gemm_plan(op: int, m: int, n: int, k: int) -> Plan:
-    """The launch plan the library uses for a call of kind `op`."""
+    """The launch plan the library uses for a call of kind `op` (given the
+    workspace qpn_workspace_bytes asks for)."""
     wg = ctypes.c_int64()
     outs = [ctypes.c_int() for _ in range(5)]
     check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *[ctypes.byref(o) for o in outs]))
@@ -133,8 +134,22 @@ def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:
     pl = gemm_plan(op, m, n, k)
     f = 1 if fmt == FMT_NVFP4 else 2
     return (f"qpn::skinny_gemm_kernel<{f}u, {pl.waves_per_panel}, {pl.panels_per_workgroup}, "
-            f"{pl.prefetch_depth}, {pl.lds_slots}, {pl.activation_rows}, "
-            f"{'true' if lmhead else 'false'}>")
+            f"{pl.prefetch_depth}, {pl.activation_rows}, {'true' if lmhead else 'false'}>")
+
+
+# Zero-initialised workspaces, one per (device, stream): the library leaves a
+# workspace's split-K counters at zero after every call, so a workspace is
+# zeroed once, when it is allocated, and then reused by calls on its stream.
+_workspaces = {}
+
+
+def workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
+    key = (torch.device(device).index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
 
 
 @dataclass
@@ -187,18 +202,26 @@ def _x_check(x, k):
         raise ValueError(f"activation K {x.shape[1]} does not match the packed K {k}")
 
 
-def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """Y = X * What^T through qpn_gemm_nvfp4 / qpn_gemm_fp8."""
+def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=None,
+         ws: torch.Tensor = None) -> torch.Tensor:
+    """Y = X * What^T through qpn_gemm_nvfp4 / qpn_gemm_fp8.  `ws` (zero-filled
+    before its first use) defaults to a cached per-stream workspace."""
     _x_check(x, pw.k)
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+    op = OP_GEMM_NVFP4 if pw.fmt == FMT_NVFP4 else OP_GEMM_FP8
     fn = lib.qpn_gemm_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_fp8
-    check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k, None, 0, _stream(stream)))
+    st = _stream(stream)
+    need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
+    if ws is None and need > 0:
+        ws = workspace(need, x.device, st.value or 0)
+    check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k,
+             _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, st))
     return out
 
 
-def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, workspace=None,
+def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, workspace_=None,
                  stream=None):
     """(logits fp16 [m, n], argmax int32 [m]) through qpn_lmhead_nvfp4."""
     if pw.fmt != FMT_NVFP4:
@@ -209,11 +232,11 @@ def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, wo
         logits = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
     if argmax is None:
         argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
+    st = _stream(stream)
     need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k)
-    if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+    ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, st.value or 0)
     check(lib.qpn_lmhead_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax), m, pw.n, pw.k,
-                               _ptr(workspace), workspace.numel(), _stream(stream)))
+                               _ptr(ws), ws.numel(), st))
     return logits, argmax
 
 

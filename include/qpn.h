@@ -37,7 +37,12 @@
  *     allocates, frees, copies to the host or synchronises.
  *   - The caller owns every buffer.  A packed blob is opaque and versioned;
  *     it records its own n, k and scales, so GEMM calls need no host reads.
- *   - Calls that share a workspace must not overlap.
+ *     A GEMM reads at most qpn_*_packed_bytes(n, k) bytes of `packed` for
+ *     its own format; passing a smaller buffer is undefined behaviour.
+ *   - Workspace (split-K partial sums and arrival counters, lm_head argmax
+ *     keys) must be zero-filled before its first use; every call leaves it
+ *     zero-filled again, so a workspace is zeroed once and then reused.
+ *     Calls that share a workspace must not overlap.
  *   - Argument checks run on the host before anything is enqueued; on any
  *     error nothing is launched.  Device faults surface, as usual for HIP,
  *     at the caller's next synchronisation.  Nothing is printed and no C++
@@ -95,23 +100,30 @@ QPN_API size_t qpn_nvfp4_packed_bytes(int64_t n, int64_t k);
  * Pure host computation. */
 QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
 
-/* Workspace bytes a call of kind `op` (QPN_OP_*) with these sizes needs.
- * The GEMM calls need none (0); the lm_head needs 8 * m * ceil(n / 16).
- * Returns (size_t)-1 for an unknown op or invalid shape.  Pure host. */
+/* Workspace bytes a call of kind `op` (QPN_OP_*) with these sizes uses for
+ * its preferred launch plan: 0 when that plan does not split K (the GEMMs
+ * then accept a NULL workspace), else room for per-split FP32 partial tiles
+ * and per-panel-group counters; the lm_head needs at least 8 * m *
+ * ceil(n / 16) bytes for its argmax keys plus any split-K room.  A call
+ * given less workspace than this still runs, with fewer K splits, as long as
+ * the fewest splits whose activation slice (m * K / splits FP16 values) fits
+ * in LDS still fit the workspace; otherwise it returns QPN_ERR_BUFFER (only
+ * for large m * k, e.g. m > 4 with k = 17408).  Returns (size_t)-1 for an
+ * unknown op or invalid shape.  Pure host. */
 QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
 
-/* Launch plan a call of kind `op` (QPN_OP_*) uses for (m, n, k): the number
- * of workgroups; the compute wavefronts per 16-row panel (they interleave
- * the panel's k-steps); the panels per workgroup (a workgroup also has one
- * wavefront that stages activations in LDS); the k-steps each compute
- * wavefront keeps in flight; the activation windows in the LDS ring; and
- * the activation rows staged per window (1, 2, 4 or 8 >= m).  A pure
- * function of the shape (and of a plan forced with qpn_debug_set_plan),
- * independent of any declared maximum.  Any output pointer may be NULL.
- * Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
+/* Launch plan a call of kind `op` (QPN_OP_*) uses for (m, n, k) when given
+ * the workspace qpn_workspace_bytes asks for: the number of workgroups; the
+ * wavefronts per 16-row panel (they interleave the panel's k-steps); the
+ * panels per workgroup; the k-steps each wavefront keeps in flight; the
+ * number of K ranges ("splits", > 1 when partial sums are combined across
+ * workgroups); and the activation rows staged in LDS (1, 2, 4 or 8 >= m).
+ * A pure function of the shape (and of a plan forced with
+ * qpn_debug_set_plan), independent of any declared maximum.  Any output
+ * pointer may be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
                           int *waves_per_panel, int *panels_per_workgroup,
-                          int *prefetch_depth, int *lds_slots, int *activation_rows);
+                          int *prefetch_depth, int *splits, int *activation_rows);
 
 /* NVFP4 pack ("pure round" quantisation, lcz.me quantisation-option table,
  * NVFP4-NVIDIA row; format per the lcz.me NVFP4 support table).
@@ -137,9 +149,11 @@ QPN_API int qpn_pack_fp8(const float *w, int64_t n, int64_t k, void *packed,
  * at M=1 and M=8; aiwitness.kr section "내가 실제로 만든 것").
  * Y[m, n] = FP16_RNE( sum_k X[m, k] * What[n, k] ), What = E2M1 * UE4M3 * g,
  * with FP32 accumulation.  packed: blob from qpn_pack_nvfp4 for this (n, k).
- * x: [m, k] FP16, y: [m, n] FP16.  workspace may be NULL (0 bytes needed).
- * If the blob header does not describe an NVFP4 [n, k] weight the kernel
- * writes FP16 NaN to every output instead of computing. */
+ * x: [m, k] FP16, y: [m, n] FP16.  workspace: zero-filled device memory of
+ * workspace_bytes bytes (see qpn_workspace_bytes; NULL with 0 bytes is
+ * valid and only limits the launch plan).  If the blob header does not
+ * describe an NVFP4 [n, k] weight the kernel writes FP16 NaN to every
+ * output. */
 QPN_API int qpn_gemm_nvfp4(const void *packed, const uint16_t *x, uint16_t *y, int m,
                    int64_t n, int64_t k, void *workspace,
                    size_t workspace_bytes, void *stream);
@@ -157,9 +171,9 @@ QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int
  * proposed by greedy / local argmax).  Computes logits exactly as
  * qpn_gemm_nvfp4 and, per row m, argmax[m] = the lowest index n whose FP16
  * logit equals the row maximum (values compared as numbers: -0 == +0).
- * n >= 1 is required.  workspace: >= qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4,
- * m, n, k) bytes of device memory, contents ignored and overwritten.  Two
- * kernels on `stream`. */
+ * n >= 1 is required.  workspace: zero-filled device memory of at least
+ * 8 * m * ceil(n / 16) bytes (qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4, m, n,
+ * k) for the preferred plan).  Two kernels on `stream`. */
 QPN_API int qpn_lmhead_nvfp4(const void *packed, const uint16_t *x, uint16_t *logits,
                      int32_t *argmax, int m, int64_t n, int64_t k,
                      void *workspace, size_t workspace_bytes, void *stream);

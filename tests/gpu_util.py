@@ -52,3 +52,17 @@ def parity(y_gpu_f16, y_ref, what=""):
     assert worst <= bound, f"{what}: max |err| {worst:.3e} > {bound:.3e}"
     assert frob <= FROB_RTOL, f"{what}: relative Frobenius {frob:.3e} > {FROB_RTOL}"
     return worst / bound, frob
+
+
+def plan_ids():
+    """Every launch plan id the library accepts (probed through the C ABI)."""
+    from fp8_quantized_skinny_qpn_amd import qpn
+    ids = []
+    for i in range(1, 65):
+        try:
+            qpn.debug_set_plan(i)
+        except qpn.QpnError:
+            continue
+        ids.append(i)
+    qpn.debug_set_plan(0)
+    return ids

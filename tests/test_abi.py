@@ -60,20 +60,33 @@ def test_packed_sizes(qpn):
 
 
 def test_gemm_plan(qpn):
-    # workgroups cover the 16-row panels; a pure function of the shape
+    # workgroups cover the 16-row panels once per K split; a pure function of the shape
     for op, m, n, k in [(1, 1, 17408, 5120), (1, 8, 17408, 5120), (1, 4, 5120, 17408),
-                        (2, 2, 6144, 5120), (3, 8, 151936, 5120), (1, 3, 17, 16), (2, 7, 24, 8)]:
+                        (1, 8, 5120, 17408), (2, 2, 6144, 5120), (3, 8, 151936, 5120),
+                        (1, 3, 17, 16), (2, 7, 24, 8), (1, 8, 64, 1 << 20)]:
         pl = qpn.gemm_plan(op, m, n, k)
         panels = -(-n // 16)
-        assert pl.workgroups == -(-panels // pl.panels_per_workgroup)
-        assert pl.waves_per_panel in (1, 2, 4, 8) and pl.panels_per_workgroup >= 1
-        assert 2 <= pl.waves_per_workgroup <= 16
-        assert pl.prefetch_depth >= 1 and pl.lds_slots >= 2
+        assert pl.workgroups % pl.splits == 0
+        groups = pl.workgroups // pl.splits
+        # panel groups hold at most panels_per_workgroup panels, spread evenly
+        assert groups * pl.panels_per_workgroup >= panels and 1 <= groups <= max(panels, 1)
+        assert pl.waves_per_panel in (1, 2, 3, 4, 8) and pl.panels_per_workgroup >= 1
+        assert 1 <= pl.waves_per_workgroup <= 16
+        assert pl.prefetch_depth >= 1 and pl.splits >= 1
         assert pl.activation_rows in (1, 2, 4, 8) and pl.activation_rows >= m
         assert pl.activation_rows < 2 * m or m == 0
+        # the activation slice of one split fits in LDS
+        ks = 128 if op != 2 else 64
+        steps = -(-(-(-k // ks)) // pl.splits)
+        assert steps * ks * pl.activation_rows * 2 <= 160 * 1024
         assert pl == qpn.gemm_plan(op, m, n, k)
+        ws = qpn.workspace_bytes(op, m, n, k)
+        if op != 3:
+            assert (ws == 0) == (pl.splits == 1)
         name = qpn.kernel_name(qpn.FMT_NVFP4 if op != 2 else qpn.FMT_FP8, m, n, k, lmhead=op == 3)
         assert name.startswith("qpn::skinny_gemm_kernel<") and name.endswith(">")
+    # K = 2^20 at M = 8 cannot be staged whole: it is split
+    assert qpn.gemm_plan(1, 8, 64, 1 << 20).splits > 1
     with pytest.raises(qpn.QpnError):
         qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 16, 24)
     with pytest.raises(qpn.QpnError):
@@ -88,11 +101,20 @@ def test_plan_override_rejects_unknown_ids(qpn):
     qpn.debug_set_plan(0)
 
 
+def _split_ws(pl):
+    groups = pl.workgroups // pl.splits
+    return 0 if pl.splits == 1 else -(-groups * 4 // 256) * 256 + pl.splits * groups * pl.panels_per_workgroup * 1024
+
+
 def test_workspace_sizes(qpn):
-    assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 5120, 17408) == 0
-    assert qpn.workspace_bytes(qpn.OP_GEMM_FP8, 4, 5120, 5120) == 0
+    for op, m, n, k in [(1, 8, 5120, 17408), (1, 1, 5120, 17408), (2, 4, 5120, 5120), (1, 1, 2048, 2048),
+                        (1, 8, 17408, 5120), (2, 8, 7168, 5120)]:
+        assert qpn.workspace_bytes(op, m, n, k) == _split_ws(qpn.gemm_plan(op, m, n, k))
+    assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 1, 17408, 5120) == 0
+    assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 5120, 17408) > 0   # K is split
     assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 8, 151936, 5120) == 8 * 8 * 9496
     assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 1, 17, 16) == 8 * 2
+    assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 0, 16, 16) == 0
     big = ctypes.c_size_t(-1).value
     assert qpn.workspace_bytes(99, 1, 16, 16) == big
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 9, 16, 16) == big

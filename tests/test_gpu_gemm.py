@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from fp8_quantized_skinny_qpn_amd import synth
-from gpu_util import dev, host, log, need_gpu, parity
+from gpu_util import dev, host, log, need_gpu, parity, plan_ids
 
 pytestmark = pytest.mark.gpu
 
@@ -179,7 +179,7 @@ def test_header_mismatch_yields_nan():
 # prefetch depth) on shapes with a partial last workgroup, a ragged K tail and
 # k-step counts that no plan's wavefront count divides.
 PLAN_SHAPES = [(37, 80), (300, 2064), (48, 9008), (16, 128)]
-PLAN_IDS = list(range(1, 9))
+PLAN_IDS = plan_ids()
 
 
 @pytest.mark.parametrize("plan", PLAN_IDS)
@@ -221,3 +221,39 @@ def test_every_plan_full_size_rows(plan):
                 parity(y[:, rows], ref[:m], f"plan {plan} nvfp4 {n}x{k} m={m}")
     finally:
         qpn.debug_set_plan(0)
+
+
+def test_split_k_workspace_reuse_and_determinism():
+    """Split-K plans: the same call repeated on one workspace gives identical
+    bits (the arrival counters re-arm themselves), matches the oracle, and a
+    call given no workspace (no split) agrees within the parity bar."""
+    qpn = need_gpu()
+    for fmt, (n, k) in (("nvfp4", (300, 4096)), ("fp8", (200, 8192)), ("nvfp4", (5120, 17408))):
+        w = synth.weights(n, k, seed=11)
+        x8 = synth.activations(8, k, seed=11)
+        pw = qpn.pack_nvfp4(dev(w)) if fmt == "nvfp4" else qpn.pack_fp8(dev(w))
+        op = qpn.OP_GEMM_NVFP4 if fmt == "nvfp4" else qpn.OP_GEMM_FP8
+        for m in (1, 4, 8):
+            pl = qpn.gemm_plan(op, m, n, k)
+            need = qpn.workspace_bytes(op, m, n, k)
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+            log(f"split-K {fmt} {n}x{k} m={m} splits={pl.splits}")
+            ys = [host(qpn.gemm(pw, dev(x8[:m]), ws=ws)) for _ in range(3)]
+            for yy in ys[1:]:
+                assert np.array_equal(yy.view(np.uint16), ys[0].view(np.uint16))
+            assert not host(ws).any(), "workspace not left zero-filled"
+            try:
+                y0 = host(qpn.gemm(pw, dev(x8[:m]), ws=torch.zeros(0, dtype=torch.uint8, device="cuda")))
+            except qpn.QpnError as e:
+                # only where one activation slice of the whole K cannot fit in LDS
+                assert e.status == 4 and pl.activation_rows * k * 2 > 80 * 1024, e
+                y0 = None
+            if fmt == "nvfp4":
+                rows = np.arange(n) if n <= 300 else _sample_rows(n, 128, seed=3)
+                ref = _oracle_nvfp4_rows(w, rows, x8[:m])
+            else:
+                rows = np.arange(n)
+                ref = _oracle_fp8_rows(w, rows, x8[:m])
+            parity(ys[0][:, rows], ref, f"split {fmt} {n}x{k} m={m}")
+            if y0 is not None:
+                parity(y0[:, rows], ref, f"unsplit {fmt} {n}x{k} m={m}")

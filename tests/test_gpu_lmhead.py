@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from fp8_quantized_skinny_qpn_amd import synth
-from gpu_util import dev, host, log, need_gpu, parity
+from gpu_util import dev, host, log, need_gpu, parity, plan_ids
 
 pytestmark = pytest.mark.gpu
 
@@ -142,7 +142,7 @@ def test_lmhead_full_vocab(m):
     _check_argmax(am, lg, y_ref, f"lmhead full m={m}")
 
 
-@pytest.mark.parametrize("plan", list(range(1, 9)))
+@pytest.mark.parametrize("plan", plan_ids())
 def test_lmhead_every_plan(plan):
     qpn = need_gpu()
     n, k = 4099, 1040
@@ -161,3 +161,25 @@ def test_lmhead_every_plan(plan):
             _check_argmax(am, lg, y_ref, f"lmhead plan {plan} m={m}")
     finally:
         qpn.debug_set_plan(0)
+
+
+def test_lmhead_leaves_workspace_zeroed():
+    """The argmax keys (and any split-K partials) are cleared after use, so one
+    zero-filled workspace serves lm_head and GEMM calls of any shape."""
+    qpn = need_gpu()
+    n, k = 3000, 2048
+    w = synth.weights(n, k, seed=5)
+    x = synth.activations(8, k, seed=5)
+    pw = qpn.pack_nvfp4(dev(w))
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    first = None
+    for m in (8, 1, 8):
+        lg, am = qpn.lmhead_nvfp4(pw, dev(x[:m]), workspace_=ws)
+        assert not host(ws).any()
+        y = host(qpn.gemm(pw, dev(x[:m]), ws=ws))
+        assert not host(ws).any()
+        assert np.array_equal(y.view(np.uint16), host(lg).view(np.uint16))
+        if m == 8:
+            if first is None:
+                first = host(am)
+            assert np.array_equal(host(am), first)
