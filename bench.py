@@ -206,6 +206,30 @@ def read_ceiling(qpn, torch):
     return (2 << 30) / float(np.median(ts)) / 1e9
 
 
+def traffic_workload(qpn, torch):
+    """Workload for the rocprofv3 PMC passes (FETCH_SIZE, WRITE_SIZE), one per
+    run: calibration kernels of known size (a 256 MiB streaming read and a
+    256 MiB fill), then each headline call six times on rotating copies."""
+    cal = 256 << 20
+    buf = torch.empty(cal, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        qpn.debug_read_ceiling(buf, sink)
+    for _ in range(3):
+        buf.zero_()
+    torch.cuda.synchronize()
+    del buf
+    for name, n, k, fmt in HEADLINE:
+        s = Shape(qpn, torch, name, n, k, fmt, HEADLINE_M)
+        for m in s.ms:
+            for _ in range(6):
+                qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws)
+            torch.cuda.synchronize()
+            log(f"{name} M={m}: {qpn.kernel_name(fmt, m, n, k)}")
+        del s
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +237,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--extra", action="store_true", help="also time the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-workload", action="store_true",
+                    help="only run the workload of the PMC traffic passes (no JSON line)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -226,6 +252,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     from fp8_quantized_skinny_qpn_amd import qpn  # fails loudly when libqpn.so is missing
+    if args.traffic_workload:
+        traffic_workload(qpn, torch)
+        return
 
     log("setting up headline shapes")
     shapes = [Shape(qpn, torch, name, n, k, fmt, HEADLINE_M) for name, n, k, fmt in HEADLINE]

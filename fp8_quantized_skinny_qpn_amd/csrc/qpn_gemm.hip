@@ -306,12 +306,16 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
 
   // ---- 5. split-K: partial tiles, arrival count, last arriver sums ----
   if (S > 1) {
-    float* mine = sp.partial + ((((int64_t)split * groups + grp) * G + gi) * kLanes + lane) * 4;
-    if (lead) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        __hip_atomic_store(mine + v, acc[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // Partial tiles go through a buffer descriptor with the device-scope
+    // cache policy (sc1: written through to memory, read coherently), one
+    // 16-byte access per lane, so no cache maintenance is needed.
+    constexpr int kDevScope = 16;  // sc1
+    const int64_t tiles = (int64_t)S * groups * G;
+    const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sp.partial, (short)0, (int)(tiles * kLanes * 16), kRsrcFlags);
+    const int mine = (int)((((int64_t)split * groups + grp) * G + gi) * kLanes + lane) * 16;
+    if (lead)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), pres, mine, 0, kDevScope);
     wait_vmcnt<0>();  // this wavefront's partial stores are complete at device scope
     bare_barrier();
     uint32_t* arrived = reinterpret_cast<uint32_t*>(smem);
@@ -327,19 +331,16 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
     bare_barrier();
     if (*arrived != (uint32_t)(S - 1)) return;  // uniform over the workgroup
     if (lead) {
-      const int64_t per_split = groups * G * kLanes * 4;
-      float* first = sp.partial + ((((int64_t)grp) * G + gi) * kLanes + lane) * 4;
+      const int per_split = (int)(groups * G * kLanes * 16);
+      const int first = (int)((((int64_t)grp) * G + gi) * kLanes + lane) * 16;
       acc = float4v{0.f, 0.f, 0.f, 0.f};
-      for (int sx = 0; sx < S; ++sx) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[v] += __hip_atomic_load(first + sx * per_split + v, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int sx = 0; sx < S; ++sx)
+        acc += __builtin_bit_cast(
+            float4v, __builtin_amdgcn_raw_buffer_load_b128(pres, first + sx * per_split, 0, kDevScope));
       // this is the only reader: clear the partials so the workspace is all
       // zeros again when the call ends (whatever layout the next call uses)
       for (int sx = 0; sx < S; ++sx)
-        *reinterpret_cast<float4v*>(first + sx * per_split) = float4v{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres, first + sx * per_split, 0, 0);
     }
   }
   if (!lead || !active) return;
