@@ -136,7 +136,7 @@ size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
 
 int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
                   int* panels_per_workgroup, int* prefetch_depth, int* splits,
-                  int* activation_rows) {
+                  int* activation_rows, int64_t* split_workgroups) {
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
   uint32_t fmt;
   switch (op) {
@@ -156,12 +156,13 @@ int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int*
   if (gemm_launch_for(fmt, m, n, k, forced_plan(), (size_t)-1, lm ? lmhead_split_offset(m, n) : 0,
                       &l) != kGemmLaunchOk)
     return QPN_ERR_SHAPE;
-  if (workgroups) *workgroups = l.groups * l.splits;
+  if (workgroups) *workgroups = l.workgroups;
   if (waves_per_panel) *waves_per_panel = l.waves_per_panel;
   if (panels_per_workgroup) *panels_per_workgroup = l.panels_per_workgroup;
   if (prefetch_depth) *prefetch_depth = l.depth;
   if (splits) *splits = l.splits;
   if (activation_rows) *activation_rows = gemm_activation_rows(m);
+  if (split_workgroups) *split_workgroups = l.split_wgs;
   return QPN_OK;
 }
 

@@ -121,6 +121,8 @@ struct SplitArgs {
   int split_steps;       // k-steps per K range (the last may be shorter)
   float* partial;        // [S][groups][G][64 lanes][4] FP32 partial tiles
   uint32_t* counters;    // [groups] arrivals; zero between calls
+  int split_wgs;         // workgroups [0, split_wgs) work on K ranges of panels [full_panels, P)
+  int full_panels;       // workgroups from split_wgs on take panels [0, full_panels) whole
 };
 
 template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX>
@@ -142,19 +144,28 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int64_t P = panels_of(n);
   const int J = (int)((k + KS - 1) / KS);
-  const int S = sp.splits;
-  const int grp = (int)(blockIdx.x / S);
-  const int split = (int)(blockIdx.x % S);
-  const int j0 = split * sp.split_steps;                       // first k-step of the range
-  const int nj = max(0, min(J - j0, sp.split_steps));          // k-steps in the range
+  // Two segments of workgroups.  The first sp.split_wgs split the panels
+  // [full_panels, P) into S K ranges each (these are dispatched first and
+  // carry the split-K fix-up); the rest take whole panels of [0, full_panels).
+  const bool in_split = (int)blockIdx.x < sp.split_wgs;
+  const int S = in_split ? sp.splits : 1;
+  const int bi = in_split ? (int)blockIdx.x : (int)blockIdx.x - sp.split_wgs;
+  const int grp = bi / S;
+  const int split = bi % S;
+  const int steps = in_split ? sp.split_steps : J;
+  const int j0 = split * steps;                          // first k-step of the range
+  const int nj = max(0, min(J - j0, steps));             // k-steps in the range
 
   const int gi = wv / W;  // panel of this wavefront inside the workgroup
   const int w = wv % W;   // its interleave position
-  // panel group grp owns panels [grp * P / groups, (grp + 1) * P / groups):
-  // G or fewer, spread evenly so that every workgroup has about the same work
-  const int64_t groups = gridDim.x / S;
-  const int64_t pbeg = (int64_t)grp * P / groups;
-  const int64_t pend = (int64_t)(grp + 1) * P / groups;
+  // panel group grp of a segment owns panels [grp * len / groups, (grp + 1) *
+  // len / groups) of it: G or fewer, spread evenly so that every workgroup
+  // has about the same work
+  const int64_t groups = in_split ? sp.split_wgs / S : (int64_t)gridDim.x - sp.split_wgs;
+  const int64_t seg0 = in_split ? sp.full_panels : 0;
+  const int64_t seglen = in_split ? P - sp.full_panels : sp.full_panels;
+  const int64_t pbeg = seg0 + (int64_t)grp * seglen / groups;
+  const int64_t pend = seg0 + (int64_t)(grp + 1) * seglen / groups;
   const int64_t p = pbeg + gi;
   const bool active = p < pend;
   const int row = lane & 15, kg = lane >> 4;
@@ -415,21 +426,19 @@ int x_step_bytes(uint32_t fmt, int m) {
 
 // LDS activation budget per workgroup: two workgroups fit in the 160 KiB of a CU.
 constexpr int kSliceBudget = 80 * 1024;
-// Wanted workgroups per launch: one per CU or more.
-constexpr int64_t kMinWorkgroups = 256;
 
 template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX>
 hipError_t launch_t(const GemmArgs& a, const GemmLaunch& l) {
-  const int xbytes = ((l.split_steps * (Fmt<FMT>::kKStep / 8) * MB + 63) / 64) * 1024;
+  const int xbytes = ((l.slice_steps * (Fmt<FMT>::kKStep / 8) * MB + 63) / 64) * 1024;
   const int red = G * W * kLanes * 16;
   const size_t lds = (size_t)(xbytes > red ? xbytes : red);
-  SplitArgs sp{l.splits, l.split_steps, nullptr, nullptr};
+  SplitArgs sp{l.splits, l.split_steps, nullptr, nullptr, (int)l.split_wgs, (int)l.full_panels};
   if (l.splits > 1) {
     sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
     sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
   }
   hipLaunchKernelGGL((skinny_gemm_kernel<FMT, W, G, D, MB, ARGMAX>),
-                     dim3((unsigned)(l.groups * l.splits)), dim3(kLanes * G * W), lds,
+                     dim3((unsigned)l.workgroups), dim3(kLanes * G * W), lds,
                      (hipStream_t)a.stream, (const uint8_t*)a.packed, a.x, a.y, a.m, a.n, a.k, sp,
                      a.keys);
   return hipGetLastError();
@@ -445,19 +454,19 @@ hipError_t launch_mb(const GemmArgs& a, const GemmLaunch& l) {
   }
 }
 
-// The compiled plans: (W, G, D).
+// The compiled plans: (W, G, D, placement, workgroups wanted).
 constexpr GemmPlan kPlans[] = {
-    {0, 0, 0},    // 0: automatic
-    {4, 1, 4},    // 1
-    {4, 1, 10},   // 2
-    {8, 1, 5},    // 3
-    {8, 1, 9},    // 4
-    {3, 5, 4},    // 5
-    {3, 5, 14},   // 6
-    {8, 2, 9},    // 7
-    {4, 4, 10},   // 8
-    {16, 1, 9},   // 9
-    {4, 2, 10},   // 10
+    {0, 0, 0, 0, 0},          // 0: automatic
+    {4, 1, 4, 0, 256},        // 1
+    {3, 5, 4, 0, 256},        // 2
+    {4, 2, 10, 0, 256},       // 3
+    {8, 1, 3, 2, 256},        // 4
+    {4, 1, 4, 2, 256},        // 5
+    {4, 1, 10, 0, 256},       // 6
+    {8, 1, 5, 0, 256},        // 7
+    {3, 5, 14, 0, 256},       // 8
+    {4, 4, 10, 0, 256},       // 9
+    {3, 4, 4, 2, 256},        // 10
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -465,15 +474,15 @@ template <uint32_t FMT, bool ARGMAX>
 hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
   switch (l.plan) {
     case 1: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
-    case 2: return launch_mb<FMT, 4, 1, 10, ARGMAX>(a, l);
-    case 3: return launch_mb<FMT, 8, 1, 5, ARGMAX>(a, l);
-    case 4: return launch_mb<FMT, 8, 1, 9, ARGMAX>(a, l);
-    case 5: return launch_mb<FMT, 3, 5, 4, ARGMAX>(a, l);
-    case 6: return launch_mb<FMT, 3, 5, 14, ARGMAX>(a, l);
-    case 7: return launch_mb<FMT, 8, 2, 9, ARGMAX>(a, l);
-    case 8: return launch_mb<FMT, 4, 4, 10, ARGMAX>(a, l);
-    case 9: return launch_mb<FMT, 16, 1, 9, ARGMAX>(a, l);
-    case 10: return launch_mb<FMT, 4, 2, 10, ARGMAX>(a, l);
+    case 2: return launch_mb<FMT, 3, 5, 4, ARGMAX>(a, l);
+    case 3: return launch_mb<FMT, 4, 2, 10, ARGMAX>(a, l);
+    case 4: return launch_mb<FMT, 8, 1, 3, ARGMAX>(a, l);
+    case 5: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
+    case 6: return launch_mb<FMT, 4, 1, 10, ARGMAX>(a, l);
+    case 7: return launch_mb<FMT, 8, 1, 5, ARGMAX>(a, l);
+    case 8: return launch_mb<FMT, 3, 5, 14, ARGMAX>(a, l);
+    case 9: return launch_mb<FMT, 4, 4, 10, ARGMAX>(a, l);
+    case 10: return launch_mb<FMT, 3, 4, 4, ARGMAX>(a, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -485,19 +494,27 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 // Automatic plan: a pure function of (format, m, n, k).  From kernel-duration
 // sweeps on MI355X (NVFP4 17408x5120 and 5120x17408, FP8 6144x5120, warm
 // clocks):
-//   m <= 2: one panel per workgroup, four wavefronts interleaving its
-//     k-steps; activations are a few KiB and cost little.
-//   m >  2: every workgroup reads all of its activation slice from L2, and
+//   m <= 2 (FP8: m <= 4): one panel per workgroup, its k-steps interleaved
+//     over the wavefronts; activations are a few KiB and cost little.  When
+//     there are 1-3 panels per CU with a remainder (e.g. 320 panels), whole
+//     panels alone would leave some CUs with twice the bytes of others, so
+//     placement 2 splits only the remainder panels in K (8 wavefronts per
+//     panel for NVFP4): 5120x17408 M=1 went from 13.0 to 11.7 us.
+//   m > 2: every workgroup reads all of its activation slice from L2, and
 //     all workgroups read the same lines, so the slice traffic must be cut:
 //     one workgroup per CU, each owning up to five panels (three wavefronts
 //     per panel) that share one staged slice.  FP8 at m > 4 does best with
 //     two panels per workgroup and a deep (10 k-step) prefetch.
 int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
-  (void)n;
   (void)k;
-  if (m <= 2) return 1;
-  if (fmt == kFmtFp8) return m <= 4 ? 1 : 10;
-  return 5;
+  const int64_t P = panels_of(n);
+  const bool uneven = P >= 256 && P < 3 * 256 && P % 256 >= 16;
+  if (fmt == kFmtNvfp4) {
+    if (m <= 2) return uneven ? 4 : 1;
+    return 2;
+  }
+  if (m <= 4) return uneven ? 5 : 1;
+  return 3;
 }
 
 bool gemm_plan_info(int id, GemmPlan* out) {
@@ -508,7 +525,7 @@ bool gemm_plan_info(int id, GemmPlan* out) {
 
 // Splits for a plan: the fewest K ranges whose activation slice fits the LDS
 // budget, then more (while each wavefront keeps >= 2 k-steps per range) until
-// there are at least kMinWorkgroups workgroups.  Splits > 1 need workspace;
+// there are at least the plan's wanted number of workgroups.  Splits > 1 need workspace;
 // with less of it the launch uses fewer splits, down to the fewest that fit
 // LDS (kGemmNoWorkspace when even those do not fit the workspace).
 int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t ws_bytes,
@@ -522,22 +539,59 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   // panel count allows it, with at most G panels each (spread evenly).
   int64_t groups = (P + pl.panels_per_workgroup - 1) / pl.panels_per_workgroup;
   const int64_t xs = x_step_bytes(fmt, m);
+  const int64_t want = pl.min_workgroups;
   auto steps_of = [&](int64_t s) { return J > 0 ? (J + s - 1) / s : 1; };
   // fewest splits whose slice fits the budget
   int64_t smin = J > 0 ? (J * xs + kSliceBudget - 1) / kSliceBudget : 1;
   if (smin < 1) smin = 1;
   if (smin > J && J > 0) smin = J;
   int64_t S = smin;
-  // spreading panels thinner costs nothing; splitting K more costs a fixup
-  if (groups * S < kMinWorkgroups)
-    groups = std::min<int64_t>(P, (kMinWorkgroups + S - 1) / S);
-  if (groups < 1) groups = 1;
-  while (groups * S < kMinWorkgroups && (J + S) / (S + 1) >= 2 * pl.waves_per_panel) ++S;
-  auto need = [&](int64_t s) -> size_t {
+  auto need_for = [&](int64_t s, int64_t g) -> size_t {
     if (s <= 1) return 0;
-    const size_t counters = ((size_t)groups * 4 + 255) / 256 * 256;
-    return counters + (size_t)s * groups * pl.panels_per_workgroup * kLanes * 16;
+    const size_t counters = ((size_t)g * 4 + 255) / 256 * 256;
+    return counters + (size_t)s * g * pl.panels_per_workgroup * kLanes * 16;
   };
+  // Placement 2: every wanted workgroup slot (one per CU) gets the same
+  // number of whole panels, and the remainder panels are split in K into
+  // about one more workgroup per slot, so that every CU streams the same
+  // bytes.  The split workgroups come first in dispatch order.
+  if (pl.placement == 2 && smin == 1 && J > 0) {
+    const int64_t G = pl.panels_per_workgroup;
+    const int64_t q = P / (want * G);
+    const int64_t full = q * want * G;
+    const int64_t rem = P - full;
+    if (q >= 1 && rem > 0) {
+      const int64_t gs = rem;  // one remainder panel per split group
+      int64_t s0 = std::max<int64_t>(1, (want + gs / 2) / gs);
+      s0 = std::min<int64_t>(s0, std::max<int64_t>(1, J / (2 * pl.waves_per_panel)));
+      const int64_t st0 = steps_of(s0);
+      s0 = (J + st0 - 1) / st0;
+      if (ws_offset + need_for(s0, gs) <= ws_bytes) {
+        out->plan = id;
+        out->waves_per_panel = pl.waves_per_panel;
+        out->panels_per_workgroup = pl.panels_per_workgroup;
+        out->depth = pl.depth;
+        out->groups = gs;
+        out->splits = (int)s0;
+        out->split_steps = (int)st0;
+        out->split_wgs = gs * s0;
+        out->full_panels = full;
+        out->workgroups = gs * s0 + full / G;
+        out->slice_steps = (int)J;
+        out->ws_counters_offset = ws_offset;
+        out->ws_partial_offset = ws_offset + (((size_t)gs * 4 + 255) / 256 * 256);
+        out->ws_needed = ws_offset + need_for(s0, gs);
+        return kGemmLaunchOk;
+      }
+    }
+  }
+  // placement 0 spreads the panels thinner (down to one per workgroup)
+  // before splitting K further; placement 1 keeps every workgroup's G panel
+  // slots filled and splits K instead.
+  if (pl.placement == 0 && groups * S < want) groups = std::min<int64_t>(P, (want + S - 1) / S);
+  if (groups < 1) groups = 1;
+  while (groups * S < want && (J + S) / (S + 1) >= 2 * pl.waves_per_panel) ++S;
+  auto need = [&](int64_t s) -> size_t { return need_for(s, groups); };
   while (S > smin && ws_offset + need(S) > ws_bytes) --S;
   if (S > 1 && ws_offset + need(S) > ws_bytes) return kGemmNoWorkspace;
   const int64_t steps = steps_of(S);
@@ -549,6 +603,10 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   out->groups = groups;
   out->splits = (int)S;
   out->split_steps = (int)steps;
+  out->split_wgs = groups * S;
+  out->full_panels = 0;
+  out->workgroups = groups * S;
+  out->slice_steps = (int)steps;
   out->ws_counters_offset = ws_offset;
   out->ws_partial_offset = ws_offset + (((size_t)groups * 4 + 255) / 256 * 256);
   out->ws_needed = ws_offset + need(S);

@@ -20,10 +20,16 @@ struct GemmArgs {
 
 // One compiled GEMM configuration: W wavefronts per 16-row panel, G panels
 // per workgroup, D k-steps of weight loads in flight per wavefront.
+// Placement 0 spreads panels thinner (fewer per workgroup) before splitting
+// K to reach the wanted workgroup count; placement 1 keeps G panels per
+// workgroup and splits K; placement 2 gives every wanted workgroup slot the
+// same whole panels and splits only the remainder.
 struct GemmPlan {
   int waves_per_panel;
   int panels_per_workgroup;
   int depth;
+  int placement;
+  int min_workgroups;  // workgroups wanted per launch
 };
 
 // Everything one launch needs: the plan plus its K split and workspace use.
@@ -32,9 +38,13 @@ struct GemmLaunch {
   int waves_per_panel;
   int panels_per_workgroup;
   int depth;
-  int64_t groups;       // workgroups per K range
-  int splits;           // K ranges (workgroups = groups * splits)
+  int64_t groups;       // panel groups of the split segment
+  int splits;           // K ranges per split-segment group
   int split_steps;      // k-steps per K range
+  int64_t split_wgs;    // workgroups of the split segment (groups * splits), dispatched first
+  int64_t full_panels;  // panels [0, full_panels) taken whole by the other workgroups
+  int64_t workgroups;   // grid size
+  int slice_steps;      // k-steps of the largest activation slice a workgroup stages
   size_t ws_counters_offset;
   size_t ws_partial_offset;
   size_t ws_needed;     // bytes of workspace this launch uses (from offset 0)

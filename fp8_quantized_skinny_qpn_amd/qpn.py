@@ -43,7 +43,7 @@ def _load():
         "qpn_nvfp4_packed_bytes": ([i64, i64], sz),
         "qpn_fp8_packed_bytes": ([i64, i64], sz),
         "qpn_workspace_bytes": ([i32, i32, i64, i64], sz),
-        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp], i32),
+        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
         "qpn_pack_nvfp4": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_pack_fp8": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
@@ -113,6 +113,7 @@ class Plan:
     prefetch_depth: int
     splits: int
     activation_rows: int
+    split_workgroups: int   # workgroups on K ranges; the rest take whole panels
 
     @property
     def waves_per_workgroup(self) -> int:
@@ -123,9 +124,11 @@ def gemm_plan(op: int, m: int, n: int, k: int) -> Plan:
     """The launch plan the library uses for a call of kind `op` (given the
     workspace qpn_workspace_bytes asks for)."""
     wg = ctypes.c_int64()
+    swg = ctypes.c_int64()
     outs = [ctypes.c_int() for _ in range(5)]
-    check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *[ctypes.byref(o) for o in outs]))
-    return Plan(wg.value, *[o.value for o in outs])
+    check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *[ctypes.byref(o) for o in outs],
+                            ctypes.byref(swg)))
+    return Plan(wg.value, *[o.value for o in outs], swg.value)
 
 
 def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:

@@ -117,13 +117,18 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * wavefronts per 16-row panel (they interleave the panel's k-steps); the
  * panels per workgroup; the k-steps each wavefront keeps in flight; the
  * number of K ranges ("splits", > 1 when partial sums are combined across
- * workgroups); and the activation rows staged in LDS (1, 2, 4 or 8 >= m).
- * A pure function of the shape (and of a plan forced with
- * qpn_debug_set_plan), independent of any declared maximum.  Any output
- * pointer may be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
+ * workgroups); the activation rows staged in LDS (1, 2, 4 or 8 >= m); and
+ * split_workgroups, the workgroups that work on K ranges (split_workgroups
+ * / splits panel groups of the last panels, dispatched first).  The other
+ * workgroups - 0 unless the plan balances whole panels per CU - each take
+ * panels_per_workgroup whole panels.  A pure function of the shape (and of
+ * a plan forced with qpn_debug_set_plan), independent of any declared
+ * maximum.  Any output pointer may be NULL.  Returns QPN_OK or
+ * QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
                           int *waves_per_panel, int *panels_per_workgroup,
-                          int *prefetch_depth, int *splits, int *activation_rows);
+                          int *prefetch_depth, int *splits, int *activation_rows,
+                          int64_t *split_workgroups);
 
 /* NVFP4 pack ("pure round" quantisation, lcz.me quantisation-option table,
  * NVFP4-NVIDIA row; format per the lcz.me NVFP4 support table).

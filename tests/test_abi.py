@@ -66,18 +66,24 @@ def test_gemm_plan(qpn):
                         (1, 3, 17, 16), (2, 7, 24, 8), (1, 8, 64, 1 << 20)]:
         pl = qpn.gemm_plan(op, m, n, k)
         panels = -(-n // 16)
-        assert pl.workgroups % pl.splits == 0
-        groups = pl.workgroups // pl.splits
-        # panel groups hold at most panels_per_workgroup panels, spread evenly
-        assert groups * pl.panels_per_workgroup >= panels and 1 <= groups <= max(panels, 1)
+        ks = 128 if op != 2 else 64
+        J = -(-k // ks)
+        assert 1 <= pl.split_workgroups <= pl.workgroups
+        assert pl.split_workgroups % pl.splits == 0
+        groups = pl.split_workgroups // pl.splits
+        whole = pl.workgroups - pl.split_workgroups
+        # the split segment's groups and the whole-panel workgroups cover every
+        # panel, at most panels_per_workgroup per workgroup
+        assert (groups + whole) * pl.panels_per_workgroup >= panels
+        assert 1 <= groups <= max(panels, 1)
         assert pl.waves_per_panel in (1, 2, 3, 4, 8) and pl.panels_per_workgroup >= 1
         assert 1 <= pl.waves_per_workgroup <= 16
         assert pl.prefetch_depth >= 1 and pl.splits >= 1
         assert pl.activation_rows in (1, 2, 4, 8) and pl.activation_rows >= m
         assert pl.activation_rows < 2 * m or m == 0
-        # the activation slice of one split fits in LDS
-        ks = 128 if op != 2 else 64
-        steps = -(-(-(-k // ks)) // pl.splits)
+        # the activation slice a workgroup stages fits in LDS (whole-panel
+        # workgroups stage all of K)
+        steps = J if whole else -(-J // pl.splits)
         assert steps * ks * pl.activation_rows * 2 <= 160 * 1024
         assert pl == qpn.gemm_plan(op, m, n, k)
         ws = qpn.workspace_bytes(op, m, n, k)
@@ -85,6 +91,9 @@ def test_gemm_plan(qpn):
             assert (ws == 0) == (pl.splits == 1)
         name = qpn.kernel_name(qpn.FMT_NVFP4 if op != 2 else qpn.FMT_FP8, m, n, k, lmhead=op == 3)
         assert name.startswith("qpn::skinny_gemm_kernel<") and name.endswith(">")
+    # 320 panels on 256 CUs: 256 whole panels plus the last 64 split four ways
+    pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)
+    assert (pl.workgroups, pl.split_workgroups, pl.splits) == (512, 256, 4)
     # K = 2^20 at M = 8 cannot be staged whole: it is split
     assert qpn.gemm_plan(1, 8, 64, 1 << 20).splits > 1
     with pytest.raises(qpn.QpnError):
@@ -102,7 +111,7 @@ def test_plan_override_rejects_unknown_ids(qpn):
 
 
 def _split_ws(pl):
-    groups = pl.workgroups // pl.splits
+    groups = pl.split_workgroups // pl.splits
     return 0 if pl.splits == 1 else -(-groups * 4 // 256) * 256 + pl.splits * groups * pl.panels_per_workgroup * 1024
 
 

@@ -223,6 +223,34 @@ def test_every_plan_full_size_rows(plan):
         qpn.debug_set_plan(0)
 
 
+HYBRID = [("nvfp4", 5120, 17408, (1, 2)), ("nvfp4", 4805, 16000, (1, 2)),
+          ("fp8", 6144, 5120, (1, 3, 4)), ("fp8", 4600, 9000, (1, 4))]
+
+
+@pytest.mark.parametrize("fmt,n,k,ms", HYBRID)
+def test_balanced_hybrid_launch(fmt, n, k, ms):
+    """Shapes with 1-3 panels per CU and a remainder: the launch takes whole
+    panels for every CU and splits only the remaining panels in K.  Every row
+    of the split panels and sampled whole-panel rows match the oracle."""
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=n ^ k)
+    x8 = synth.activations(8, k, seed=n ^ k)
+    pw = qpn.pack_nvfp4(dev(w)) if fmt == "nvfp4" else qpn.pack_fp8(dev(w))
+    op = qpn.OP_GEMM_NVFP4 if fmt == "nvfp4" else qpn.OP_GEMM_FP8
+    for m in ms:
+        pl = qpn.gemm_plan(op, m, n, k)
+        whole = pl.workgroups - pl.split_workgroups
+        assert whole > 0 and pl.splits > 1, pl
+        first_split_row = whole * pl.panels_per_workgroup * 16
+        rows = np.union1d(np.arange(first_split_row, n), _sample_rows(first_split_row, 96, seed=m))
+        ref = (_oracle_nvfp4_rows if fmt == "nvfp4" else _oracle_fp8_rows)(w, rows, x8[:m])
+        log(f"hybrid {fmt} {n}x{k} m={m} workgroups={pl.workgroups} split={pl.split_workgroups}x{pl.splits}")
+        ws = torch.zeros(max(qpn.workspace_bytes(op, m, n, k), 256), dtype=torch.uint8, device="cuda")
+        y = host(qpn.gemm(pw, dev(x8[:m]), ws=ws))
+        parity(y[:, rows], ref, f"hybrid {fmt} {n}x{k} m={m}")
+        assert not host(ws).any(), "workspace not left zero-filled"
+
+
 def test_split_k_workspace_reuse_and_determinism():
     """Split-K plans: the same call repeated on one workspace gives identical
     bits (the arrival counters re-arm themselves), matches the oracle, and a
