@@ -23,10 +23,12 @@
 //     panels read it from there (ds_read, a separate counter from the weight
 //     loads).  Activation traffic from L2 is (panels / G) * M * K * 2 bytes,
 //     so at M = 8 G is raised to keep it well below the weight bytes.
-//   * Vector memory loads of one wavefront complete in order.  The
-//     activation loads are issued before the weight prefetch, so waiting for
-//     them never waits for weights; after one barrier the main loop has no
-//     barriers and no activation loads at all.
+//   * Vector memory loads of one wavefront complete in order.  Each
+//     wavefront sends its first weight k-step to memory, then its share of
+//     the activation loads, then the rest of its weight prefetch; waiting for
+//     the activations therefore waits for one weight k-step only (its HBM
+//     latency overlaps the L2-served activation reads).  After one barrier
+//     the main loop has no barriers and no activation loads at all.
 //   * Weight loads go through one buffer descriptor per chunk: 32-bit
 //     offsets, and, being memory intrinsics, they keep program order in the
 //     load queue, so every wait count the compiler derives is exact.  Past
@@ -191,31 +193,6 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   }
   asm volatile("" ::: "memory");
 
-  // ---- 1. activation slice -> LDS (issued first: see the header) ----
-  // Unit u (16 bytes) = ((jl * GR + t) * 4 + kg) * MB + mm holds
-  // X[mm][K .. K + 8), K = (j0 + jl) * KS + kg * KS / 4 + 8 t; load q of the
-  // slice fills units [64 q, 64 q + 64).  Rows >= m and K outside the range
-  // read zeros (out-of-range buffer offsets).  Offsets stay below 2^25.
-  {
-    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrcFlags);
-    const int units = nj * XSTEP;
-    const int nq = (units + 63) / 64;
-    for (int q = wv; q < nq; q += NW) {
-      const int u = q * 64 + lane;
-      const int mm = u % MB;
-      const int rest = u / MB;
-      const int jl = rest / (4 * GR);
-      const int kpos = (j0 + jl) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
-      const bool ok = u < units && mm < m && kpos < k;
-      const int off = ok ? (int)(((int64_t)mm * k + kpos) * 2) : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xres, (__attribute__((address_space(3))) void*)(smem + q * 1024), 16, off, 0, 0, 0);
-    }
-  }
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-
   // ---- 2. weight prefetch ----
   // chunk (p, j) = codes + (j * P + p) * chunk bytes (step-major layout)
   const uint8_t* cbase = blob + (FMT == kFmtNvfp4 ? (uint64_t)kHeaderBytes : f8_codes_offset(n)) +
@@ -240,14 +217,43 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   };
 
   WFrag ring[R];
+  // the first k-step goes out before the activation loads, the rest after
+  issue(0, ring[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 1. activation slice -> LDS (after the first weight k-step) ----
+  // Unit u (16 bytes) = ((jl * GR + t) * 4 + kg) * MB + mm holds
+  // X[mm][K .. K + 8), K = (j0 + jl) * KS + kg * KS / 4 + 8 t; load q of the
+  // slice fills units [64 q, 64 q + 64).  Rows >= m and K outside the range
+  // read zeros (out-of-range buffer offsets).  Offsets stay below 2^25.
+  {
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrcFlags);
+    const int units = nj * XSTEP;
+    const int nq = (units + 63) / 64;
+    for (int q = wv; q < nq; q += NW) {
+      const int u = q * 64 + lane;
+      const int mm = u % MB;
+      const int rest = u / MB;
+      const int jl = rest / (4 * GR);
+      const int kpos = (j0 + jl) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
+      const bool ok = u < units && mm < m && kpos < k;
+      const int off = ok ? (int)(((int64_t)mm * k + kpos) * 2) : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)(smem + q * 1024), 16, off, 0, 0, 0);
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
+  for (int i = 1; i < D; ++i) {
     issue(i, ring[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // this wavefront's activation loads (older than the D weight steps) are
-  // in LDS; after the barrier everyone's are
-  wait_vmcnt<D * LPS>();
+  // this wavefront's first k-step and activation loads are in (older than
+  // the other D - 1 weight steps); after the barrier everyone's are
+  wait_vmcnt<(D - 1) * LPS>();
   bare_barrier();
   // the header loads were older than the activation loads: they are in
   // (BlobHeader: magic, format, layout_version, reserved, n, k, ..., tensor_scale at 48)
