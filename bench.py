@@ -334,6 +334,13 @@ def main():
             med = float(np.median(per))
             extra[f"{name}_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
                                      "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
+            # the same weights through the plain GEMM (no argmax), for the argmax's share
+            g = capture(torch, lambda: [qpn.gemm(copies[i % 3], xm, out=lg) for i in range(12)])
+            per = [t / 12 for t in time_graph(torch, g, 5)]
+            del g
+            med = float(np.median(per))
+            extra[f"{name}_gemm_only_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
+                                               "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
         del copies, pw
         torch.cuda.empty_cache()
 

@@ -52,7 +52,10 @@ int forced_plan() { return g_plan.load(std::memory_order_relaxed); }
 
 // Bytes of lm_head argmax keys at the start of its workspace, and where the
 // split-K area starts after them.
-size_t lmhead_keys_bytes(int m, int64_t n) { return (size_t)8 * (size_t)m * (size_t)panels_of(n); }
+size_t lmhead_keys_bytes(int m, int64_t n) {
+  (void)n;
+  return (size_t)8 * (size_t)m * (size_t)kArgmaxSlots;
+}
 size_t lmhead_split_offset(int m, int64_t n) { return (lmhead_keys_bytes(m, n) + 255) / 256 * 256; }
 
 int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, const void* y,
@@ -220,7 +223,7 @@ int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, in
   hipError_t e = launch_gemm(kFmtNvfp4, true, a, l);
   if (e != hipSuccess) return QPN_ERR_LAUNCH;
   return launch_status(
-      launch_argmax_finalize((uint64_t*)workspace, panels_of(n), m, argmax, stream));
+      launch_argmax_finalize((uint64_t*)workspace, m, argmax, stream));
 }
 
 int qpn_debug_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,

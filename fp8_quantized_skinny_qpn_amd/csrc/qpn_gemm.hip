@@ -392,32 +392,26 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
     best = o16 > best ? o16 : best;
     uint64_t o32 = shfl_xor_u64(best, 32);
     best = o32 > best ? o32 : best;
-    if (lane < 16 && mcol < m) keys[(int64_t)mcol * P + p] = best;
+    if (lane < 16 && mcol < m)
+      __hip_atomic_fetch_max(keys + (int64_t)mcol * kArgmaxSlots + (int)(p % kArgmaxSlots), best,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Final argmax: one block per activation row reduces that row's panel keys.
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(uint64_t* __restrict__ keys,
-                                                              int64_t panels,
-                                                              int32_t* __restrict__ argmax) {
-  __shared__ uint64_t part[256];
-  const int mi = blockIdx.x;
-  uint64_t best = 0;
-  for (int64_t i = threadIdx.x; i < panels; i += 256) {
-    uint64_t kv = keys[(int64_t)mi * panels + i];
-    keys[(int64_t)mi * panels + i] = 0;  // leave the workspace all zeros
-    best = kv > best ? kv : best;
+// Final argmax: one wavefront per activation row reduces that row's key
+// slots (and zeroes them).
+__global__ __launch_bounds__(kLanes) void argmax_finalize_kernel(uint64_t* __restrict__ keys,
+                                                                 int32_t* __restrict__ argmax) {
+  static_assert(kArgmaxSlots == kLanes, "one slot per lane");
+  uint64_t* row = keys + (int64_t)blockIdx.x * kArgmaxSlots;
+  uint64_t best = row[threadIdx.x];
+  row[threadIdx.x] = 0;  // leave the workspace all zeros
+#pragma unroll
+  for (int off = kLanes / 2; off > 0; off >>= 1) {
+    const uint64_t o = shfl_xor_u64(best, off);
+    best = o > best ? o : best;
   }
-  part[threadIdx.x] = best;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      uint64_t o = part[threadIdx.x + s];
-      if (o > part[threadIdx.x]) part[threadIdx.x] = o;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) argmax[mi] = (int32_t)(0xFFFFFFFFu - (uint32_t)(part[0] & 0xFFFFFFFFu));
+  if (threadIdx.x == 0) argmax[blockIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
 }
 
 // ---------------------------------------------------------------------------
@@ -626,10 +620,9 @@ hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmL
   return launch_plan<kFmtFp8, false>(a, l);
 }
 
-hipError_t launch_argmax_finalize(uint64_t* keys, int64_t panels, int m, int32_t* argmax,
-                                  void* stream) {
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(m), dim3(256), 0, (hipStream_t)stream, keys,
-                     panels, argmax);
+hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, void* stream) {
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(m), dim3(kLanes), 0, (hipStream_t)stream, keys,
+                     argmax);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ struct GemmArgs {
   int m;
   int64_t n;
   int64_t k;
-  uint64_t* keys;  // lm_head only: [m, panels] argmax keys
+  uint64_t* keys;  // lm_head only: [m, kArgmaxSlots] argmax keys (atomic max)
   void* ws;        // caller workspace (split-K partials and counters), may be NULL
   void* stream;
 };
@@ -67,10 +67,15 @@ constexpr int kGemmNoWorkspace = 2;   // K must be split and the workspace is to
 int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t ws_bytes,
                     size_t ws_offset, GemmLaunch* out);
 
+// Argmax key slots per activation row: panel p folds its key into slot
+// p % kArgmaxSlots with a 64-bit atomic max, so the final pass reads a few
+// keys per row instead of one per panel.
+constexpr int kArgmaxSlots = 64;
+
 // Launch the GEMM (and, with `argmax`, the per-panel argmax keys).
 hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmLaunch& l);
 
-hipError_t launch_argmax_finalize(uint64_t* keys, int64_t panels, int m, int32_t* argmax,
+hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax,
                                   void* stream);
 
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream);

@@ -121,8 +121,8 @@ def test_workspace_sizes(qpn):
         assert qpn.workspace_bytes(op, m, n, k) == _split_ws(qpn.gemm_plan(op, m, n, k))
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 1, 17408, 5120) == 0
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 5120, 17408) > 0   # K is split
-    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 8, 151936, 5120) == 8 * 8 * 9496
-    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 1, 17, 16) == 8 * 2
+    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 8, 151936, 5120) == 8 * 8 * 64
+    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 1, 17, 16) == 8 * 64
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 0, 16, 16) == 0
     big = ctypes.c_size_t(-1).value
     assert qpn.workspace_bytes(99, 1, 16, 16) == big
@@ -173,8 +173,8 @@ def test_lmhead_argument_errors(qpn):
     assert call(n=0) == 2
     assert call(am=A16 + 2) == 3
     assert call(ws=A16 + 4) == 3
-    assert call(wsb=8 * 1 * 1 - 1) == 4                       # workspace too small
-    assert call(m=8, n=160, wsb=8 * 8 * 10 - 8) == 4
+    assert call(wsb=8 * 1 * 64 - 1) == 4                      # workspace too small
+    assert call(m=8, n=160, wsb=8 * 8 * 64 - 8) == 4
     assert call(m=0) == 0
 
 
