@@ -180,35 +180,40 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(const float* __restrict
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const float* __restrict__ w, int64_t n,
                                                        int64_t k, uint8_t* __restrict__ blob) {
   __shared__ float part[256];
-  const int64_t r = blockIdx.x;
   const int64_t J = f8_ksteps_of(k);
-  const bool real = r < n;
-  float a = 0.0f;
-  if (real)
-    for (int64_t i = threadIdx.x; i < k; i += 256) a = fmaxf(a, fabsf(w[r * k + i]));
-  part[threadIdx.x] = a;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) part[threadIdx.x] = fmaxf(part[threadIdx.x], part[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const float s = part[0] / 448.0f;
-  if (threadIdx.x == 0) reinterpret_cast<float*>(blob + kHeaderBytes)[r] = s;
-  const int64_t p = r / kPanelRows;
+  const int64_t rows = panels_of(n) * kPanelRows;
   uint8_t* chunks = blob + f8_codes_offset(n);
-  for (int64_t f = threadIdx.x; f < 4 * J; f += 256) {
-    uint32_t words[4] = {0, 0, 0, 0};
-    if (real && s != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t kk = 16 * f + i;
-        if (kk < k) words[i / 4] |= quant_e4m3(w[r * k + kk] / s) << (8 * (i % 4));
-      }
+  // one block per row, striding over the rows (the grid is capped so that
+  // the launch stays within the work-item limit at n = 2^24)
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const bool real = r < n;
+    float a = 0.0f;
+    if (real)
+      for (int64_t i = threadIdx.x; i < k; i += 256) a = fmaxf(a, fabsf(w[r * k + i]));
+    part[threadIdx.x] = a;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if ((int)threadIdx.x < s) part[threadIdx.x] = fmaxf(part[threadIdx.x], part[threadIdx.x + s]);
+      __syncthreads();
     }
-    const int64_t j = f / 4;
-    const int lane = (int)(r % kPanelRows) + 16 * (int)(f % 4);
-    uint8_t* ch = chunks + chunk_index(p, j, panels_of(n)) * kF8ChunkBytes;
-    *reinterpret_cast<u32x4*>(ch + 16 * lane) = u32x4{words[0], words[1], words[2], words[3]};
+    const float s = part[0] / 448.0f;
+    __syncthreads();  // everyone has read part[0] before the next row reuses it
+    if (threadIdx.x == 0) reinterpret_cast<float*>(blob + kHeaderBytes)[r] = s;
+    const int64_t p = r / kPanelRows;
+    for (int64_t f = threadIdx.x; f < 4 * J; f += 256) {
+      uint32_t words[4] = {0, 0, 0, 0};
+      if (real && s != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t kk = 16 * f + i;
+          if (kk < k) words[i / 4] |= quant_e4m3(w[r * k + kk] / s) << (8 * (i % 4));
+        }
+      }
+      const int64_t j = f / 4;
+      const int lane = (int)(r % kPanelRows) + 16 * (int)(f % 4);
+      uint8_t* ch = chunks + chunk_index(p, j, panels_of(n)) * kF8ChunkBytes;
+      *reinterpret_cast<u32x4*>(ch + 16 * lane) = u32x4{words[0], words[1], words[2], words[3]};
+    }
   }
 }
 
@@ -318,6 +323,9 @@ __global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4* __restri
 
 inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
+// Grid cap for the row-per-block FP8 pack (it strides over the rows).
+constexpr int64_t kMaxPackBlocks = 1 << 16;
+
 }  // namespace
 
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream) {
@@ -343,7 +351,8 @@ hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, v
   hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, blob, kFmtFp8, n, k);
   const int64_t rows = panels_of(n) * kPanelRows;
   if (rows > 0)
-    hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, s, w, n, k, blob);
+    hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)(rows < kMaxPackBlocks ? rows : kMaxPackBlocks)),
+                       dim3(256), 0, s, w, n, k, blob);
   return hipGetLastError();
 }
 

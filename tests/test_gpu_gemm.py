@@ -105,6 +105,31 @@ def test_fp8_full_size_sampled(n, k, ms):
         assert np.isfinite(y).all()
 
 
+MAX_SIZES = [("nvfp4", 48, 1 << 20), ("fp8", 40, 1 << 20), ("nvfp4", 1 << 24, 16), ("fp8", 1 << 24, 8)]
+
+
+@pytest.mark.parametrize("fmt,n,k", MAX_SIZES)
+def test_documented_maximum_sizes(fmt, n, k):
+    """k = 2^20 (the K limit; at M = 8 the activation slice is split over
+    hundreds of K ranges) and n = 2^24 (the N limit: 2^20 panels), sampled
+    rows against the oracle."""
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=5)
+    x8 = synth.activations(8, k, seed=5)
+    pw = qpn.pack_nvfp4(dev(w)) if fmt == "nvfp4" else qpn.pack_fp8(dev(w))
+    rows = _sample_rows(n, 64, seed=1)
+    ref8 = (_oracle_nvfp4_rows if fmt == "nvfp4" else _oracle_fp8_rows)(w, rows, x8)
+    op = qpn.OP_GEMM_NVFP4 if fmt == "nvfp4" else qpn.OP_GEMM_FP8
+    del w
+    for m in (1, 3, 8):
+        pl = qpn.gemm_plan(op, m, n, k)
+        log(f"max size {fmt} {n}x{k} m={m} workgroups={pl.workgroups} splits={pl.splits}")
+        y = qpn.gemm(pw, dev(x8[:m]))
+        yr = host(y[:, torch.from_numpy(rows).cuda()])
+        del y
+        parity(yr, ref8[:m], f"max size {fmt} {n}x{k} m={m}")
+
+
 def test_one_hot_activation_pins_layout():
     qpn = need_gpu()
     n, k = 40, 384
