@@ -60,6 +60,18 @@ EXTRA = [  # measured only with --extra (the other configurations' timings)
     ("layer_gateup_nvfp4_K5120_N34816", 34816, 5120, "nvfp4", (8,)),
 ]
 LMHEAD = ("lmhead_nvfp4_K5120_N151936", 151936, 5120)
+# One decoder layer's four projections at M = 8, back to back: QKV and O in
+# FP8, gate/up and down in NVFP4 (213,368,840 weight bytes per layer).
+LAYER = [("qkv_fp8_K5120_N7168", 7168, 5120, "fp8"), ("o_fp8_K5120_N5120", 5120, 5120, "fp8"),
+         ("gateup_nvfp4_K5120_N34816", 34816, 5120, "nvfp4"),
+         ("down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4")]
+# The same layer's per-rank shards under 4-way tensor parallelism (column-
+# parallel QKV and gate/up split N, row-parallel O and down split K), and the
+# per-rank lm_head vocabulary shard, each on one GPU.
+TP4 = [("tp4_qkv_fp8_K5120_N1792", 1792, 5120, "fp8"), ("tp4_o_fp8_K1280_N5120", 5120, 1280, "fp8"),
+       ("tp4_gateup_nvfp4_K5120_N8704", 8704, 5120, "nvfp4"),
+       ("tp4_down_nvfp4_K4352_N5120", 5120, 4352, "nvfp4")]
+TP4_LMHEAD = ("tp4_lmhead_nvfp4_K5120_N37984", 37984, 5120, "nvfp4")
 
 
 def algo_bytes(n, k, fmt):
@@ -343,6 +355,35 @@ def main():
                                                "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
         del copies, pw
         torch.cuda.empty_cache()
+        # per-rank (TP=4) shard shapes, one call at a time
+        for name, n, k, fmt in TP4 + [TP4_LMHEAD]:
+            log(f"extra: {name}")
+            sh = Shape(qpn, torch, name, n, k, fmt, (1, 8))
+            for m in (1, 8):
+                per = time_call(qpn, torch, sh, m)
+                med = float(np.median(per))
+                extra[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k), "us": round(med * 1e6, 3),
+                                         "GBps": round(sh.bytes / med / 1e9, 1),
+                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
+            del sh
+            torch.cuda.empty_cache()
+        # whole layers at M = 8: the four projections back to back (full and per-rank)
+        for lname, layer in (("layer_M8", LAYER), ("tp4_layer_M8", TP4)):
+            log(f"extra: {lname}")
+            lshapes = [Shape(qpn, torch, name, n, k, fmt, (8,)) for name, n, k, fmt in layer]
+            lbytes = sum(sh.bytes for sh in lshapes)
+            g = capture(torch, lambda: [qpn.gemm(sh.next_copy(), sh.xm[8], out=sh.y[8], ws=sh.ws)
+                                        for _ in range(BATCH // 4) for sh in lshapes])
+            g.replay()
+            torch.cuda.synchronize()
+            per = [t / (BATCH // 4) for t in time_graph(torch, g, 5)]
+            del g
+            med = float(np.median(per))
+            extra[lname] = {"calls": [sh.name for sh in lshapes], "us": round(med * 1e6, 3),
+                            "weight_bytes": lbytes, "GBps": round(lbytes / med / 1e9, 1),
+                            "pct_hbm_peak": round(100 * lbytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
+            del lshapes
+            torch.cuda.empty_cache()
 
     ceiling = read_ceiling(qpn, torch)
 

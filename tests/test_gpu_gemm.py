@@ -73,8 +73,12 @@ def test_nvfp4_2048_square_m1_full():
     parity(y, oracle.gemm_nvfp4(codes, scales, g, x), "2048^2 m=1")
 
 
-FULL_NV = [(17408, 5120, (1, 4, 8)), (5120, 17408, (1, 4, 8)), (34816, 5120, (8,))]
-FULL_F8 = [(6144, 5120, (1, 2, 4)), (5120, 5120, (1, 2, 4, 8)), (7168, 5120, (8,))]
+# decoder shapes, then the per-rank shards under 4-way tensor parallelism
+# (gate/up N/4, down K/4, lm_head vocabulary N/4; QKV N/4, O K/4)
+FULL_NV = [(17408, 5120, (1, 4, 8)), (5120, 17408, (1, 4, 8)), (34816, 5120, (8,)),
+           (8704, 5120, (1, 8)), (5120, 4352, (1, 8)), (37984, 5120, (1, 8))]
+FULL_F8 = [(6144, 5120, (1, 2, 4)), (5120, 5120, (1, 2, 4, 8)), (7168, 5120, (8,)),
+           (1792, 5120, (1, 8)), (5120, 1280, (1, 8))]
 
 
 @pytest.mark.parametrize("n,k,ms", FULL_NV)
