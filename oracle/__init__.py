@@ -247,3 +247,29 @@ def lmhead_nvfp4(codes, scales, g, x):
     """(y_ref FP64 [m, n], argmax int32 [m]) -- argmax of the FP16-rounded y."""
     y = gemm_nvfp4(codes, scales, g, x)
     return y, argmax_f16(round_f16(y))
+
+
+def greedy_verify(argmax, draft):
+    """Greedy speculative verification of one round (taozi.news page: section
+    "自研 QPN 内核" maps a k = 7 verify round onto the M = 8 path; the opening
+    comparison counts tokens committed per round; section
+    "一些工程细节与长上下文发现" has the drafter propose by greedy / local
+    argmax).  Row i of the verified block holds the target's greedy token for
+    position i + 1, and draft[i] is the drafter's token for that position.
+    The pages do not spell out the rule; the plainest reading is the greedy
+    one: accept drafts while each equals the target's token, then commit the
+    target's token at the first position not accepted.
+    Returns (accepted, next_token): accepted = the length of the longest
+    prefix of draft equal to argmax[:len(draft)], next_token =
+    argmax[accepted]; the round commits accepted + 1 tokens."""
+    argmax = [int(a) for a in argmax]
+    draft = [int(d) for d in draft]
+    if len(draft) != len(argmax) - 1:
+        raise ValueError("a round verifies m - 1 drafts with m rows")
+    accepted = 0
+    for proposed, target in zip(draft, argmax):
+        if proposed != target:
+            break
+        accepted += 1
+    return accepted, argmax[accepted]
+

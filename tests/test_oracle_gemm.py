@@ -185,3 +185,44 @@ def test_duplicate_rows_tie_to_lower_index():
     y, am = oracle.lmhead_nvfp4(codes, scales, g, x)
     assert np.array_equal(y[:, dst], y[:, src])
     assert am[0] == min(src, dst)
+
+
+# ---- greedy speculative verification (oracle.greedy_verify) -----------------
+# Worked by hand from the rule: accept drafts while each equals the target's
+# greedy token for its position; the next token is the target's token at the
+# first position not accepted (a bonus token when every draft is accepted).
+VERIFY_CASES = [
+    # argmax (m rows)          drafts (m - 1)        accepted, next
+    ([5, 7, 9, 2], [5, 7, 1], (2, 9)),
+    ([5, 7, 9, 2], [5, 7, 9], (3, 2)),      # all accepted: bonus token
+    ([5, 7, 9, 2], [4, 7, 9], (0, 5)),      # first draft rejected
+    ([5, 7, 9, 2], [5, 1, 9], (1, 7)),      # a later match does not count
+    ([3], [], (0, 3)),                       # M = 1: plain greedy decode
+    ([0, 0, 0, 0, 0, 0, 0, 0], [0] * 7, (7, 0)),
+    ([1, 2, 3, 4, 5, 6, 7, 8], [1, 2, 3, 4, 5, 6, 0], (6, 7)),
+]
+
+
+@pytest.mark.parametrize("argmax,draft,want", VERIFY_CASES)
+def test_greedy_verify_worked_examples(argmax, draft, want):
+    assert oracle.greedy_verify(argmax, draft) == want
+
+
+@given(st.integers(1, 8).flatmap(lambda m: st.tuples(
+    st.lists(st.integers(0, 3), min_size=m, max_size=m),
+    st.lists(st.integers(0, 3), min_size=m - 1, max_size=m - 1))))
+@settings(max_examples=300, deadline=None)
+def test_greedy_verify_prefix_property(case):
+    # characterised without the oracle's loop: the accepted drafts are exactly
+    # a matching prefix, and it cannot be extended
+    argmax, draft = case
+    acc, nxt = oracle.greedy_verify(argmax, draft)
+    assert 0 <= acc <= len(draft)
+    assert draft[:acc] == argmax[:acc]
+    assert acc == len(draft) or draft[acc] != argmax[acc]
+    assert nxt == argmax[acc]
+
+
+def test_greedy_verify_rejects_wrong_draft_count():
+    with pytest.raises(ValueError):
+        oracle.greedy_verify([1, 2], [1, 2])
