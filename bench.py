@@ -353,6 +353,18 @@ def main():
             med = float(np.median(per))
             extra[f"{name}_gemm_only_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
                                                "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
+            # the lm_head of a k = m - 1 draft verify round, acceptance fused
+            if m > 1:
+                draft = torch.zeros((m - 1,), dtype=torch.int32, device="cuda")
+                res = torch.empty((2,), dtype=torch.int32, device="cuda")
+                qpn.lmhead_verify_nvfp4(copies[0], xm, draft, lg, am, res, ws)
+                g = capture(torch, lambda: [qpn.lmhead_verify_nvfp4(copies[i % 3], xm, draft, lg, am, res, ws)
+                                            for i in range(12)])
+                per = [t / 12 for t in time_graph(torch, g, 5)]
+                del g
+                med = float(np.median(per))
+                extra[f"{name}_verify_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
+                                                "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
         del copies, pw
         torch.cuda.empty_cache()
         # per-rank (TP=4) shard shapes, one call at a time

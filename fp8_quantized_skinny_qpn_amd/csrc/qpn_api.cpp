@@ -201,9 +201,11 @@ int qpn_gemm_fp8(const void* packed, const uint16_t* x, uint16_t* y, int m, int6
   return gemm_entry(kFmtFp8, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
 }
 
-int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
-                     int m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+namespace {
+
+int lmhead_common(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
+                  const int32_t* draft, int32_t* result, int m, int64_t n, int64_t k,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (n < 1) return QPN_ERR_SHAPE;
   int rc = gemm_common_checks(kFmtNvfp4, packed, x, logits, m, n, k);
   if (rc != QPN_OK) return rc;
@@ -222,8 +224,28 @@ int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, in
   GemmArgs a{packed, x, logits, m, n, k, (uint64_t*)workspace, workspace, stream};
   hipError_t e = launch_gemm(kFmtNvfp4, true, a, l);
   if (e != hipSuccess) return QPN_ERR_LAUNCH;
-  return launch_status(
-      launch_argmax_finalize((uint64_t*)workspace, m, argmax, stream));
+  return launch_status(launch_argmax_finalize((uint64_t*)workspace, m, argmax, draft, result, stream));
+}
+
+}  // namespace
+
+int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
+                     int m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return lmhead_common(packed, x, logits, argmax, nullptr, nullptr, m, n, k, workspace,
+                       workspace_bytes, stream);
+}
+
+int qpn_lmhead_verify_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits,
+                            int32_t* argmax, const int32_t* draft, int32_t* result, int m,
+                            int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (m > 0) {
+    if (!result || (m > 1 && !draft)) return QPN_ERR_NULL;
+    if (!aligned(result, 4) || (draft && !aligned(draft, 4))) return QPN_ERR_ALIGN;
+  }
+  return lmhead_common(packed, x, logits, argmax, m > 1 ? draft : nullptr, result, m, n, k,
+                       workspace, workspace_bytes, stream);
 }
 
 int qpn_debug_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,

@@ -398,20 +398,41 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   }
 }
 
-// Final argmax: one wavefront per activation row reduces that row's key
-// slots (and zeroes them).
-__global__ __launch_bounds__(kLanes) void argmax_finalize_kernel(uint64_t* __restrict__ keys,
-                                                                 int32_t* __restrict__ argmax) {
+// Final argmax: one workgroup, wavefront r reduces activation row r's key
+// slots (and zeroes them).  With drafts, one thread then checks the round:
+// row i's argmax is the target's token for position i + 1 and draft[i] the
+// drafter's, so the drafts are accepted up to the first mismatch and the
+// next token is the target's at that position (result = {accepted, next}).
+__global__ __launch_bounds__(kLanes * kMaxM) void argmax_finalize_kernel(
+    uint64_t* __restrict__ keys, int m, int32_t* __restrict__ argmax,
+    const int32_t* __restrict__ draft, int32_t* __restrict__ result) {
   static_assert(kArgmaxSlots == kLanes, "one slot per lane");
-  uint64_t* row = keys + (int64_t)blockIdx.x * kArgmaxSlots;
-  uint64_t best = row[threadIdx.x];
-  row[threadIdx.x] = 0;  // leave the workspace all zeros
+  __shared__ int32_t best_index[kMaxM];
+  const int r = threadIdx.x / kLanes;
+  const int lane = threadIdx.x % kLanes;
+  if (r < m) {
+    uint64_t* row = keys + (int64_t)r * kArgmaxSlots;
+    uint64_t best = row[lane];
+    row[lane] = 0;  // leave the workspace all zeros
 #pragma unroll
-  for (int off = kLanes / 2; off > 0; off >>= 1) {
-    const uint64_t o = shfl_xor_u64(best, off);
-    best = o > best ? o : best;
+    for (int off = kLanes / 2; off > 0; off >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, off);
+      best = o > best ? o : best;
+    }
+    if (lane == 0) {
+      const int32_t idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+      argmax[r] = idx;
+      best_index[r] = idx;
+    }
   }
-  if (threadIdx.x == 0) argmax[blockIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+  if (result == nullptr) return;  // uniform over the workgroup
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int accepted = 0;
+    while (accepted < m - 1 && draft[accepted] == best_index[accepted]) ++accepted;
+    result[0] = accepted;
+    result[1] = best_index[accepted];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -620,9 +641,10 @@ hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmL
   return launch_plan<kFmtFp8, false>(a, l);
 }
 
-hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, void* stream) {
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(m), dim3(kLanes), 0, (hipStream_t)stream, keys,
-                     argmax);
+hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const int32_t* draft,
+                                  int32_t* result, void* stream) {
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(kLanes * m), 0, (hipStream_t)stream,
+                     keys, m, argmax, draft, result);
   return hipGetLastError();
 }
 

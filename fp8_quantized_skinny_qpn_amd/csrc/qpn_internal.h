@@ -75,8 +75,11 @@ constexpr int kArgmaxSlots = 64;
 // Launch the GEMM (and, with `argmax`, the per-panel argmax keys).
 hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmLaunch& l);
 
-hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax,
-                                  void* stream);
+// Final argmax of the lm_head; with drafts (m - 1 of them) and result (2
+// ints) also the greedy verification of the round.  draft and result may
+// be NULL together.
+hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const int32_t* draft,
+                                  int32_t* result, void* stream);
 
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream);
 hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, void* stream);

@@ -49,6 +49,7 @@ def _load():
         "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_lmhead_nvfp4": ([vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_lmhead_verify_nvfp4": ([vp, vp, vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_debug_unpack_nvfp4": ([vp, i64, i64, vp, vp, vp, vp], i32),
         "qpn_debug_unpack_fp8": ([vp, i64, i64, vp, vp, vp], i32),
         "qpn_debug_decode_nvfp4": ([vp, vp, i64, vp, vp], i32),
@@ -68,7 +69,8 @@ lib = _load()
 # Symbols the C header declares (the CPU tests check that each one loads).
 EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_fp8_packed_bytes", "qpn_workspace_bytes", "qpn_gemm_plan", "qpn_pack_nvfp4", "qpn_pack_fp8",
-            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_lmhead_nvfp4", "qpn_debug_unpack_nvfp4",
+            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
+            "qpn_debug_unpack_nvfp4",
             "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",
             "qpn_debug_read_ceiling", "qpn_debug_set_plan")
 
@@ -241,6 +243,33 @@ def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, wo
     check(lib.qpn_lmhead_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax), m, pw.n, pw.k,
                                _ptr(ws), ws.numel(), st))
     return logits, argmax
+
+
+def lmhead_verify_nvfp4(pw: PackedWeight, x: torch.Tensor, draft: torch.Tensor, logits=None,
+                        argmax=None, result=None, workspace_=None, stream=None):
+    """(logits, argmax, result int32 [2] = (accepted drafts, next token)) through
+    qpn_lmhead_verify_nvfp4; draft: int32 [m - 1] on the device."""
+    if pw.fmt != FMT_NVFP4:
+        raise ValueError("lm_head needs an NVFP4 blob")
+    _x_check(x, pw.k)
+    m = x.shape[0]
+    if draft.dtype != torch.int32 or draft.dim() != 1 or draft.numel() != max(m - 1, 0):
+        raise ValueError("draft must be int32 [m - 1]")
+    if draft.numel() and (draft.device != x.device or not draft.is_contiguous()):
+        raise ValueError("draft must be contiguous on the activation's device")
+    if logits is None:
+        logits = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+    if argmax is None:
+        argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
+    if result is None:
+        result = torch.empty((2,), dtype=torch.int32, device=x.device)
+    st = _stream(stream)
+    need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k)
+    ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, st.value or 0)
+    check(lib.qpn_lmhead_verify_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax),
+                                      _ptr(draft) if draft.numel() else None, _ptr(result), m,
+                                      pw.n, pw.k, _ptr(ws), ws.numel(), st))
+    return logits, argmax, result
 
 
 def debug_unpack_nvfp4(pw: PackedWeight, stream=None):

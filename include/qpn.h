@@ -183,6 +183,27 @@ QPN_API int qpn_lmhead_nvfp4(const void *packed, const uint16_t *x, uint16_t *lo
                      int32_t *argmax, int m, int64_t n, int64_t k,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* NVFP4 lm_head, fused argmax and greedy verification of one speculative
+ * round (taozi.news section "自研 QPN 内核": M=8 is the verify step of a
+ * round with k=7 drafts; section "一些工程细节与长上下文发现": drafts come
+ * from greedy / local argmax and the round is checked without host
+ * synchronisation).  Row i of x is the input at position i of the round,
+ * so argmax[i] is the target's token after it; draft[i] (i < m - 1) is the
+ * drafter's token at that position.  The greedy acceptance read here:
+ * result[0] = L, the length of the longest prefix with draft[i] ==
+ * argmax[i], and result[1] = argmax[L], the target's token that follows
+ * the accepted drafts (the correction, or the bonus token when all m - 1
+ * are accepted).  logits and argmax as qpn_lmhead_nvfp4; everything stays
+ * on the device, in stream order.  draft: m - 1 int32 device values (may
+ * be NULL when m == 1); result: 2 int32 device values, 4-byte aligned.
+ * Same workspace and failure behaviour as qpn_lmhead_nvfp4; m == 0 writes
+ * nothing.  Two kernels on `stream`. */
+QPN_API int qpn_lmhead_verify_nvfp4(const void *packed, const uint16_t *x,
+                                    uint16_t *logits, int32_t *argmax,
+                                    const int32_t *draft, int32_t *result, int m,
+                                    int64_t n, int64_t k, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /* --- test exports: the device-side layout and decode, for parity checks --- */
 
 /* Canonical export of an NVFP4 blob: codes [n, k/2] (element 2j in the low
@@ -214,7 +235,7 @@ QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
                          uint16_t *out, void *stream);
 
 /* Diagnostic: forces the launch plan (wavefronts per panel, panels per
- * workgroup, prefetch depth; ids 1..8) of every later GEMM and lm_head call
+ * workgroup, prefetch depth; ids 1..10) of every later GEMM and lm_head call
  * in this process, for A/B timing of configurations on identical inputs.
  * 0 restores the automatic choice.  Returns QPN_ERR_SHAPE for an unknown id
  * (nothing changes).  Not for concurrent use with other calls. */

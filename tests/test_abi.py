@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(qpn):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = ctypes.CDLL(qpn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -176,6 +176,25 @@ def test_lmhead_argument_errors(qpn):
     assert call(wsb=8 * 1 * 64 - 1) == 4                      # workspace too small
     assert call(m=8, n=160, wsb=8 * 8 * 64 - 8) == 4
     assert call(m=0) == 0
+
+
+def test_lmhead_verify_argument_errors(qpn):
+    L = qpn.lib
+    v = ctypes.c_void_p
+
+    def call(dr=A16, res=A16, m=2, n=16, k=16, am=A16, ws=A16, wsb=8 * 8 * 64):
+        return L.qpn_lmhead_verify_nvfp4(v(A256), v(A16), v(A16), v(am), v(dr), v(res), m, n, k,
+                                         v(ws), wsb, None)
+
+    assert call(res=0) == 1                                   # result is required
+    assert call(dr=0) == 1                                    # drafts are required for m >= 2
+    assert call(res=A16 + 2) == 3
+    assert call(dr=A16 + 1) == 3
+    assert call(am=0) == 1                                    # the lm_head's own checks follow
+    assert call(n=0) == 2
+    assert call(wsb=8 * 2 * 64 - 1) == 4
+    assert call(m=0, dr=0, res=0) == 0                        # nothing to do
+    assert call(m=9) == 2
 
 
 def test_pack_argument_errors(qpn):

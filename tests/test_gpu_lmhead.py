@@ -183,3 +183,69 @@ def test_lmhead_leaves_workspace_zeroed():
             if first is None:
                 first = host(am)
             assert np.array_equal(host(am), first)
+
+
+@pytest.mark.parametrize("n,k", [(4099, 1024), (151936, 5120)])
+def test_lmhead_verify_every_accept_length(n, k):
+    """Fused greedy verification: for each accepted length L of a k = m - 1
+    draft round, (accepted, next token) equals the oracle's greedy_verify of
+    the same argmax, with the logits and argmax as the plain lm_head's.  The
+    m calls go back to back on one stream with a single synchronisation."""
+    qpn = need_gpu()
+    log(f"lmhead verify {n}x{k}: drawing weights")
+    w = synth.weights(n, k, seed=n + 1)
+    x = synth.activations(8, k, seed=n + 1)
+    pw = qpn.pack_nvfp4(dev(w))
+    for m in (1, 2, 8):
+        lg0, am0 = qpn.lmhead_nvfp4(pw, dev(x[:m]))
+        am0 = host(am0)
+        drafts = []
+        for L in range(m):
+            d = am0[:m - 1].copy()
+            if L < m - 1:
+                d[L] = (d[L] + 1 + L) % n      # first mismatch at L
+            drafts.append(d)
+        log(f"lmhead verify {n}x{k} m={m}")
+        outs = [qpn.lmhead_verify_nvfp4(pw, dev(x[:m]), dev(d)) for d in drafts]
+        torch.cuda.synchronize()
+        for L, (d, (lg, am, res)) in enumerate(zip(drafts, outs)):
+            assert np.array_equal(host(lg).view(np.uint16), host(lg0).view(np.uint16))
+            assert np.array_equal(host(am), am0)
+            assert tuple(int(v) for v in host(res)) == oracle.greedy_verify(am0, d) == \
+                (L, int(am0[L])), f"m={m} L={L}"
+    # the argmax these rounds were judged on, against the oracle
+    if n * k <= 4099 * 1024:
+        codes, scales, g = oracle.pack_nvfp4(w)
+        y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
+        lg, am, res = qpn.lmhead_verify_nvfp4(pw, dev(x), dev(np.zeros(7, np.int32)))
+        parity(host(lg), y_ref, f"lmhead verify {n}x{k}")
+        _check_argmax(host(am), host(lg), y_ref, f"lmhead verify {n}x{k}")
+        assert tuple(int(v) for v in host(res)) == oracle.greedy_verify(host(am), np.zeros(7, np.int32))
+
+
+def test_lmhead_verify_against_oracle_drafts():
+    """Drafts built from the oracle's own argmax (so the expected acceptance
+    is fixed by the oracle alone) on rows whose top two logits are far apart."""
+    qpn = need_gpu()
+    n, k = 2048, 256
+    # one-hot rows: x row i selects weight row t_i, so logit t_i dominates
+    targets = np.array([17, 900, 5, 2047, 1024, 33, 600, 1500])
+    w = np.zeros((n, k), np.float32)
+    w[:, :] = synth.weights(n, k, seed=3) * 0.01
+    for i, t in enumerate(targets):
+        w[t, i * 16:(i + 1) * 16] = 4.0
+    x = np.zeros((8, k), np.float16)
+    for i in range(8):
+        x[i, i * 16:(i + 1) * 16] = 1.0
+    codes, scales, g = oracle.pack_nvfp4(w)
+    y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
+    am_ref = oracle.argmax_f16(oracle.round_f16(y_ref))
+    assert np.array_equal(am_ref, targets)
+    pw = qpn.pack_nvfp4(dev(w))
+    for L in range(8):
+        d = am_ref[:7].astype(np.int32).copy()
+        if L < 7:
+            d[L] = 0
+        lg, am, res = qpn.lmhead_verify_nvfp4(pw, dev(x), dev(d))
+        assert np.array_equal(host(am), am_ref)
+        assert tuple(int(v) for v in host(res)) == oracle.greedy_verify(am_ref, d) == (L, int(am_ref[L]))
