@@ -184,6 +184,21 @@ def dequant_fp8(codes, row_scale):
     return out
 
 
+def requant_fp8_to_nvfp4(codes, row_scale):
+    """FP8 -> NVFP4 conversion of one weight (taozi.news page, section
+    "v1.1 的关键改进": before FP8 regions had their own path they were turned
+    into NVFP4, serving a derived checkpoint; aiwitness.kr page, section
+    "내가 실제로 만든 것", same account).  The pages do not give the recipe;
+    the plainest reading: decode each FP8 weight to its value E4M3(code) * s_r
+    (exact in FP64, then one rounding to FP32, the precision the pack works
+    in), and quantise that tensor with the NVFP4 recipe used for the FP4
+    regions.  Codes must not be the NaN codes.  Returns (codes, scales, g)."""
+    w = dequant_fp8(codes, row_scale)
+    if not np.all(np.isfinite(w)):
+        raise ValueError("FP8 NaN code in the weight")
+    return pack_nvfp4(w.astype(np.float32))
+
+
 def _x_bits(x):
     x = np.asarray(x)
     if x.dtype == np.float16:

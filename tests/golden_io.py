@@ -22,8 +22,9 @@ def value_code_table(name):
 
 
 def worked_example(name):
-    """Dict with per-row 'w', 'codes', 'scales' / 'scale' and optional 'g'."""
-    out = {"w": {}, "codes": {}, "scales": {}, "scale": {}}
+    """Dict with per-row 'w', 'fp8' (input E4M3 codes), 'codes', 'scales' /
+    'scale' and optional 'g'."""
+    out = {"w": {}, "codes": {}, "scales": {}, "scale": {}, "fp8": {}}
     for tok in _lines(name):
         key = tok[0]
         if key == "g":
@@ -34,6 +35,8 @@ def worked_example(name):
             out["codes"][int(tok[1])] = [int(v, 16) for v in tok[2:]]
         elif key == "scales":
             out["scales"][int(tok[1])] = [int(v, 16) for v in tok[2:]]
+        elif key == "fp8":
+            out["fp8"][int(tok[1])] = [int(v, 16) for v in tok[2:]]
         elif key == "scale":
             out["scale"][int(tok[1])] = float(tok[2])
     return out

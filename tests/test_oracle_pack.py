@@ -6,6 +6,7 @@ subnormal block scale; invariants that hold for any input pin the rest.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from fp8_quantized_skinny_qpn_amd import synth
@@ -134,3 +135,48 @@ def test_synth_chunks_equal_one_shot():
     assert np.array_equal(synth.weight_rows(50, 48, rows, seed=2, rows_per_chunk=7), w[rows])
     x8 = synth.activations(8, 48, seed=2)
     assert np.array_equal(synth.activations(3, 48, seed=2), x8[:3])
+
+
+def test_requant_worked_example():
+    ex = worked_example("requant_worked_example.txt")
+    c8 = np.array([ex["fp8"][r] for r in range(2)], np.uint8)
+    rs = np.array([ex["scale"][r] for r in range(2)], np.float32)
+    codes, scales, g = oracle.requant_fp8_to_nvfp4(c8, rs)
+    assert float(g) == ex["g"]
+    for r in range(2):
+        assert list(scales[r]) == ex["scales"][r], r
+        assert _nib(codes[r]) == ex["codes"][r], r
+
+
+def test_requant_error_bound():
+    # Against the FP8 weight it converts: every block scale is the E4M3
+    # rounding of (block amax / 6) / g, so d = S*g is within 2^-4 (relative,
+    # normal scales) or 2^-10 g (subnormal scales) of amax / 6, and every
+    # element is within half an E2M1 step of d (saturation above 6 only after
+    # a scale rounded down).  Rows get scales spread over 2^-12 .. 2^4.
+    w = synth.weights(24, 96, seed=29) * (2.0 ** np.arange(-12, 12, dtype=np.float32))[:, None] ** 0.5
+    c8, rs = oracle.pack_fp8(w.astype(np.float32))
+    # the FP8 values from torch's own float8_e4m3fn decode, not the oracle's
+    v = torch.from_numpy(c8).view(torch.float8_e4m3fn).to(torch.float64).numpy() * \
+        rs.astype(np.float64)[:, None]
+    codes, scales, g = oracle.requant_fp8_to_nvfp4(c8, rs)
+    wh = oracle.dequant_nvfp4(codes, scales, g)
+    g = float(g)
+    for r in range(24):
+        for b in range(6):
+            blk = v[r, 16 * b:16 * (b + 1)]
+            a = float(np.max(np.abs(blk)))
+            S = oracle.ue4m3_value(int(scales[r, b]))
+            d = float(np.float32(np.float32(S) * np.float32(g)))
+            assert abs(d - a / 6) <= (a / 6) * 2.0 ** -4 + g * 2.0 ** -10 + 1e-6 * d, (r, b)
+            for i in range(16):
+                t = abs(blk[i]) / d
+                hs = 0.25 if t < 2 else (0.5 if t < 4 else 1.0)
+                assert abs(blk[i] - wh[r, 16 * b + i]) <= d * hs * (1 + 1e-6) + 1e-30, (r, b, i)
+
+
+def test_requant_rejects_nan_codes():
+    c8 = np.zeros((1, 16), np.uint8)
+    c8[0, 3] = 0x7F
+    with pytest.raises(ValueError):
+        oracle.requant_fp8_to_nvfp4(c8, np.ones(1, np.float32))
