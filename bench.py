@@ -65,6 +65,10 @@ LMHEAD = ("lmhead_nvfp4_K5120_N151936", 151936, 5120)
 LAYER = [("qkv_fp8_K5120_N7168", 7168, 5120, "fp8"), ("o_fp8_K5120_N5120", 5120, 5120, "fp8"),
          ("gateup_nvfp4_K5120_N34816", 34816, 5120, "nvfp4"),
          ("down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4")]
+# The same layer with its FP8 projections converted to NVFP4 (all-FP4, the
+# derived-checkpoint variant: 0.5625 instead of 1 byte per QKV/O weight).
+LAYER_ALLFP4 = [("qkv_fp8>nvfp4_K5120_N7168", 7168, 5120, "fp8>nvfp4"),
+                ("o_fp8>nvfp4_K5120_N5120", 5120, 5120, "fp8>nvfp4")] + LAYER[2:]
 # The same layer's per-rank shards under 4-way tensor parallelism (column-
 # parallel QKV and gate/up split N, row-parallel O and down split K), and the
 # per-rank lm_head vocabulary shard, each on one GPU.
@@ -98,7 +102,11 @@ class Shape:
         from fp8_quantized_skinny_qpn_amd import synth
         self.name, self.n, self.k, self.fmt, self.ms = name, n, k, fmt, ms
         w = torch.from_numpy(synth.weights(n, k, seed=seed)).cuda()
-        pw = qpn.pack_nvfp4(w) if fmt == "nvfp4" else qpn.pack_fp8(w)
+        if fmt == "fp8>nvfp4":  # FP8 weights converted to NVFP4 (the derived checkpoint)
+            pw = qpn.requant_fp8_to_nvfp4(qpn.pack_fp8(w))
+            fmt = self.fmt = "nvfp4"
+        else:
+            pw = qpn.pack_nvfp4(w) if fmt == "nvfp4" else qpn.pack_fp8(w)
         del w
         self.copies = [pw] + [pw.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / pw.nbytes)) - 1)]
         self.x = torch.from_numpy(synth.activations(8, k, seed=seed)).cuda()
@@ -380,7 +388,8 @@ def main():
             del sh
             torch.cuda.empty_cache()
         # whole layers at M = 8: the four projections back to back (full and per-rank)
-        for lname, layer in (("layer_M8", LAYER), ("tp4_layer_M8", TP4)):
+        for lname, layer in (("layer_M8", LAYER), ("layer_allfp4_M8", LAYER_ALLFP4),
+                             ("tp4_layer_M8", TP4)):
             log(f"extra: {lname}")
             lshapes = [Shape(qpn, torch, name, n, k, fmt, (8,)) for name, n, k, fmt in layer]
             lbytes = sum(sh.bytes for sh in lshapes)

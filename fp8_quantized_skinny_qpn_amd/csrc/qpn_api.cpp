@@ -191,6 +191,19 @@ int qpn_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, size_t pack
   return launch_status(launch_pack_fp8(w, n, k, packed, stream));
 }
 
+int qpn_requant_fp8_to_nvfp4(const void* fp8_packed, size_t fp8_bytes, int64_t n, int64_t k,
+                             void* nvfp4_packed, size_t nvfp4_bytes, void* stream) {
+  if (!nv_shape_ok(n, k) || !f8_shape_ok(n, k)) return QPN_ERR_SHAPE;
+  if (!fp8_packed || !nvfp4_packed) return QPN_ERR_NULL;
+  if (!aligned(fp8_packed, 256) || !aligned(nvfp4_packed, 256)) return QPN_ERR_ALIGN;
+  if (fp8_bytes < f8_blob_bytes(n, k) || nvfp4_bytes < nv_blob_bytes(n, k)) return QPN_ERR_BUFFER;
+  const uintptr_t a = (uintptr_t)fp8_packed, b = (uintptr_t)nvfp4_packed;
+  if (a < b + nv_blob_bytes(n, k) && b < a + f8_blob_bytes(n, k)) return QPN_ERR_BUFFER;  // overlap
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  return launch_status(launch_requant_fp8_to_nvfp4(fp8_packed, n, k, nvfp4_packed, stream));
+}
+
 int qpn_gemm_nvfp4(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
                    int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_entry(kFmtNvfp4, packed, x, y, m, n, k, workspace, workspace_bytes, stream);

@@ -83,6 +83,8 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream);
 hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, void* stream);
+hipError_t launch_requant_fp8_to_nvfp4(const void* fp8, int64_t n, int64_t k, void* packed,
+                                       void* stream);
 
 hipError_t launch_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,
                                uint8_t* scales, float* g, void* stream);

@@ -1,6 +1,6 @@
 // qpn_pack.hip -- NVFP4 and FP8 pack kernels (FP32 -> codes + scales in the
-// packed layout of qpn_common.h) and the canonical-export / decode kernels
-// used by the parity tests.
+// packed layout of qpn_common.h), the FP8 -> NVFP4 conversion of a packed
+// weight, and the canonical-export / decode kernels used by the parity tests.
 //
 // Quantisation is "pure round" (lcz.me page, quantisation option table,
 // NVFP4-NVIDIA row): round to nearest, ties to the even code, saturating at
@@ -59,13 +59,23 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (mnt << 20));
 }
 
-__global__ void header_kernel(uint8_t* blob, uint32_t fmt, int64_t n, int64_t k) {
+// With `source` (an FP8 blob being converted) the new header is marked
+// invalid (magic 0) unless the source's header describes an FP8 [n, k]
+// weight of this layout version; GEMMs then write NaN for the blob.
+__global__ void header_kernel(uint8_t* blob, uint32_t fmt, int64_t n, int64_t k,
+                              const uint8_t* source) {
   // 64 threads zero the 256-byte header, then thread 0 fills the fields
   reinterpret_cast<uint32_t*>(blob)[threadIdx.x] = 0;
   __syncthreads();
   if (threadIdx.x != 0) return;
   BlobHeader* h = reinterpret_cast<BlobHeader*>(blob);
-  h->magic = kMagic;
+  bool ok = true;
+  if (source != nullptr) {
+    const BlobHeader* sh = reinterpret_cast<const BlobHeader*>(source);
+    ok = sh->magic == kMagic && sh->format == kFmtFp8 && sh->layout_version == kLayoutVersion &&
+         sh->n == n && sh->k == k;
+  }
+  h->magic = ok ? kMagic : 0u;
   h->format = fmt;
   h->layout_version = kLayoutVersion;
   h->n = n;
@@ -115,9 +125,79 @@ __global__ __launch_bounds__(256) void amax_kernel(const float* __restrict__ w, 
   if (threadIdx.x == 0) atomicMax(amax_bits, part[0]);
 }
 
+// Where the NVFP4 pack reads its weights: 16 consecutive K elements of one
+// row (k0 % 16 == 0, k0 < k) as FP32 values.
+struct F32Weights {
+  const float* __restrict__ w;
+  int64_t k;
+  __device__ __forceinline__ void load16(int64_t r, int64_t k0, float v[16]) const {
+    const float4* src = reinterpret_cast<const float4*>(w + r * k + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = src[q];
+      v[4 * q + 0] = t.x;
+      v[4 * q + 1] = t.y;
+      v[4 * q + 2] = t.z;
+      v[4 * q + 3] = t.w;
+    }
+  }
+};
+
+// An FP8 blob as the source of an FP8 -> NVFP4 conversion: the 16 codes are
+// one 16-byte lane slot of a chunk, each decoded as E4M3(code) * s_r (one
+// FP32 multiply, the exact product rounded once).  NaN codes never occur in
+// blobs written by the FP8 pack.
+struct Fp8BlobWeights {
+  const uint8_t* __restrict__ blob;
+  int64_t n;
+  __device__ __forceinline__ void load16(int64_t r, int64_t k0, float v[16]) const {
+    const float s = reinterpret_cast<const float*>(blob + kHeaderBytes)[r];
+    const int64_t f = k0 / 16;
+    const int lane = (int)(r % kPanelRows) + 16 * (int)(f % 4);
+    const uint8_t* ch = blob + f8_codes_offset(n) +
+                        chunk_index(r / kPanelRows, f / 4, panels_of(n)) * kF8ChunkBytes;
+    const u32x4 c = *reinterpret_cast<const u32x4*>(ch + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t code = (c[i / 4] >> (8 * (i % 4))) & 0xFFu;
+      const float mag = e4m3_to_f32(code & 0x7Fu);
+      v[i] = ((code & 0x80u) ? -mag : mag) * s;
+    }
+  }
+};
+
+// max |w| over the n x k weights of a source, one 16-element block per
+// thread-iteration; merged as in amax_kernel.
+template <class Src>
+__global__ __launch_bounds__(256) void amax_blocks_kernel(Src src, int64_t n, int64_t k,
+                                                          uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t part[256];
+  uint32_t best = 0;
+  const int64_t per_row = k / 16;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n * per_row;
+       i += (int64_t)gridDim.x * 256) {
+    float v[16];
+    src.load16(i / per_row, 16 * (i % per_row), v);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t a = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+      best = best > a ? best : a;
+    }
+  }
+  part[threadIdx.x] = best;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s && part[threadIdx.x + s] > part[threadIdx.x])
+      part[threadIdx.x] = part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicMax(amax_bits, part[0]);
+}
+
 // One thread per 32-code fragment (row r, fragment f of 32 K elements).
-__global__ __launch_bounds__(256) void pack_nvfp4_kernel(const float* __restrict__ w, int64_t n,
-                                                         int64_t k, uint8_t* __restrict__ blob) {
+template <class Src>
+__global__ __launch_bounds__(256) void pack_nvfp4_kernel(Src src, int64_t n, int64_t k,
+                                                         uint8_t* __restrict__ blob) {
   BlobHeader* hdr = reinterpret_cast<BlobHeader*>(blob);
   const int64_t P = panels_of(n);
   const int64_t J = nv_ksteps_of(k);
@@ -137,16 +217,8 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(const float* __restrict
   for (int b = 0; b < 2; ++b) {
     const int64_t k0 = 32 * f + 16 * b;
     if (r >= n || k0 >= k) continue;  // padding block: zero scale, zero codes
-    const float4* src = reinterpret_cast<const float4*>(w + r * k + k0);
     float v[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float4 t = src[q];
-      v[4 * q + 0] = t.x;
-      v[4 * q + 1] = t.y;
-      v[4 * q + 2] = t.z;
-      v[4 * q + 3] = t.w;
-    }
+    src.load16(r, k0, v);
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fabsf(v[i]) > a ? fabsf(v[i]) : a;
@@ -331,7 +403,7 @@ constexpr int64_t kMaxPackBlocks = 1 << 16;
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   uint8_t* blob = (uint8_t*)packed;
-  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, blob, kFmtNvfp4, n, k);
+  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, blob, kFmtNvfp4, n, k, nullptr);
   const int64_t count = n * k;
   if (count > 0) {
     int64_t blocks = (count / 4 + 255) / 256;
@@ -341,14 +413,36 @@ hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed,
   }
   const int64_t frags = panels_of(n) * kPanelRows * 4 * nv_ksteps_of(k);
   if (frags > 0)
-    hipLaunchKernelGGL(pack_nvfp4_kernel, dim3(blocks_for(frags)), dim3(256), 0, s, w, n, k, blob);
+    hipLaunchKernelGGL(pack_nvfp4_kernel<F32Weights>, dim3(blocks_for(frags)), dim3(256), 0, s,
+                       F32Weights{w, k}, n, k, blob);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_fp8_to_nvfp4(const void* fp8, int64_t n, int64_t k, void* packed,
+                                       void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* blob = (uint8_t*)packed;
+  const uint8_t* src = (const uint8_t*)fp8;
+  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, blob, kFmtNvfp4, n, k, src);
+  const Fp8BlobWeights w{src, n};
+  const int64_t units = n * (k / 16);
+  if (units > 0) {
+    int64_t blocks = (units + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(amax_blocks_kernel<Fp8BlobWeights>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       w, n, k, &reinterpret_cast<BlobHeader*>(blob)->amax_bits);
+  }
+  const int64_t frags = panels_of(n) * kPanelRows * 4 * nv_ksteps_of(k);
+  if (frags > 0)
+    hipLaunchKernelGGL(pack_nvfp4_kernel<Fp8BlobWeights>, dim3(blocks_for(frags)), dim3(256), 0, s,
+                       w, n, k, blob);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   uint8_t* blob = (uint8_t*)packed;
-  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, blob, kFmtFp8, n, k);
+  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, blob, kFmtFp8, n, k, nullptr);
   const int64_t rows = panels_of(n) * kPanelRows;
   if (rows > 0)
     hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)(rows < kMaxPackBlocks ? rows : kMaxPackBlocks)),

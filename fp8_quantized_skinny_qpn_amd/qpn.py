@@ -46,6 +46,7 @@ def _load():
         "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
         "qpn_pack_nvfp4": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_pack_fp8": ([vp, i64, i64, vp, sz, vp], i32),
+        "qpn_requant_fp8_to_nvfp4": ([vp, sz, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_lmhead_nvfp4": ([vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
@@ -69,6 +70,7 @@ lib = _load()
 # Symbols the C header declares (the CPU tests check that each one loads).
 EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_fp8_packed_bytes", "qpn_workspace_bytes", "qpn_gemm_plan", "qpn_pack_nvfp4", "qpn_pack_fp8",
+            "qpn_requant_fp8_to_nvfp4",
             "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
             "qpn_debug_unpack_nvfp4",
             "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",
@@ -198,6 +200,19 @@ def pack_fp8(w: torch.Tensor, stream=None) -> PackedWeight:
     blob = torch.empty(nb, dtype=torch.uint8, device=w.device)
     check(lib.qpn_pack_fp8(_ptr(w), n, k, _ptr(blob), nb, _stream(stream)))
     return PackedWeight(blob, n, k, FMT_FP8)
+
+
+def requant_fp8_to_nvfp4(pw: PackedWeight, stream=None) -> PackedWeight:
+    """The NVFP4 blob converted from an FP8 blob through qpn_requant_fp8_to_nvfp4."""
+    if pw.fmt != FMT_FP8:
+        raise ValueError("the source must be an FP8 blob")
+    nb = nvfp4_packed_bytes(pw.n, pw.k)
+    if nb == 0:
+        raise QpnError(2, status_string(2))
+    blob = torch.empty(nb, dtype=torch.uint8, device=pw.blob.device)
+    check(lib.qpn_requant_fp8_to_nvfp4(_ptr(pw.blob), pw.nbytes, pw.n, pw.k, _ptr(blob), nb,
+                                       _stream(stream)))
+    return PackedWeight(blob, pw.n, pw.k, FMT_NVFP4)
 
 
 def _x_check(x, k):

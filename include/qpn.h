@@ -150,6 +150,22 @@ QPN_API int qpn_pack_nvfp4(const float *w, int64_t n, int64_t k, void *packed,
 QPN_API int qpn_pack_fp8(const float *w, int64_t n, int64_t k, void *packed,
                  size_t packed_bytes, void *stream);
 
+/* FP8 -> NVFP4 conversion of a packed weight: the derived-checkpoint variant
+ * (taozi.news section "v1.1 的关键改进" and aiwitness.kr section
+ * "내가 실제로 만든 것": before FP8 regions had an execution path of their
+ * own, they were converted to NVFP4).  Every weight is decoded to its FP8
+ * value E4M3(code) * s_n (the exact product rounded once to FP32) and that
+ * FP32 tensor is packed exactly as qpn_pack_nvfp4 packs its input.
+ * fp8_packed: a blob from qpn_pack_fp8 for this (n, k), fp8_bytes >=
+ * qpn_fp8_packed_bytes(n, k); nvfp4_packed: output, nvfp4_bytes >=
+ * qpn_nvfp4_packed_bytes(n, k).  Both device, 256-byte aligned, not
+ * overlapping (QPN_ERR_BUFFER otherwise).  k % 16 == 0.  If the source
+ * header does not describe an FP8 [n, k] weight the output is marked
+ * invalid and GEMMs on it write NaN.  Three kernels on `stream`. */
+QPN_API int qpn_requant_fp8_to_nvfp4(const void *fp8_packed, size_t fp8_bytes, int64_t n,
+                                     int64_t k, void *nvfp4_packed, size_t nvfp4_bytes,
+                                     void *stream);
+
 /* QPN NVFP4 skinny GEMM (taozi.news section "自研 QPN 内核", the NVFP4 path
  * at M=1 and M=8; aiwitness.kr section "내가 실제로 만든 것").
  * Y[m, n] = FP16_RNE( sum_k X[m, k] * What[n, k] ), What = E2M1 * UE4M3 * g,

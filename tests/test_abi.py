@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(qpn):
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = ctypes.CDLL(qpn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -195,6 +195,26 @@ def test_lmhead_verify_argument_errors(qpn):
     assert call(wsb=8 * 2 * 64 - 1) == 4
     assert call(m=0, dr=0, res=0) == 0                        # nothing to do
     assert call(m=9) == 2
+
+
+def test_requant_argument_errors(qpn):
+    L = qpn.lib
+    v = ctypes.c_void_p
+    n8, n4 = qpn.fp8_packed_bytes(32, 64), qpn.nvfp4_packed_bytes(32, 64)
+    far = A256 + (1 << 20)
+
+    def call(src=A256, sb=n8, n=32, k=64, dst=far, db=n4):
+        return L.qpn_requant_fp8_to_nvfp4(v(src), sb, n, k, v(dst), db, None)
+
+    assert call(src=0) == 1
+    assert call(dst=0) == 1
+    assert call(k=40) == 2                                    # NVFP4 needs k % 16 == 0
+    assert call(n=-1) == 2
+    assert call(src=A256 + 16) == 3
+    assert call(dst=far + 128) == 3
+    assert call(sb=n8 - 1) == 4
+    assert call(db=n4 - 1) == 4
+    assert call(dst=A256 + 256) == 4                          # overlapping blobs
 
 
 def test_pack_argument_errors(qpn):
