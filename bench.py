@@ -27,6 +27,7 @@ computing one complete headline step (all six calls, every row), repeated
 until about ten seconds of CPU time have been spent.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
+    python bench.py --traffic-workload | --contraction-ab   (profiling workloads)
 """
 import argparse
 import hashlib
@@ -250,6 +251,38 @@ def traffic_workload(qpn, torch):
         torch.cuda.empty_cache()
 
 
+# The contraction A/B: plans 1 and 2 (MFMA) against plans 12 and 11, the same
+# launch shapes contracting with VALU dot products instead.
+CONTRACTION_AB = ((1, 1, 12), (8, 2, 11))  # (M, MFMA plan, VALU-dot plan)
+
+
+def contraction_ab(qpn, torch):
+    """Headline shapes at M = 1 and 8 through the MFMA plan and its VALU-dot
+    twin: six launches each (for the PMC passes), then the time of each in
+    back-to-back graphs.  Prints one JSON line."""
+    rows = []
+    try:
+        for name, n, k, fmt in HEADLINE:
+            s = Shape(qpn, torch, name, n, k, fmt, (1, 8))
+            for m, p_mfma, p_vdot in CONTRACTION_AB:
+                for plan in (p_mfma, p_vdot):
+                    qpn.debug_set_plan(plan)
+                    for _ in range(6):
+                        qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws)
+                    torch.cuda.synchronize()
+                    med = float(np.median(time_call(qpn, torch, s, m)))
+                    kname = qpn.kernel_name(fmt, m, n, k)
+                    log(f"{name} M={m} plan {plan}: {med * 1e6:.2f} us  {kname}")
+                    rows.append({"call": f"{name}_M{m}", "plan": plan, "kernel": kname,
+                                 "contraction": "valu_dot" if plan == p_vdot else "mfma",
+                                 "us": round(med * 1e6, 3), "GBps": round(s.bytes / med / 1e9, 1)})
+            del s
+            torch.cuda.empty_cache()
+    finally:
+        qpn.debug_set_plan(0)
+    print(json.dumps({"contraction_ab": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +292,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
+    ap.add_argument("--contraction-ab", action="store_true",
+                    help="only time the headline calls with MFMA and with VALU-dot contraction")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -274,6 +309,9 @@ def main():
     from fp8_quantized_skinny_qpn_amd import qpn  # fails loudly when libqpn.so is missing
     if args.traffic_workload:
         traffic_workload(qpn, torch)
+        return
+    if args.contraction_ab:
+        contraction_ab(qpn, torch)
         return
 
     log("setting up headline shapes")

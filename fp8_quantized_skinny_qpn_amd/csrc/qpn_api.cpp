@@ -139,7 +139,7 @@ size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
 
 int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
                   int* panels_per_workgroup, int* prefetch_depth, int* splits,
-                  int* activation_rows, int64_t* split_workgroups) {
+                  int* activation_rows, int64_t* split_workgroups, int* valu_dot) {
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
   uint32_t fmt;
   switch (op) {
@@ -166,6 +166,7 @@ int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int*
   if (splits) *splits = l.splits;
   if (activation_rows) *activation_rows = gemm_activation_rows(m);
   if (split_workgroups) *split_workgroups = l.split_wgs;
+  if (valu_dot) *valu_dot = l.valu_dot;
   return QPN_OK;
 }
 

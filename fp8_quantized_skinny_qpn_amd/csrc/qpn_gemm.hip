@@ -9,7 +9,9 @@
 // 16x16x32 MFMA (the other columns are discarded).  At 2M flops per weight
 // the MFMA runs at a few percent of its peak: the kernel is bound by HBM, and
 // the MFMA is used because it does the K-reduction across lanes for free and
-// leaves the VALU to the decode.
+// leaves the VALU to the decode.  (A VALU dot-product contraction of the same
+// launch shapes, kept as diagnostic plans, measures 2x slower at M = 8 and
+// about 15% slower at M = 1 on MI355X.)
 //
 // Work split.  A workgroup owns G consecutive 16-row panels and one of S
 // contiguous K ranges ("splits") of them.  Each panel is worked on by W
@@ -127,7 +129,10 @@ struct SplitArgs {
   int full_panels;       // workgroups from split_wgs on take panels [0, full_panels) whole
 };
 
-template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX>
+// VDOT selects the contraction: false = the 16x16x32 MFMA; true = VALU dot
+// products (v_dot2_f32_f16 per activation row on the decoded weight pairs),
+// compiled only as a diagnostic plan to compare the two on identical work.
+template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX, bool VDOT>
 __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
     const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     int m, int64_t n, int64_t k, SplitArgs sp, uint64_t* __restrict__ keys) {
@@ -276,17 +281,41 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   const uint8_t* xlane = smem + ((w * GR * 4 + kg) * MB + xrow) * 16;
   constexpr int XC = W * GR * 4 * MB * 16;  // LDS bytes per interleave round
 
+  // VALU-dot contraction: lane (row, kg) keeps one FP32 sum per activation
+  // row over its own K positions, reading all MB rows' units of its K group
+  float vacc[MB];
+#pragma unroll
+  for (int mm = 0; mm < MB; ++mm) vacc[mm] = 0.f;
+  const uint8_t* xkg = smem + ((w * GR * 4 + kg) * MB) * 16;
+
   auto compute = [&](int c, const WFrag& f) {
     half8 a[GR];
     if constexpr (FMT == kFmtNvfp4)
       decode_nvfp4_fragment(f.codes, (uint32_t)f.scales, a);
     else
       decode_fp8_fragment(f.codes, a);
-    const uint8_t* xs = xlane + c * XC;
+    if constexpr (VDOT) {
+      const uint8_t* xs = xkg + c * XC;
 #pragma unroll
-    for (int t = 0; t < GR; ++t) {
-      const half8 b = *reinterpret_cast<const half8*>(xs + t * 4 * MB * 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc, 0, 0, 0);
+      for (int t = 0; t < GR; ++t) {
+#pragma unroll
+        for (int mm = 0; mm < MB; ++mm) {
+          const half8 b = *reinterpret_cast<const half8*>(xs + (t * 4 * MB + mm) * 16);
+          float sacc = vacc[mm];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc = __builtin_amdgcn_fdot2(half2v{a[t][2 * e], a[t][2 * e + 1]},
+                                          half2v{b[2 * e], b[2 * e + 1]}, sacc, false);
+          vacc[mm] = sacc;
+        }
+      }
+    } else {
+      const uint8_t* xs = xlane + c * XC;
+#pragma unroll
+      for (int t = 0; t < GR; ++t) {
+        const half8 b = *reinterpret_cast<const half8*>(xs + t * 4 * MB * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc, 0, 0, 0);
+      }
     }
   };
 
@@ -304,6 +333,26 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
     }
     c0 += R;
   } while (c0 < nc_pad);
+
+  if constexpr (VDOT) {
+    // sum the four K groups of each row (fixed order), then move the sums
+    // into the MFMA tile layout: lane L holds rows 4 (L >> 4) + v of
+    // activation row L & 15
+#pragma unroll
+    for (int mm = 0; mm < MB; ++mm) {
+      vacc[mm] += __shfl_xor(vacc[mm], 16, 64);
+      vacc[mm] += __shfl_xor(vacc[mm], 32, 64);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int src = 4 * (lane >> 4) + v;
+#pragma unroll
+      for (int mm = 0; mm < MB; ++mm) {
+        const float t = __shfl(vacc[mm], src, 64);
+        if ((lane & 15) == mm) acc[v] = t;
+      }
+    }
+  }
 
   // ---- 4. fixed-order sum of the W partial tiles of each panel ----
   wait_vmcnt<0>();  // surplus (size-zero) loads retired before the wavefront ends
@@ -448,7 +497,7 @@ int x_step_bytes(uint32_t fmt, int m) {
 // LDS activation budget per workgroup: two workgroups fit in the 160 KiB of a CU.
 constexpr int kSliceBudget = 80 * 1024;
 
-template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX>
+template <uint32_t FMT, int W, int G, int D, int MB, bool ARGMAX, bool VDOT>
 hipError_t launch_t(const GemmArgs& a, const GemmLaunch& l) {
   const int xbytes = ((l.slice_steps * (Fmt<FMT>::kKStep / 8) * MB + 63) / 64) * 1024;
   const int red = G * W * kLanes * 16;
@@ -458,24 +507,26 @@ hipError_t launch_t(const GemmArgs& a, const GemmLaunch& l) {
     sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
     sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
   }
-  hipLaunchKernelGGL((skinny_gemm_kernel<FMT, W, G, D, MB, ARGMAX>),
+  hipLaunchKernelGGL((skinny_gemm_kernel<FMT, W, G, D, MB, ARGMAX, VDOT>),
                      dim3((unsigned)l.workgroups), dim3(kLanes * G * W), lds,
                      (hipStream_t)a.stream, (const uint8_t*)a.packed, a.x, a.y, a.m, a.n, a.k, sp,
                      a.keys);
   return hipGetLastError();
 }
 
-template <uint32_t FMT, int W, int G, int D, bool ARGMAX>
+template <uint32_t FMT, int W, int G, int D, bool ARGMAX, bool VDOT = false>
 hipError_t launch_mb(const GemmArgs& a, const GemmLaunch& l) {
   switch (gemm_activation_rows(a.m)) {
-    case 1: return launch_t<FMT, W, G, D, 1, ARGMAX>(a, l);
-    case 2: return launch_t<FMT, W, G, D, 2, ARGMAX>(a, l);
-    case 4: return launch_t<FMT, W, G, D, 4, ARGMAX>(a, l);
-    default: return launch_t<FMT, W, G, D, 8, ARGMAX>(a, l);
+    case 1: return launch_t<FMT, W, G, D, 1, ARGMAX, VDOT>(a, l);
+    case 2: return launch_t<FMT, W, G, D, 2, ARGMAX, VDOT>(a, l);
+    case 4: return launch_t<FMT, W, G, D, 4, ARGMAX, VDOT>(a, l);
+    default: return launch_t<FMT, W, G, D, 8, ARGMAX, VDOT>(a, l);
   }
 }
 
-// The compiled plans: (W, G, D, placement, workgroups wanted).
+// The compiled plans: (W, G, D, placement, workgroups wanted, contraction).
+// Plans 11 and 12 repeat plans 2 and 1 with the VALU-dot contraction; the
+// automatic choice never uses them.
 constexpr GemmPlan kPlans[] = {
     {0, 0, 0, 0, 0},          // 0: automatic
     {4, 1, 4, 0, 256},        // 1
@@ -488,6 +539,8 @@ constexpr GemmPlan kPlans[] = {
     {3, 5, 14, 0, 256},       // 8
     {4, 4, 10, 0, 256},       // 9
     {3, 4, 4, 2, 256},        // 10
+    {3, 5, 4, 0, 256, 1},     // 11: plan 2, VALU dot
+    {4, 1, 4, 0, 256, 1},     // 12: plan 1, VALU dot
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -504,6 +557,8 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
     case 8: return launch_mb<FMT, 3, 5, 14, ARGMAX>(a, l);
     case 9: return launch_mb<FMT, 4, 4, 10, ARGMAX>(a, l);
     case 10: return launch_mb<FMT, 3, 4, 4, ARGMAX>(a, l);
+    case 11: return launch_mb<FMT, 3, 5, 4, ARGMAX, true>(a, l);
+    case 12: return launch_mb<FMT, 4, 1, 4, ARGMAX, true>(a, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -592,6 +647,7 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
         out->waves_per_panel = pl.waves_per_panel;
         out->panels_per_workgroup = pl.panels_per_workgroup;
         out->depth = pl.depth;
+        out->valu_dot = pl.valu_dot;
         out->groups = gs;
         out->splits = (int)s0;
         out->split_steps = (int)st0;
@@ -621,6 +677,7 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   out->waves_per_panel = pl.waves_per_panel;
   out->panels_per_workgroup = pl.panels_per_workgroup;
   out->depth = pl.depth;
+  out->valu_dot = pl.valu_dot;
   out->groups = groups;
   out->splits = (int)S;
   out->split_steps = (int)steps;

@@ -30,6 +30,7 @@ struct GemmPlan {
   int depth;
   int placement;
   int min_workgroups;  // workgroups wanted per launch
+  int valu_dot;        // 1: VALU dot products instead of MFMA (diagnostic plans)
 };
 
 // Everything one launch needs: the plan plus its K split and workspace use.
@@ -38,6 +39,7 @@ struct GemmLaunch {
   int waves_per_panel;
   int panels_per_workgroup;
   int depth;
+  int valu_dot;
   int64_t groups;       // panel groups of the split segment
   int splits;           // K ranges per split-segment group
   int split_steps;      // k-steps per K range

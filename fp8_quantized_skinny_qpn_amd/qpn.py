@@ -43,7 +43,7 @@ def _load():
         "qpn_nvfp4_packed_bytes": ([i64, i64], sz),
         "qpn_fp8_packed_bytes": ([i64, i64], sz),
         "qpn_workspace_bytes": ([i32, i32, i64, i64], sz),
-        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
+        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "qpn_pack_nvfp4": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_pack_fp8": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_requant_fp8_to_nvfp4": ([vp, sz, i64, i64, vp, sz, vp], i32),
@@ -118,6 +118,7 @@ class Plan:
     splits: int
     activation_rows: int
     split_workgroups: int   # workgroups on K ranges; the rest take whole panels
+    valu_dot: int = 0       # 1: VALU dot products instead of MFMA (diagnostic plans)
 
     @property
     def waves_per_workgroup(self) -> int:
@@ -130,9 +131,10 @@ def gemm_plan(op: int, m: int, n: int, k: int) -> Plan:
     wg = ctypes.c_int64()
     swg = ctypes.c_int64()
     outs = [ctypes.c_int() for _ in range(5)]
+    vd = ctypes.c_int()
     check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *[ctypes.byref(o) for o in outs],
-                            ctypes.byref(swg)))
-    return Plan(wg.value, *[o.value for o in outs], swg.value)
+                            ctypes.byref(swg), ctypes.byref(vd)))
+    return Plan(wg.value, *[o.value for o in outs], swg.value, vd.value)
 
 
 def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:
@@ -141,7 +143,8 @@ def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:
     pl = gemm_plan(op, m, n, k)
     f = 1 if fmt == FMT_NVFP4 else 2
     return (f"qpn::skinny_gemm_kernel<{f}u, {pl.waves_per_panel}, {pl.panels_per_workgroup}, "
-            f"{pl.prefetch_depth}, {pl.activation_rows}, {'true' if lmhead else 'false'}>")
+            f"{pl.prefetch_depth}, {pl.activation_rows}, {'true' if lmhead else 'false'}, "
+            f"{'true' if pl.valu_dot else 'false'}>")
 
 
 # Zero-initialised workspaces, one per (device, stream): the library leaves a

@@ -121,14 +121,16 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * split_workgroups, the workgroups that work on K ranges (split_workgroups
  * / splits panel groups of the last panels, dispatched first).  The other
  * workgroups - 0 unless the plan balances whole panels per CU - each take
- * panels_per_workgroup whole panels.  A pure function of the shape (and of
+ * panels_per_workgroup whole panels.  valu_dot is 1 for the diagnostic
+ * plans that contract with VALU dot products instead of the MFMA (only when
+ * forced with qpn_debug_set_plan).  A pure function of the shape (and of
  * a plan forced with qpn_debug_set_plan), independent of any declared
  * maximum.  Any output pointer may be NULL.  Returns QPN_OK or
  * QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
                           int *waves_per_panel, int *panels_per_workgroup,
                           int *prefetch_depth, int *splits, int *activation_rows,
-                          int64_t *split_workgroups);
+                          int64_t *split_workgroups, int *valu_dot);
 
 /* NVFP4 pack ("pure round" quantisation, lcz.me quantisation-option table,
  * NVFP4-NVIDIA row; format per the lcz.me NVFP4 support table).
@@ -251,7 +253,8 @@ QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
                          uint16_t *out, void *stream);
 
 /* Diagnostic: forces the launch plan (wavefronts per panel, panels per
- * workgroup, prefetch depth; ids 1..10) of every later GEMM and lm_head call
+ * workgroup, prefetch depth, contraction; ids 1..12, where 11 and 12 repeat
+ * 2 and 1 with VALU dot products in place of the MFMA) of every later GEMM and lm_head call
  * in this process, for A/B timing of configurations on identical inputs.
  * 0 restores the automatic choice.  Returns QPN_ERR_SHAPE for an unknown id
  * (nothing changes).  Not for concurrent use with other calls. */

@@ -2,6 +2,7 @@
 declares, and its host-side size queries and argument checks behave as
 include/qpn.h documents.  No kernel is launched by any test here."""
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -90,10 +91,23 @@ def test_gemm_plan(qpn):
         if op != 3:
             assert (ws == 0) == (pl.splits == 1)
         name = qpn.kernel_name(qpn.FMT_NVFP4 if op != 2 else qpn.FMT_FP8, m, n, k, lmhead=op == 3)
-        assert name.startswith("qpn::skinny_gemm_kernel<") and name.endswith(">")
+        assert name.startswith("qpn::skinny_gemm_kernel<") and name.endswith(", false>")
+        assert pl.valu_dot == 0                               # automatic plans use the MFMA
     # 320 panels on 256 CUs: 256 whole panels plus the last 64 split four ways
     pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)
     assert (pl.workgroups, pl.split_workgroups, pl.splits) == (512, 256, 4)
+    # the VALU-dot diagnostic plans repeat plans 2 and 1 with the other contraction
+    try:
+        for vd, base in ((11, 2), (12, 1)):
+            qpn.debug_set_plan(base)
+            a = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
+            qpn.debug_set_plan(vd)
+            b = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
+            assert (a.valu_dot, b.valu_dot) == (0, 1)
+            assert dataclasses.replace(a, valu_dot=1) == b
+            assert qpn.kernel_name(qpn.FMT_NVFP4, 8, 17408, 5120).endswith("false, true>")
+    finally:
+        qpn.debug_set_plan(0)
     # K = 2^20 at M = 8 cannot be staged whole: it is split
     assert qpn.gemm_plan(1, 8, 64, 1 << 20).splits > 1
     with pytest.raises(qpn.QpnError):
