@@ -77,6 +77,11 @@ TP4 = [("tp4_qkv_fp8_K5120_N1792", 1792, 5120, "fp8"), ("tp4_o_fp8_K1280_N5120",
        ("tp4_gateup_nvfp4_K5120_N8704", 8704, 5120, "nvfp4"),
        ("tp4_down_nvfp4_K4352_N5120", 5120, 4352, "nvfp4")]
 TP4_LMHEAD = ("tp4_lmhead_nvfp4_K5120_N37984", 37984, 5120, "nvfp4")
+# Prefill-sized activation blocks through the tiled MFMA kernel.
+PREFILL = [("prefill_gate_up_nvfp4_K5120_N17408", 17408, 5120, "nvfp4", (16, 64, 128, 256)),
+           ("prefill_down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4", (16, 64, 128, 256)),
+           ("prefill_fp8_K5120_N6144", 6144, 5120, "fp8", (64, 256))]
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix peak
 
 
 def algo_bytes(n, k, fmt):
@@ -116,7 +121,7 @@ class Shape:
         self.bytes = algo_bytes(n, k, fmt)
         op = qpn.OP_GEMM_NVFP4 if fmt == "nvfp4" else qpn.OP_GEMM_FP8
         # split-K workspace, zero-filled once (the library keeps it zeroed)
-        self.ws = torch.zeros(max(256, max(qpn.workspace_bytes(op, m, n, k) for m in ms)),
+        self.ws = torch.zeros(max(256, max((qpn.workspace_bytes(op, m, n, k) for m in ms), default=0)),
                               dtype=torch.uint8, device="cuda")
         self.i = 0
 
@@ -424,6 +429,31 @@ def main():
                                          "GBps": round(sh.bytes / med / 1e9, 1),
                                          "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
             del sh
+            torch.cuda.empty_cache()
+        # prefill-sized blocks: time, matrix-unit rate and weight rate
+        for name, n, k, fmt, ms in PREFILL:
+            log(f"extra: {name}")
+            sh = Shape(qpn, torch, name, n, k, fmt, ())
+            xs = torch.from_numpy(synth.activations(256, k, seed=0, m_max=256)).cuda()
+            op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+            ws = torch.zeros(max(256, max(qpn.workspace_bytes(op, m, n, k) for m in ms)),
+                             dtype=torch.uint8, device="cuda")
+            for m in ms:
+                xm = xs[:m].contiguous()
+                ym = torch.empty((m, n), dtype=torch.float16, device="cuda")
+                qpn.prefill(sh.next_copy(), xm, out=ym, ws=ws)
+                g = capture(torch, lambda: [qpn.prefill(sh.next_copy(), xm, out=ym, ws=ws) for _ in range(16)])
+                per = [t / 16 for t in time_graph(torch, g, 5)]
+                del g
+                med = float(np.median(per))
+                tf = 2.0 * m * n * k / med / 1e12
+                pl = qpn.gemm_plan(op, m, n, k)
+                extra[f"{name}_M{m}"] = {"us": round(med * 1e6, 3), "TFLOPs": round(tf, 1),
+                                         "pct_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
+                                         "GBps": round(sh.bytes / med / 1e9, 1),
+                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1),
+                                         "workgroups": pl.workgroups, "splits": pl.splits}
+            del sh, xs, ws
             torch.cuda.empty_cache()
         # whole layers at M = 8: the four projections back to back (full and per-rank)
         for lname, layer in (("layer_M8", LAYER), ("layer_allfp4_M8", LAYER_ALLFP4),

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqpn.so")
 
-SOURCES = ["qpn_api.cpp", "qpn_gemm.hip", "qpn_pack.hip"]
+SOURCES = ["qpn_api.cpp", "qpn_gemm.hip", "qpn_pack.hip", "qpn_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -113,6 +113,15 @@ size_t qpn_fp8_packed_bytes(int64_t n, int64_t k) {
 }
 
 size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
+  if (op == QPN_OP_PREFILL_NVFP4 || op == QPN_OP_PREFILL_FP8) {
+    const uint32_t fmt = op == QPN_OP_PREFILL_NVFP4 ? kFmtNvfp4 : kFmtFp8;
+    if (m < 0 || m > kMaxPrefillM) return (size_t)-1;
+    if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return (size_t)-1;
+    if (m == 0 || n == 0) return 0;
+    PrefillLaunch l;
+    if (prefill_launch_for(fmt, m, n, k, (size_t)-1, &l) != kGemmLaunchOk) return (size_t)-1;
+    return l.ws_needed;
+  }
   if (m < 0 || m > kMaxM) return (size_t)-1;
   uint32_t fmt;
   switch (op) {
@@ -140,6 +149,23 @@ size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
 int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
                   int* panels_per_workgroup, int* prefetch_depth, int* splits,
                   int* activation_rows, int64_t* split_workgroups, int* valu_dot) {
+  if (op == QPN_OP_PREFILL_NVFP4 || op == QPN_OP_PREFILL_FP8) {
+    const uint32_t fmt = op == QPN_OP_PREFILL_NVFP4 ? kFmtNvfp4 : kFmtFp8;
+    if (m < 0 || m > kMaxPrefillM) return QPN_ERR_SHAPE;
+    if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
+    PrefillLaunch l;
+    if (prefill_launch_for(fmt, m > 0 ? m : 1, n, k, (size_t)-1, &l) != kGemmLaunchOk)
+      return QPN_ERR_SHAPE;
+    if (workgroups) *workgroups = l.workgroups;
+    if (waves_per_panel) *waves_per_panel = 2;  // two wavefronts, one per half of the rows
+    if (panels_per_workgroup) *panels_per_workgroup = 8;
+    if (prefetch_depth) *prefetch_depth = l.depth;
+    if (splits) *splits = l.splits;
+    if (activation_rows) *activation_rows = 32 * l.mt;
+    if (split_workgroups) *split_workgroups = l.workgroups;
+    if (valu_dot) *valu_dot = 0;
+    return QPN_OK;
+  }
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
   uint32_t fmt;
   switch (op) {
@@ -217,6 +243,23 @@ int qpn_gemm_fp8(const void* packed, const uint16_t* x, uint16_t* y, int m, int6
 
 namespace {
 
+int prefill_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y, int m,
+                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || m > kMaxPrefillM) return QPN_ERR_SHAPE;
+  if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
+  if (m == 0 || n == 0) return QPN_OK;
+  if (!packed || (!x && k > 0) || !y) return QPN_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 2)) return QPN_ERR_ALIGN;
+  if (workspace && !aligned(workspace, 16)) return QPN_ERR_ALIGN;
+  int rc = device_check();
+  if (rc != QPN_OK) return rc;
+  PrefillLaunch l;
+  if (prefill_launch_for(fmt, m, n, k, workspace ? workspace_bytes : 0, &l) != kGemmLaunchOk)
+    return QPN_ERR_BUFFER;
+  GemmArgs a{packed, x, y, m, n, k, nullptr, workspace, stream};
+  return launch_status(launch_prefill(fmt, a, l));
+}
+
 int lmhead_common(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
                   const int32_t* draft, int32_t* result, int m, int64_t n, int64_t k,
                   void* workspace, size_t workspace_bytes, void* stream) {
@@ -242,6 +285,16 @@ int lmhead_common(const void* packed, const uint16_t* x, uint16_t* logits, int32
 }
 
 }  // namespace
+
+int qpn_gemm_prefill_nvfp4(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
+                           int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_entry(kFmtNvfp4, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+}
+
+int qpn_gemm_prefill_fp8(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
+                         int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_entry(kFmtFp8, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+}
 
 int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
                      int m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,

@@ -83,6 +83,26 @@ hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmL
 hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const int32_t* draft,
                                   int32_t* result, void* stream);
 
+// Prefill-sized activation blocks (9 <= m <= 256): one launch of the tiled
+// MFMA kernel, 128 output channels by 32 mt activation rows per workgroup.
+constexpr int kMaxPrefillM = 256;
+struct PrefillLaunch {
+  int mt;               // 16-row activation tiles per wavefront (workgroup rows = 32 mt)
+  int depth;            // k-steps of weight loads in flight per wavefront
+  int64_t blocks;       // 128-channel blocks
+  int splits;           // K ranges per block
+  int split_steps;      // k-steps per K range
+  int64_t workgroups;   // blocks * splits
+  size_t ws_counters_offset;
+  size_t ws_partial_offset;
+  size_t ws_needed;
+};
+int prefill_tiles(int m);
+// A pure function of its arguments; fewer K splits when ws_bytes is short.
+int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
+                       PrefillLaunch* out);
+hipError_t launch_prefill(uint32_t fmt, const GemmArgs& a, const PrefillLaunch& l);
+
 hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, void* packed, void* stream);
 hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, void* packed, void* stream);
 hipError_t launch_requant_fp8_to_nvfp4(const void* fp8, int64_t n, int64_t k, void* packed,

@@ -1,0 +1,461 @@
+// qpn_prefill.hip -- the same compressed weights against prefill-sized
+// activation blocks (M = 9 .. 256 rows) on gfx950.
+//
+// Y[m, n] = FP16( scale * sum_k X[m, k] * Wq[n, k] ), FP32 accumulation, the
+// weights read from the packed blob and decoded in registers exactly as in
+// the skinny kernel.  The pages run prefill on FP16 tensor-core tiles and
+// name it as the phase where the old card falls furthest behind (lcz.me
+// page, "strata" section; aiwitness.kr page, questions section); here it
+// is the f16 MFMA with the activation block filling whole 16-column tiles.
+// At 2M flops per weight the work turns from HBM-bound (M below ~90 on
+// MI355X) to matrix-unit-bound.
+//
+// Work split.  A workgroup of four wavefronts owns 8 consecutive 16-row
+// panels (128 output channels) and all BM = 32 MT activation rows, over one
+// K range ("split").  Wavefront (wn, wm) decodes panels 4 wn .. 4 wn + 3 and
+// multiplies them against activation tiles MT wm .. MT wm + MT - 1, so each
+// decoded weight fragment feeds MT MFMAs and each activation fragment read
+// from LDS feeds 4.
+//
+// Pipeline per k-step c (static wait counts; loads of a wavefront complete
+// in order):
+//   wait until this wavefront's loads for step c are in; barrier (everyone's
+//   activation slice for c is in LDS, and everyone is done reading the
+//   buffer the next slice goes to);
+//   send the activation slice of step c + 1 to the other LDS buffer
+//   (direct-to-LDS loads) and the weights of step c + D to the register
+//   ring;
+//   decode step c's weights, MFMAs against the slice in LDS.
+// The two slices live in two separate LDS arrays and the loop is unrolled
+// by two, so the compiler sees that the reads of one never alias the
+// direct-to-LDS writes of the other and keeps the waits exact.
+//
+// Split-K (S > 1) combines FP32 partial tiles exactly as the skinny kernel
+// does: device-scope write-through partial stores, an arrival counter per
+// panel block, and the last arriver summing the S partials in split order
+// (deterministic) and clearing them.
+#include <algorithm>
+
+#include "qpn_common.h"
+#include "qpn_internal.h"
+
+namespace qpn {
+
+namespace {
+
+template <uint32_t FMT>
+struct PFmt;
+template <>
+struct PFmt<kFmtNvfp4> {
+  static constexpr int kKStep = kNvKStep;
+  static constexpr int kChunk = kNvChunkBytes;
+  static constexpr int kGroups = 4;
+};
+template <>
+struct PFmt<kFmtFp8> {
+  static constexpr int kKStep = kF8KStep;
+  static constexpr int kChunk = kF8ChunkBytes;
+  static constexpr int kGroups = 2;
+};
+
+constexpr int kRsrc = 0x00020000;  // raw dword access
+constexpr int kPanelsPerBlock = 8;  // 128 output channels per workgroup
+constexpr int kWaves = 4;
+
+template <int N>
+__device__ __forceinline__ void pf_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void pf_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct PFrag {
+  u32x4 codes;
+  uint16_t scales;
+};
+
+// Slice buffer `I` of a kernel instantiation: one LDS object per stage, so
+// the compiler can tell the reads of one stage from the direct-to-LDS
+// writes of another and keeps its waits exact.
+template <int I, int BYTES>
+__device__ __forceinline__ uint8_t* slice_stage() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[BYTES];
+  return buf;
+}
+
+}  // namespace
+
+struct PrefillSplit {
+  int splits;
+  int split_steps;
+  float* partial;      // [S][blocks][4 MT tiles][256 threads] float4 partials
+  uint32_t* counters;  // [blocks] arrivals; zero between calls
+};
+
+// D: k-steps of weights in flight (ring R = D + 1); NS: activation slice
+// stages in LDS (2, or R when they fit), the slice being sent NS - 1 steps ahead.
+template <uint32_t FMT, int MT, int D, int NS>
+__global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
+    const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    int m, int64_t n, int64_t k, PrefillSplit sp) {
+  using F = PFmt<FMT>;
+  constexpr int KS = F::kKStep;
+  constexpr int GR = F::kGroups;
+  constexpr int MTW = 2 * MT;                        // 16-row activation tiles per workgroup
+  constexpr int STAGE = GR * MTW * 1024;             // LDS bytes of one step's slice
+  constexpr int XQ = GR * MTW / kWaves;              // slice loads per wavefront per step
+  constexpr int LPS = FMT == kFmtNvfp4 ? 2 : 1;      // weight loads per chunk
+  constexpr int WL = 4 * LPS;                        // weight loads per wavefront per step
+  constexpr int R = D + 1;
+  constexpr int AX = NS - 1;  // slice distance
+  // Step c needs slice c and weights c.  Both went out in step c - AX when
+  // AX == D (weights second), else the weights went earlier; younger loads
+  // are then the AX - 1 whole steps after that (plus, when AX < D, the
+  // weights sent together with slice c).
+  constexpr int WAITN = (AX < D ? WL : 0) + (AX - 1) * (XQ + WL);
+  static_assert(AX >= 1 && AX <= D, "weights go at least as far ahead as slices");
+  static_assert(R % NS == 0, "stages repeat within one ring cycle");
+  static_assert(WAITN < 64, "vmcnt range");
+  static_assert(XQ * kWaves == GR * MTW, "slice loads split evenly");
+  auto stage = [](int c) -> uint8_t* {
+    switch (c % NS) {
+      case 0: return slice_stage<0, STAGE>();
+      case 1: return slice_stage<1, STAGE>();
+      case 2: if constexpr (NS > 2) return slice_stage<2, STAGE>(); else return nullptr;
+      case 3: if constexpr (NS > 3) return slice_stage<3, STAGE>(); else return nullptr;
+      case 4: if constexpr (NS > 4) return slice_stage<4, STAGE>(); else return nullptr;
+      default: if constexpr (NS > 5) return slice_stage<5, STAGE>(); else return nullptr;
+    }
+  };
+  static_assert(NS <= 6, "stage objects");
+
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+  const int wn = wv & 1, wm = wv >> 1;
+  const int S = sp.splits;
+  const int64_t blk = blockIdx.x / S;
+  const int split = blockIdx.x % S;
+  const int64_t P = panels_of(n);
+  const int J = (int)((k + KS - 1) / KS);
+  const int j0 = split * sp.split_steps;
+  const int nj = max(0, min(J - j0, sp.split_steps));
+  const int64_t pbase = blk * kPanelsPerBlock + 4 * wn;  // first of this wavefront's 4 panels
+
+  // ---- header (and FP8 row scales): used in the epilogue ----
+  const __amdgpu_buffer_rsrc_t hres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, kHeaderBytes, kRsrc);
+  const u32x4 hd0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, 0, 0, 0));
+  const u32x4 hd1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, 16, 0, 0));
+  const uint32_t hd2 = __builtin_amdgcn_raw_buffer_load_b32(hres, 48, 0, 0);
+  float4v row_scale[4] = {};
+  if constexpr (FMT == kFmtFp8) {
+    // the padded scale area holds 16 P floats; panels past P read zeros
+    const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + kHeaderBytes), (short)0, (int)(P * kPanelRows * 4), kRsrc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
+      const int off = pbase + i < P ? (int)(r0 * 4) : 0x7FFFFFF0;
+      row_scale[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0));
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  // ---- weights: chunk (p, j) at codes + (j P + p) * chunk bytes ----
+  const uint8_t* codes = blob + (FMT == kFmtNvfp4 ? (uint64_t)kHeaderBytes : f8_codes_offset(n));
+  const uint64_t sstride = (uint64_t)P * F::kChunk;
+  auto issue_w = [&](int c, PFrag (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // the address is formed unconditionally (no access happens through a
+      // descriptor of size zero), so the load itself never sits behind a branch
+      const bool ok = c < nj && pbase + i < P;
+      const uint8_t* ch = codes + (uint64_t)(j0 + c) * sstride + (uint64_t)(pbase + i) * F::kChunk;
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)ch, (short)0, ok ? F::kChunk : 0, kRsrc);
+      f[i].codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 2));
+      if constexpr (FMT == kFmtNvfp4)
+        f[i].scales = __builtin_amdgcn_raw_buffer_load_b16(r, kNvCodeBytes + 2 * lane, 0, 0);
+    }
+  };
+
+  // ---- activation slice of step c -> LDS: load q = t * MTW + tile fills
+  // 1 KiB; lane (kg, col) takes X[16 tile + col][K .. K + 8), K = (j0 + c) KS
+  // + kg KS / 4 + 8 t.  Rows >= m and K >= k read zeros. ----
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrc);
+  const int col = lane & 15, kg = lane >> 4;
+  auto issue_x = [&](int c, uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < XQ; ++i) {
+      const int q = wv + kWaves * i;
+      const int t = q / MTW, tile = q % MTW;
+      const int row = tile * 16 + col;
+      const int64_t kpos = (int64_t)(j0 + c) * KS + kg * (KS / 4) + 8 * t;
+      const bool ok = c < nj && row < m && kpos < k;
+      const int off = ok ? (int)(((int64_t)row * k + kpos) * 2) : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  float4v acc[4][MT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  PFrag ring[R][4];
+  // prologue: what steps -D .. -1 would have sent (slice s + AX when it is
+  // >= 0, weights s + D), in the same order, so that the wait count at the
+  // top of every step is the same.  The scheduler may not move loads across
+  // these points.
+#pragma unroll
+  for (int sidx = -D; sidx < 0; ++sidx) {
+    if (sidx + AX >= 0) issue_x(sidx + AX, stage(sidx + AX));
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(sidx + D, ring[sidx + D]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  auto step = [&](int c, const uint8_t* xread, uint8_t* xnext, PFrag (&cur)[4], PFrag (&ahead)[4]) {
+    // everything up to this step's slice is in, then everyone's slice is
+    // (and everyone is done reading the stage the next slice goes to)
+    pf_wait_vmcnt<WAITN>();
+    pf_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(c + AX, xnext);
+    __builtin_amdgcn_sched_barrier(0);  // all of the slice before any of the weights
+    issue_w(c + D, ahead);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c >= nj) return;  // padding step: loads only (no memory access)
+    half8 a[4][GR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (FMT == kFmtNvfp4)
+        decode_nvfp4_fragment(cur[i].codes, (uint32_t)cur[i].scales, a[i]);
+      else
+        decode_fp8_fragment(cur[i].codes, a[i]);
+    }
+    const uint8_t* xs = xread + (wm * MT) * 1024 + lane * 16;
+    // the activation fragments of group t + 1 are read while group t's
+    // MFMAs run
+    half8 b[2][MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) b[0][mt] = *reinterpret_cast<const half8*>(xs + mt * 1024);
+#pragma unroll
+    for (int t = 0; t < GR; ++t) {
+      if (t + 1 < GR) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          b[(t + 1) & 1][mt] = *reinterpret_cast<const half8*>(xs + ((t + 1) * MTW + mt) * 1024);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i][t], b[t & 1][mt], acc[i][mt], 0, 0, 0);
+    }
+  };
+
+  // unrolled by the ring length (a multiple of the stage count, so stages
+  // and ring slots are static) over a whole number of ring cycles; steps
+  // past nj only issue size-zero loads, so every wait count is static
+  const int nj_pad = ((nj + R - 1) / R) * R;
+  for (int c0 = 0; c0 < nj_pad; c0 += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      step(c0 + i, stage(i), stage(i + AX), ring[i], ring[(i + D) % R]);
+  }
+  pf_wait_vmcnt<0>();  // size-zero surplus loads retired
+
+  // ---- header check ----
+  const uint32_t h_magic = __builtin_amdgcn_readfirstlane(hd0[0]);
+  const uint32_t h_format = __builtin_amdgcn_readfirstlane(hd0[1]);
+  const uint32_t h_version = __builtin_amdgcn_readfirstlane(hd0[2]);
+  const int64_t h_n = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
+                                __builtin_amdgcn_readfirstlane(hd1[0]));
+  const int64_t h_k = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[3]) << 32) |
+                                __builtin_amdgcn_readfirstlane(hd1[2]));
+  const float h_scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(hd2));
+  const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
+                     h_n == n && h_k == k;
+
+  // ---- split-K ----
+  if (S > 1) {
+    constexpr int kDevScope = 16;  // sc1: write-through stores, coherent loads
+    const int64_t blocks = gridDim.x / S;
+    const int64_t per_split = blocks * (kLanes * kWaves) * (4 * MT) * 16;
+    const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sp.partial, (short)0, (int)(S * per_split), kRsrc);
+    // tile u of this thread at blk * 4 MT * 4 KiB + u * 4 KiB + 16 tid (each
+    // store instruction of the workgroup writes 4 KiB contiguously)
+    const int mine = (int)((blk * (4 * MT) * (kLanes * kWaves) + threadIdx.x) * 16);
+    constexpr int kTile = kLanes * kWaves * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
+                                               (int)(split * per_split) + mine + (i * MT + t) * kTile,
+                                               0, kDevScope);
+    pf_wait_vmcnt<0>();
+    pf_barrier();
+    __shared__ uint32_t arrived;
+    if (threadIdx.x == 0) {
+      const uint32_t before =
+          __hip_atomic_fetch_add(sp.counters + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (before == (uint32_t)(S - 1))
+        __hip_atomic_store(sp.counters + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      arrived = before;
+    }
+    __syncthreads();
+    if (arrived != (uint32_t)(S - 1)) return;  // uniform over the workgroup
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        float4v s = {0.f, 0.f, 0.f, 0.f};
+        for (int sx = 0; sx < S; ++sx)
+          s += __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                               pres, (int)(sx * per_split) + mine + (i * MT + t) * kTile,
+                                               0, kDevScope));
+        acc[i][t] = s;
+      }
+    // the only reader clears the partials (the workspace ends all zeros)
+    for (int sx = 0; sx < S; ++sx)
+#pragma unroll
+      for (int i = 0; i < 4 * MT; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
+                                               (int)(sx * per_split) + mine + i * kTile, 0, 0);
+  }
+
+  // ---- epilogue: lane holds, for panel i and tile t, output channels
+  // 16 p + 4 (lane >> 4) + v (v < 4) of activation row 16 (MT wm + t) + (lane & 15) ----
+  const bool vec = (n & 3) == 0 && (((uintptr_t)y) & 7) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
+    if (n0 >= n) continue;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int row = (wm * MT + t) * 16 + col;
+      if (row >= m) continue;
+      uint16_t h[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sc = FMT == kFmtNvfp4 ? h_scale : row_scale[i][v];
+        const _Float16 o = valid ? (_Float16)(sc * acc[i][t][v]) : (_Float16)__builtin_nanf("");
+        h[v] = __builtin_bit_cast(uint16_t, o);
+      }
+      uint16_t* dst = y + (int64_t)row * n + n0;
+      if (vec && n0 + 3 < n) {
+        *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                               (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n0 + v < n) dst[v] = h[v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch plumbing
+// ---------------------------------------------------------------------------
+
+int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; }
+
+// K splits.  With 32 or 64 rows the call is HBM-bound: enough workgroups for
+// every CU, and few splits (their partial tiles are extra traffic).  With
+// 128 or 256 rows the matrix unit bounds it and one workgroup fills a CU
+// (its slice stages take 128 KiB of LDS): the split count minimises whole
+// waves of 256 workgroups times k-steps per workgroup (about 0.107 us of
+// MFMA work per activation tile and k-step) plus the partial tiles'
+// write-and-read traffic at ~5 TB/s.
+int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
+                       PrefillLaunch* out) {
+  const int mt = prefill_tiles(m);
+  const int64_t P = panels_of(n);
+  const int64_t blocks = (P + kPanelsPerBlock - 1) / kPanelsPerBlock;
+  const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
+  const int64_t smax = std::max<int64_t>(1, J / 4);
+  auto need = [&](int64_t s) -> size_t {
+    if (s <= 1) return 0;
+    const size_t counters = ((size_t)blocks * 4 + 255) / 256 * 256;
+    return counters + (size_t)s * blocks * (kLanes * kWaves) * (4 * mt) * 16;
+  };
+  int64_t S = 1;
+  if (blocks > 0 && mt <= 2) {
+    S = std::min<int64_t>((256 + blocks - 1) / blocks, smax);
+  } else if (blocks > 0) {
+    double best = 0.0;
+    for (int64_t s = 1; s <= std::min<int64_t>(smax, 16); ++s) {
+      const double waves = (double)((blocks * s + 255) / 256);
+      const double cost = waves * (double)((J + s - 1) / s) * 0.107 * mt +
+                          2.0 * (double)need(s) / 5e6;  // us
+      if (s == 1 || cost < best) {
+        best = cost;
+        S = s;
+      }
+    }
+  }
+  int64_t steps = J > 0 ? (J + S - 1) / S : 1;
+  S = J > 0 ? (J + steps - 1) / steps : 1;
+  while (S > 1 && need(S) > ws_bytes) {
+    S -= 1;
+    steps = (J + S - 1) / S;
+    S = (J + steps - 1) / steps;
+  }
+  // the partial area is addressed with 32-bit offsets
+  if (need(S) >= ((size_t)1 << 31)) return kGemmNoWorkspace;
+  out->mt = mt;
+  out->depth = mt >= 4 ? 3 : 5;  // as compiled below
+  out->blocks = blocks;
+  out->splits = (int)S;
+  out->split_steps = (int)steps;
+  out->workgroups = blocks * S;
+  out->ws_counters_offset = 0;
+  out->ws_partial_offset = ((size_t)blocks * 4 + 255) / 256 * 256;
+  out->ws_needed = need(S);
+  return kGemmLaunchOk;
+}
+
+namespace {
+
+template <uint32_t FMT, int MT, int D, int NS>
+hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
+  PrefillSplit sp{l.splits, l.split_steps, nullptr, nullptr};
+  if (l.splits > 1) {
+    sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
+    sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
+  }
+  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS>), dim3((unsigned)l.workgroups),
+                     dim3(kLanes * kWaves), 0, (hipStream_t)a.stream, (const uint8_t*)a.packed,
+                     a.x, a.y, a.m, a.n, a.k, sp);
+  return hipGetLastError();
+}
+
+template <uint32_t FMT>
+hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
+  switch (l.mt) {
+    case 1: return launch_pf<FMT, 1, 5, 6>(a, l);
+    case 2: return launch_pf<FMT, 2, 5, 6>(a, l);
+    case 4: return launch_pf<FMT, 4, 3, 4>(a, l);
+    default: return launch_pf<FMT, 8, 3, 2>(a, l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(uint32_t fmt, const GemmArgs& a, const PrefillLaunch& l) {
+  return fmt == kFmtNvfp4 ? launch_pf_fmt<kFmtNvfp4>(a, l) : launch_pf_fmt<kFmtFp8>(a, l);
+}
+
+}  // namespace qpn

@@ -18,6 +18,8 @@ QPN_OK = 0
 OP_GEMM_NVFP4 = 1
 OP_GEMM_FP8 = 2
 OP_LMHEAD_NVFP4 = 3
+OP_PREFILL_NVFP4 = 4
+OP_PREFILL_FP8 = 5
 
 FMT_NVFP4 = "nvfp4"
 FMT_FP8 = "fp8"
@@ -49,6 +51,8 @@ def _load():
         "qpn_requant_fp8_to_nvfp4": ([vp, sz, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_gemm_prefill_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_gemm_prefill_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_lmhead_nvfp4": ([vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_lmhead_verify_nvfp4": ([vp, vp, vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_debug_unpack_nvfp4": ([vp, i64, i64, vp, vp, vp, vp], i32),
@@ -71,7 +75,8 @@ lib = _load()
 EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_fp8_packed_bytes", "qpn_workspace_bytes", "qpn_gemm_plan", "qpn_pack_nvfp4", "qpn_pack_fp8",
             "qpn_requant_fp8_to_nvfp4",
-            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
+            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_gemm_prefill_nvfp4", "qpn_gemm_prefill_fp8",
+            "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
             "qpn_debug_unpack_nvfp4",
             "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",
             "qpn_debug_read_ceiling", "qpn_debug_set_plan")
@@ -235,6 +240,26 @@ def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=Non
         out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
     op = OP_GEMM_NVFP4 if pw.fmt == FMT_NVFP4 else OP_GEMM_FP8
     fn = lib.qpn_gemm_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_fp8
+    st = _stream(stream)
+    need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
+    if ws is None and need > 0:
+        ws = workspace(need, x.device, st.value or 0)
+    check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k,
+             _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, st))
+    return out
+
+
+def prefill(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=None,
+            ws: torch.Tensor = None) -> torch.Tensor:
+    """Y = X * What^T for 0 <= m <= 256 activation rows through
+    qpn_gemm_prefill_nvfp4 / qpn_gemm_prefill_fp8.  `ws` (zero-filled before
+    its first use) defaults to a cached per-stream workspace."""
+    _x_check(x, pw.k)
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+    op = OP_PREFILL_NVFP4 if pw.fmt == FMT_NVFP4 else OP_PREFILL_FP8
+    fn = lib.qpn_gemm_prefill_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_prefill_fp8
     st = _stream(stream)
     need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
     if ws is None and need > 0:

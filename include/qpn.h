@@ -83,6 +83,8 @@ extern "C" {
 #define QPN_OP_GEMM_NVFP4 1
 #define QPN_OP_GEMM_FP8 2
 #define QPN_OP_LMHEAD_NVFP4 3
+#define QPN_OP_PREFILL_NVFP4 4
+#define QPN_OP_PREFILL_FP8 5
 
 /* Human-readable name of a status code (static string, never NULL). */
 QPN_API const char *qpn_status_string(int status);
@@ -108,8 +110,10 @@ QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
  * given less workspace than this still runs, with fewer K splits, as long as
  * the fewest splits whose activation slice (m * K / splits FP16 values) fits
  * in LDS still fit the workspace; otherwise it returns QPN_ERR_BUFFER (only
- * for large m * k, e.g. m > 4 with k = 17408).  Returns (size_t)-1 for an
- * unknown op or invalid shape.  Pure host. */
+ * for large m * k, e.g. m > 4 with k = 17408).  The prefill ops take
+ * 0 <= m <= 256 and run with fewer splits (down to none) on any smaller
+ * workspace.  Returns (size_t)-1 for an unknown op or invalid shape.  Pure
+ * host. */
 QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
 
 /* Launch plan a call of kind `op` (QPN_OP_*) uses for (m, n, k) when given
@@ -123,7 +127,10 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * workgroups - 0 unless the plan balances whole panels per CU - each take
  * panels_per_workgroup whole panels.  valu_dot is 1 for the diagnostic
  * plans that contract with VALU dot products instead of the MFMA (only when
- * forced with qpn_debug_set_plan).  A pure function of the shape (and of
+ * forced with qpn_debug_set_plan).  For the prefill ops: every workgroup
+ * covers 8 panels (two wavefronts per panel, one per half of the activation
+ * rows), activation_rows is the 32, 64, 128 or 256 rows a workgroup takes,
+ * and split_workgroups equals workgroups.  A pure function of the shape (and of
  * a plan forced with qpn_debug_set_plan), independent of any declared
  * maximum.  Any output pointer may be NULL.  Returns QPN_OK or
  * QPN_ERR_SHAPE.  Pure host. */
@@ -188,6 +195,26 @@ QPN_API int qpn_gemm_nvfp4(const void *packed, const uint16_t *x, uint16_t *y, i
 QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int m,
                  int64_t n, int64_t k, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/* Prefill-sized activation blocks against the same packed weights (lcz.me
+ * page, "strata" section: prompt processing on FP16 tensor-core tiles, with
+ * activations in FP16; aiwitness.kr page, questions section: prefill is the
+ * phase that the old card loses).  The same product as qpn_gemm_nvfp4 /
+ * qpn_gemm_fp8 for 0 <= m <= 256 activation rows: Y[m, n] = FP16_RNE(scale *
+ * sum_k X[m, k] * W[n, k]), FP32 accumulation, weights decoded in registers,
+ * no dequantised copy.  Meant for m > 8 (for m <= 8 the skinny entry points
+ * are faster).  x: [m, k] FP16, 16-byte aligned; y: [m, n] FP16.
+ * workspace: zero-filled device memory, 16-byte aligned, of
+ * qpn_workspace_bytes(QPN_OP_PREFILL_*, m, n, k) bytes for the preferred K
+ * split (NULL with 0 bytes is valid and runs without splitting K); every
+ * call leaves it zero-filled.  m > 256 gives QPN_ERR_SHAPE.  A blob whose
+ * header does not match gives FP16 NaN outputs.  One kernel on `stream`. */
+QPN_API int qpn_gemm_prefill_nvfp4(const void *packed, const uint16_t *x, uint16_t *y,
+                                   int m, int64_t n, int64_t k, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+QPN_API int qpn_gemm_prefill_fp8(const void *packed, const uint16_t *x, uint16_t *y, int m,
+                                 int64_t n, int64_t k, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* NVFP4 lm_head with fused greedy argmax (taozi.news section "自研 QPN 内核",
  * the native 4-bit lm_head; section "一些工程细节与长上下文发现", drafts

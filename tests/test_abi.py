@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(qpn):
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     lib = ctypes.CDLL(qpn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -229,6 +229,52 @@ def test_requant_argument_errors(qpn):
     assert call(sb=n8 - 1) == 4
     assert call(db=n4 - 1) == 4
     assert call(dst=A256 + 256) == 4                          # overlapping blobs
+
+
+def test_prefill_queries(qpn):
+    for op in (qpn.OP_PREFILL_NVFP4, qpn.OP_PREFILL_FP8):
+        for m, n, k in [(9, 17408, 5120), (64, 5120, 17408), (256, 17408, 5120), (256, 5120, 17408),
+                        (130, 200, 1024), (1, 16, 64), (256, 6144, 5120)]:
+            pl = qpn.gemm_plan(op, m, n, k)
+            ks = 128 if op == qpn.OP_PREFILL_NVFP4 else 64
+            J = -(-k // ks)
+            blocks = -(-n // 128)
+            assert pl.activation_rows in (32, 64, 128, 256) and pl.activation_rows >= m
+            assert pl.activation_rows < 2 * m or pl.activation_rows == 32
+            assert pl.workgroups == blocks * pl.splits == pl.split_workgroups
+            assert 1 <= pl.splits <= max(1, J // 4)
+            # every split has at least one k-step and together they cover K
+            steps = -(-J // pl.splits)
+            assert (pl.splits - 1) * steps < J <= pl.splits * steps
+            ws = qpn.workspace_bytes(op, m, n, k)
+            assert (ws == 0) == (pl.splits == 1)
+            if pl.splits > 1:   # counters, then S partial tiles of 128 x rows FP32 per block
+                cnt = -(-blocks * 4 // 256) * 256
+                assert ws == cnt + pl.splits * blocks * 128 * pl.activation_rows * 4
+        assert qpn.workspace_bytes(op, 0, 64, 64) == 0
+        assert qpn.workspace_bytes(op, 257, 64, 64) == 2 ** 64 - 1
+        with pytest.raises(qpn.QpnError):
+            qpn.gemm_plan(op, 257, 64, 64)
+    # a long-K call is split so that nearly every CU gets one workgroup (one wave of them)
+    assert 200 <= qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 5120, 17408).workgroups <= 256
+
+
+def test_prefill_argument_errors(qpn):
+    L = qpn.lib
+    v = ctypes.c_void_p
+    for fn in (L.qpn_gemm_prefill_nvfp4, L.qpn_gemm_prefill_fp8):
+        def call(packed=A256, x=A16, y=A16, m=16, n=32, k=64, ws=0, wsb=0):
+            return fn(v(packed), v(x), v(y), m, n, k, v(ws), wsb, None)
+        assert call(m=257) == 2
+        assert call(m=-1) == 2
+        assert call(k=12) == 2
+        assert call(packed=0) == 1
+        assert call(y=0) == 1
+        assert call(x=A16 + 8) == 3
+        assert call(packed=A256 + 16) == 3
+        assert call(y=A16 + 1) == 3
+        assert call(ws=A16 + 4, wsb=1024) == 3
+        assert call(m=0) == 0 and call(n=0) == 0
 
 
 def test_pack_argument_errors(qpn):

@@ -1,0 +1,128 @@
+"""Prefill-sized activation blocks (9 <= m <= 256) against the oracle.
+
+The same parity bar as the skinny GEMM: per element |err| <= 1e-2 rms(ref)
++ 1e-3 and relative Frobenius error <= 2e-3 against the FP64 oracle product
+of the canonical codes.  Shapes span several 128-channel blocks, ragged N
+and M tails, K splits, every activation-tile count (32, 64, 128, 256 rows)
+and the full decoder shapes (sampled output channels).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_quantized_skinny_qpn_amd import synth
+from gpu_util import dev, host, log, need_gpu, parity
+
+pytestmark = pytest.mark.gpu
+
+MS = (9, 16, 31, 33, 64, 100, 128, 129, 200, 256)
+
+
+def _prefill_one_range(qpn, pw, xd):
+    """The call without a workspace: one K range, so every workgroup runs
+    all k-steps through many cycles of its prefetch ring."""
+    out = torch.empty((xd.shape[0], pw.n), dtype=torch.float16, device="cuda")
+    fn = qpn.lib.qpn_gemm_prefill_nvfp4 if pw.fmt == qpn.FMT_NVFP4 else qpn.lib.qpn_gemm_prefill_fp8
+    assert fn(pw.blob.data_ptr(), xd.data_ptr(), out.data_ptr(), xd.shape[0], pw.n, pw.k, None, 0, None) == 0
+    return out
+
+
+def _pack(qpn, fmt, w):
+    if fmt == "nvfp4":
+        codes, scales, g = oracle.pack_nvfp4(w)
+        return qpn.pack_nvfp4(dev(w)), lambda x, rows=slice(None): oracle.gemm_nvfp4(codes[rows], scales[rows], g, x)
+    codes, rs = oracle.pack_fp8(w)
+    return qpn.pack_fp8(dev(w)), lambda x, rows=slice(None): oracle.gemm_fp8(codes[rows], rs[rows], x)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("n,k", [(200, 1024), (1000, 256), (130, 4096), (16, 64)])
+def test_prefill_small(fmt, n, k):
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=n + k)
+    x = synth.activations(256, k, seed=n + k, m_max=256)
+    pw, ref = _pack(qpn, fmt, w)
+    op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+    for m in MS:
+        pl = qpn.gemm_plan(op, m, n, k)
+        log(f"prefill {fmt} {n}x{k} m={m}: {pl.activation_rows} rows, {pl.splits} splits")
+        xd = dev(x[:m])
+        y_ref = ref(x[:m])
+        parity(host(qpn.prefill(pw, xd)), y_ref, f"prefill {fmt} {n}x{k} m={m}")
+        parity(host(_prefill_one_range(qpn, pw, xd)), y_ref, f"prefill {fmt} {n}x{k} m={m} one K range")
+
+
+@pytest.mark.parametrize("fmt,n,k", [("nvfp4", 17408, 5120), ("nvfp4", 5120, 17408),
+                                     ("fp8", 6144, 5120), ("fp8", 7168, 5120)])
+def test_prefill_full_size_sampled(fmt, n, k):
+    """Decoder shapes at the launch configuration the benchmark times; the
+    oracle computes 192 sampled output channels (including the last)."""
+    qpn = need_gpu()
+    log(f"prefill full {fmt} {n}x{k}: drawing weights")
+    w = synth.weights(n, k, seed=7)
+    x = synth.activations(256, k, seed=7, m_max=256)
+    pw, ref = _pack(qpn, fmt, w)
+    rows = np.sort(np.concatenate([np.random.default_rng(n).choice(n - 1, 191, replace=False), [n - 1]]))
+    for m in (16, 64, 128, 256):
+        log(f"prefill full {fmt} {n}x{k} m={m}")
+        y = host(qpn.prefill(pw, dev(x[:m])))
+        parity(y[:, rows], ref(x[:m], rows), f"prefill full {fmt} {n}x{k} m={m}")
+    y = host(_prefill_one_range(qpn, pw, dev(x[:128])))
+    parity(y[:, rows], ref(x[:128], rows), f"prefill full {fmt} {n}x{k} m=128 one K range")
+
+
+def test_prefill_is_deterministic_and_row_independent():
+    """Two identical calls give identical bits (split-K partials are summed
+    in split order), and a row's result does not depend on the rows around
+    it: the first 20 rows of a 200-row block equal a 20-row call bit for bit
+    (the K summation order of a row is the same in every tile)."""
+    qpn = need_gpu()
+    n, k = 3000, 2048
+    w = synth.weights(n, k, seed=9)
+    x = synth.activations(200, k, seed=9, m_max=200)
+    pw, ref = _pack(qpn, "nvfp4", w)
+    y1 = host(qpn.prefill(pw, dev(x)))
+    y2 = host(qpn.prefill(pw, dev(x)))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    parity(y1, ref(x), "prefill 200 rows")
+    y20 = host(qpn.prefill(pw, dev(x[:20])))
+    splits = [qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, n, k).splits for m in (20, 200)]
+    if splits[0] == splits[1]:
+        assert np.array_equal(y20.view(np.uint16), y1[:20].view(np.uint16))
+    else:  # a different K split regroups the FP32 sums: parity only
+        parity(y20, ref(x[:20]), "prefill 20 rows")
+
+
+def test_prefill_leaves_workspace_zeroed_and_runs_without_one():
+    qpn = need_gpu()
+    n, k = 640, 8192
+    w = synth.weights(n, k, seed=4)
+    x = synth.activations(96, k, seed=4, m_max=96)
+    pw, ref = _pack(qpn, "nvfp4", w)
+    need = qpn.workspace_bytes(qpn.OP_PREFILL_NVFP4, 96, n, k)
+    assert need > 0  # this shape splits K
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y_ref = ref(x)
+    for _ in range(2):
+        y = host(qpn.prefill(pw, dev(x), ws=ws))
+        assert not host(ws).any()
+        parity(y, y_ref, "prefill with workspace")
+    # no workspace: one K range
+    parity(host(_prefill_one_range(qpn, pw, dev(x))), y_ref, "prefill without workspace")
+
+
+def test_prefill_wrong_blob_gives_nan():
+    qpn = need_gpu()
+    n, k = 256, 512
+    pw8 = qpn.pack_fp8(dev(synth.weights(n, k, seed=2)))
+    x = dev(synth.activations(40, k, seed=2, m_max=40))
+    bad = qpn.PackedWeight(torch.zeros(qpn.nvfp4_packed_bytes(n, k), dtype=torch.uint8, device="cuda"),
+                           n, k, qpn.FMT_NVFP4)
+    assert np.all(np.isnan(host(qpn.prefill(bad, x)).astype(np.float32)))
+    # an FP8 blob read as NVFP4 of the same shape (its header names FP8)
+    blob = torch.zeros(qpn.nvfp4_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
+    nb = min(blob.numel(), pw8.nbytes)
+    blob[:nb] = pw8.blob[:nb]
+    y = host(qpn.prefill(qpn.PackedWeight(blob, n, k, qpn.FMT_NVFP4), x))
+    assert np.all(np.isnan(y.astype(np.float32)))
