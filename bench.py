@@ -27,7 +27,7 @@ computing one complete headline step (all six calls, every row), repeated
 until about ten seconds of CPU time have been spent.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
-    python bench.py --traffic-workload | --contraction-ab   (profiling workloads)
+    python bench.py --traffic-workload | --contraction-ab | --prefill-workload   (profiling)
 """
 import argparse
 import hashlib
@@ -288,6 +288,24 @@ def contraction_ab(qpn, torch):
     print(json.dumps({"contraction_ab": rows}), flush=True)
 
 
+def prefill_workload(qpn, torch):
+    """Workload for profiling the prefill kernel: each PREFILL call and block
+    size six times on rotating copies."""
+    from fp8_quantized_skinny_qpn_amd import synth
+    for name, n, k, fmt, ms in PREFILL:
+        sh = Shape(qpn, torch, name, n, k, fmt, ())
+        xs = torch.from_numpy(synth.activations(256, k, seed=0, m_max=256)).cuda()
+        for m in ms:
+            xm = xs[:m].contiguous()
+            ym = torch.empty((m, n), dtype=torch.float16, device="cuda")
+            for _ in range(6):
+                qpn.prefill(sh.next_copy(), xm, out=ym)
+            torch.cuda.synchronize()
+            log(f"{name} M={m}")
+        del sh, xs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +315,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
+    ap.add_argument("--prefill-workload", action="store_true",
+                    help="only run the prefill calls (for profiling; no JSON line)")
     ap.add_argument("--contraction-ab", action="store_true",
                     help="only time the headline calls with MFMA and with VALU-dot contraction")
     args = ap.parse_args()
@@ -317,6 +337,9 @@ def main():
         return
     if args.contraction_ab:
         contraction_ab(qpn, torch)
+        return
+    if args.prefill_workload:
+        prefill_workload(qpn, torch)
         return
 
     log("setting up headline shapes")
