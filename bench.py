@@ -232,6 +232,25 @@ def read_ceiling(qpn, torch):
     return (2 << 30) / float(np.median(ts)) / 1e9
 
 
+def read_ceiling_call(qpn, torch, nbytes):
+    """Read ceiling at one call's size: the same streaming read over nbytes
+    (rounded down to 16), on rotating regions of >= 1 GiB in all, timed like
+    a GEMM call (average launch time in back-to-back graphs).  Returns
+    (seconds per launch, bytes read)."""
+    nb = nbytes // 256 * 256
+    regions = max(2, math.ceil(ROTATE_BYTES / nb))
+    buf = torch.empty(regions * nb, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    views = [buf[i * nb:(i + 1) * nb] for i in range(regions)]
+    g = capture(torch, lambda: [qpn.debug_read_ceiling(views[i % regions], sink) for i in range(BATCH)])
+    g.replay()
+    torch.cuda.synchronize()
+    per = [t / BATCH for t in time_graph(torch, g, 5)]
+    del g, views, buf
+    torch.cuda.empty_cache()
+    return float(np.median(per)), nb
+
+
 def traffic_workload(qpn, torch):
     """Workload for the rocprofv3 PMC passes (FETCH_SIZE, WRITE_SIZE), one per
     run: calibration kernels of known size (a 256 MiB streaming read and a
@@ -498,6 +517,7 @@ def main():
             torch.cuda.empty_cache()
 
     ceiling = read_ceiling(qpn, torch)
+    call_s, call_b = read_ceiling_call(qpn, torch, dk["bytes"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -543,6 +563,12 @@ def main():
             "algorithmic_bytes_per_launch": dk["bytes"],
             "avg_launch_us": round(avg_s * 1e6, 3),
             "launches_timed": len(dk["t"]) * BATCH,
+            # the same streaming read at this call's size: what any single
+            # launch of this many bytes reaches on this GPU
+            "read_ceiling_at_call_size": {"bytes": call_b, "us": round(call_s * 1e6, 3),
+                                          "GBps": round(call_b / call_s / 1e9, 1),
+                                          "frac_hbm_peak": round(call_b / call_s / 1e9 / HBM_PEAK_GBPS, 4)},
+            "frac_of_read_ceiling_at_call_size": round(achieved / (call_b / call_s / 1e9), 4),
         },
         "cpu_baseline": cpu,
         "breakdown": breakdown,

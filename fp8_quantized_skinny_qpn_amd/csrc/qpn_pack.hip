@@ -9,6 +9,8 @@
 // section "v1.1 的关键改进").  Every FP32 step is one IEEE operation in the
 // order documented in include/qpn.h; the library is built with contraction
 // off and correctly rounded division.
+#include <algorithm>
+
 #include "qpn_common.h"
 #include "qpn_internal.h"
 
@@ -372,20 +374,35 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(const uint8_t* __restri
 
 // Streaming-read ceiling: block b reads 2048 consecutive 16-byte units with
 // nontemporal loads (eight per thread, all in flight together).
-__global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4* __restrict__ buf,
-                                                           int64_t count16,
-                                                           uint32_t* __restrict__ sink) {
+// Streaming read of count16 16-byte units.  A grid-stride loop in which every
+// pass of the grid covers one contiguous window (all workgroups read
+// neighbouring lines at the same time) with four loads in flight per thread.
+// Of the shapes measured on MI355X (one-shot blocks, per-workgroup slabs,
+// grid-stride windows; 256 to 2048 workgroups of 256 to 1024 threads), 1024
+// workgroups of 512 threads striding over the buffer read a 50 MB buffer
+// fastest; on multi-GiB buffers a single pass (one workgroup per window) read
+// about 4% faster than the capped grid, so the grid is capped only up to
+// kCeilCappedUnits.
+constexpr int kCeilThreads = 512;
+constexpr int kCeilUnroll = 4;
+constexpr int64_t kCeilMaxBlocks = 1024;
+constexpr int64_t kCeilCappedUnits = (int64_t)1 << 24;  // 256 MiB
+
+__global__ __launch_bounds__(kCeilThreads) void read_ceiling_kernel(const u32x4* __restrict__ buf,
+                                                                    int64_t count16,
+                                                                    uint32_t* __restrict__ sink) {
   u32x4 acc = {0, 0, 0, 0};
-  const int64_t base = (int64_t)blockIdx.x * (256 * 8) + threadIdx.x;
-  if (base + 7 * 256 < count16) {
-    u32x4 v[8];
+  const int64_t window = (int64_t)gridDim.x * kCeilThreads * kCeilUnroll;
+  for (int64_t b = (int64_t)blockIdx.x * kCeilThreads * kCeilUnroll + threadIdx.x; b < count16;
+       b += window) {
+    u32x4 v[kCeilUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + base + u * 256);
+    for (int u = 0; u < kCeilUnroll; ++u) {
+      const int64_t i = b + (int64_t)u * kCeilThreads;
+      v[u] = i < count16 ? __builtin_nontemporal_load(buf + i) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= v[u];
-  } else {
-    for (int u = 0; u < 8; ++u)
-      if (base + u * 256 < count16) acc ^= __builtin_nontemporal_load(buf + base + u * 256);
+    for (int u = 0; u < kCeilUnroll; ++u) acc ^= v[u];
   }
   // The fold is stored only when it equals a fixed value, which keeps the
   // loads alive without tens of thousands of atomics on one word.
@@ -475,8 +492,11 @@ hipError_t launch_decode_nvfp4(const uint8_t* codes16, const uint8_t* scales2, i
 }
 
 hipError_t launch_read_ceiling(const void* buf, int64_t count16, uint32_t* sink, void* stream) {
-  const int64_t blocks = (count16 + 2047) / 2048;
-  hipLaunchKernelGGL(read_ceiling_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+  const int64_t per_block = (int64_t)kCeilThreads * kCeilUnroll;
+  const int64_t needed = (count16 + per_block - 1) / per_block;
+  const int64_t blocks = count16 > kCeilCappedUnits ? needed : std::min<int64_t>(kCeilMaxBlocks, needed);
+  hipLaunchKernelGGL(read_ceiling_kernel, dim3((unsigned)blocks), dim3(kCeilThreads), 0,
+                     (hipStream_t)stream,
                      (const u32x4*)buf, count16, sink);
   return hipGetLastError();
 }
