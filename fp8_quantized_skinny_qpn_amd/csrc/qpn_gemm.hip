@@ -145,6 +145,18 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   constexpr int XSTEP = (KS / 8) * MB;               // 16-byte activation units per k-step
   static_assert(NW <= 16, "at most 16 wavefronts");
   static_assert(D * LPS < 64, "wait count");
+  // Order of a k-step's activation units in LDS.  Unit xunit(t, kg, mm)
+  // feeds MFMA t of lane (mm, kg), i.e. X[mm][kg * KS / 4 + 8 t, + 8).  The
+  // plain order (t, kg, mm) makes one 64-lane staging load cover whole
+  // 128-byte lines of every row except for NVFP4 at 8 rows, where it would
+  // take half of 16 lines (each line then read by two loads); there the
+  // order (kg / 2, t, kg % 2, mm) gives each load the first or second 64 K
+  // of the k-step, one whole line per row.
+  constexpr bool XLINE = FMT == kFmtNvfp4 && MB == 8;
+  constexpr int XT = XLINE ? 2 * MB : 4 * MB;  // units between MFMA t and t + 1
+  auto xunit = [](int t, int kg, int mm) {
+    return XLINE ? (((kg >> 1) * GR + t) * 2 + (kg & 1)) * MB + mm : (t * 4 + kg) * MB + mm;
+  };
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int lane = threadIdx.x & (kLanes - 1);
@@ -227,10 +239,11 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 1. activation slice -> LDS (after the first weight k-step) ----
-  // Unit u (16 bytes) = ((jl * GR + t) * 4 + kg) * MB + mm holds
-  // X[mm][K .. K + 8), K = (j0 + jl) * KS + kg * KS / 4 + 8 t; load q of the
-  // slice fills units [64 q, 64 q + 64).  Rows >= m and K outside the range
-  // read zeros (out-of-range buffer offsets).  Offsets stay below 2^25.
+  // Unit jl * XSTEP + xunit(t, kg, mm) (16 bytes) holds X[mm][K .. K + 8),
+  // K = (j0 + jl) * KS + kg * KS / 4 + 8 t: what lane (mm, kg) feeds MFMA t
+  // of local k-step jl.  Load q of the slice fills units [64 q, 64 q + 64).
+  // Rows >= m and K outside the range read zeros (out-of-range buffer
+  // offsets).  Offsets stay below 2^25.
   {
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrcFlags);
@@ -240,8 +253,15 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
       const int u = q * 64 + lane;
       const int mm = u % MB;
       const int rest = u / MB;
-      const int jl = rest / (4 * GR);
-      const int kpos = (j0 + jl) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
+      int kpos;
+      if constexpr (XLINE) {
+        const int jl = u / XSTEP;
+        const int r = rest % (XSTEP / MB);
+        kpos = (j0 + jl) * KS + (2 * (r / (2 * GR)) + (r & 1)) * (KS / 4) + 8 * ((r / 2) % GR);
+      } else {
+        const int jl = rest / (4 * GR);
+        kpos = (j0 + jl) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
+      }
       const bool ok = u < units && mm < m && kpos < k;
       const int off = ok ? (int)(((int64_t)mm * k + kpos) * 2) : 0x7FFFFFF0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -278,15 +298,16 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   // activation operand for this lane: row min(row, MB-1) (columns >= m are
   // discarded by the epilogue), K group kg, local step w + c W
   const int xrow = row < MB ? row : MB - 1;
-  const uint8_t* xlane = smem + ((w * GR * 4 + kg) * MB + xrow) * 16;
-  constexpr int XC = W * GR * 4 * MB * 16;  // LDS bytes per interleave round
+  const uint8_t* xlane =
+      XLINE ? smem + (w * XSTEP + xunit(0, kg, xrow)) * 16 : smem + ((w * GR * 4 + kg) * MB + xrow) * 16;
+  constexpr int XC = W * XSTEP * 16;  // LDS bytes per interleave round
 
   // VALU-dot contraction: lane (row, kg) keeps one FP32 sum per activation
   // row over its own K positions, reading all MB rows' units of its K group
   float vacc[MB];
 #pragma unroll
   for (int mm = 0; mm < MB; ++mm) vacc[mm] = 0.f;
-  const uint8_t* xkg = smem + ((w * GR * 4 + kg) * MB) * 16;
+  const uint8_t* xkg = smem + (w * XSTEP + xunit(0, kg, 0)) * 16;
 
   auto compute = [&](int c, const WFrag& f) {
     half8 a[GR];
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
       for (int t = 0; t < GR; ++t) {
 #pragma unroll
         for (int mm = 0; mm < MB; ++mm) {
-          const half8 b = *reinterpret_cast<const half8*>(xs + (t * 4 * MB + mm) * 16);
+          const half8 b = *reinterpret_cast<const half8*>(xs + (t * XT + mm) * 16);
           float sacc = vacc[mm];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -313,7 +334,7 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
       const uint8_t* xs = xlane + c * XC;
 #pragma unroll
       for (int t = 0; t < GR; ++t) {
-        const half8 b = *reinterpret_cast<const half8*>(xs + t * 4 * MB * 16);
+        const half8 b = *reinterpret_cast<const half8*>(xs + t * XT * 16);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc, 0, 0, 0);
       }
     }
