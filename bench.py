@@ -28,6 +28,7 @@ until about ten seconds of CPU time have been spent.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
     python bench.py --traffic-workload | --contraction-ab | --prefill-workload   (profiling)
+    python bench.py --summarize-traffic FETCH_CSV WRITE_CSV   (profiles/traffic.json from the PMC passes)
 """
 import argparse
 import hashlib
@@ -275,6 +276,64 @@ def traffic_workload(qpn, torch):
         torch.cuda.empty_cache()
 
 
+def summarize_traffic(fetch_csv, write_csv):
+    """Turn the two rocprofv3 PMC passes of --traffic-workload (FETCH_SIZE and
+    WRITE_SIZE counter_collection CSVs) into per-launch HBM bytes: each
+    counter is scaled by what it reads for the calibration kernel of known
+    size (the 256 MiB streaming read for FETCH_SIZE, the 256 MiB fill for
+    WRITE_SIZE), and the GEMM launches are assigned, in order, six to each
+    headline call.  Writes profiles/traffic.json (tagged with the kernel
+    source hash, so bench.py reports it only while the kernel is unchanged)
+    and prints the markdown table of the traffic summary."""
+    import csv
+    cal = 256 << 20
+
+    def rows(path, counter):
+        out = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]) * 1024))
+        out.sort()
+        return out
+
+    def factor(rs, pick):
+        vals = [v for _, name, v in rs if pick(name)]
+        if not vals:
+            raise SystemExit("calibration kernel not found")
+        return cal / float(np.median(vals))
+
+    fr, wr = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    f_fac = factor(fr, lambda n: "read_ceiling_kernel" in n)
+    w_fac = factor(wr, lambda n: "FillFunctor<unsigned char>" in n)
+    calls = [f"{name}_M{m}" for name, _, _, _ in HEADLINE for m in HEADLINE_M]
+    gf = [(name, v * f_fac) for _, name, v in fr if "skinny_gemm_kernel" in name]
+    gw = [(name, v * w_fac) for _, name, v in wr if "skinny_gemm_kernel" in name]
+    if len(gf) != 6 * len(calls) or len(gw) != 6 * len(calls):
+        raise SystemExit(f"expected {6 * len(calls)} GEMM launches, got {len(gf)} / {len(gw)}")
+    per_kernel = {}
+    lines = ["| call | kernel | HBM read MB | HBM write MB | read / algorithmic |", "|---|---|---:|---:|---:|"]
+    hsh = kernel_source_hash()
+    for i, call in enumerate(calls):
+        kname = gf[6 * i][0].split("(")[0].replace("void ", "")
+        rd = float(np.mean([v for _, v in gf[6 * i:6 * i + 6]]))
+        wt = float(np.mean([v for _, v in gw[6 * i:6 * i + 6]]))
+        n, k = next((n, k) for name, n, k, _ in HEADLINE if call.startswith(name))
+        ab = algo_bytes(n, k, "nvfp4")
+        lines.append(f"| {call} | `{kname}` | {rd / 1e6:.3f} | {wt / 1e6:.3f} | {rd / ab:.3f} |")
+        e = per_kernel.setdefault(kname, {"source_hash": hsh, "calls": [], "read_bytes": [], "write_bytes": []})
+        e["calls"].append(call)
+        e["read_bytes"].append(int(round(rd)))
+        e["write_bytes"].append(int(round(wt)))
+    for e in per_kernel.values():
+        e["bytes_per_launch"] = int(round(np.mean(e["read_bytes"]) + np.mean(e["write_bytes"])))
+    with open(os.path.join(HERE, "profiles", "traffic.json"), "w") as fh:
+        json.dump(per_kernel, fh, indent=1)
+        fh.write("\n")
+    print(f"FETCH_SIZE factor {f_fac:.4f}, WRITE_SIZE factor {w_fac:.4f}")
+    print("\n".join(lines))
+
+
 # The contraction A/B: plans 1 and 2 (MFMA) against plans 12 and 11, the same
 # launch shapes contracting with VALU dot products instead.
 CONTRACTION_AB = ((1, 1, 12), (8, 2, 11))  # (M, MFMA plan, VALU-dot plan)
@@ -332,6 +391,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--extra", action="store_true", help="also time the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from the two PMC passes of --traffic-workload")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
     ap.add_argument("--prefill-workload", action="store_true",
@@ -340,6 +401,9 @@ def main():
                     help="only time the headline calls with MFMA and with VALU-dot contraction")
     args = ap.parse_args()
 
+    if args.summarize_traffic:  # host only: post-processes rocprofv3 output
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}): the QPN skinny "
               "GEMM is measured on one MI355X; sharding across GPUs is a design note only.",
