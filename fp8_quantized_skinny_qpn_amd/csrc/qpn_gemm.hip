@@ -562,6 +562,7 @@ constexpr GemmPlan kPlans[] = {
     {3, 4, 4, 2, 256},        // 10
     {3, 5, 4, 0, 256, 1},     // 11: plan 2, VALU dot
     {4, 1, 4, 0, 256, 1},     // 12: plan 1, VALU dot
+    {2, 8, 4, 0, 256},        // 13
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -580,6 +581,7 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
     case 10: return launch_mb<FMT, 3, 4, 4, ARGMAX>(a, l);
     case 11: return launch_mb<FMT, 3, 5, 4, ARGMAX, true>(a, l);
     case 12: return launch_mb<FMT, 4, 1, 4, ARGMAX, true>(a, l);
+    case 13: return launch_mb<FMT, 2, 8, 4, ARGMAX>(a, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -602,12 +604,27 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 //     one workgroup per CU, each owning up to five panels (three wavefronts
 //     per panel) that share one staged slice.  FP8 at m > 4 does best with
 //     two panels per workgroup and a deep (10 k-step) prefetch.
+//   NVFP4 m > 2 with many panels (lm_head-sized N): eight panels per
+//     workgroup with two wavefronts each stage the slice once for 8 panels
+//     instead of 5 (a third less slice traffic).  It is used when the
+//     workgroups it gives fill whole rounds of 256 about as well as the
+//     five-panel plan's (0.927 against 0.928 at 151936x5120): 151936x5120
+//     M=8 went from 88.6 to 75.8 us, M=4 from 78.4 to 69.0 us, 65536x5120
+//     M=8 from 42.3 to 34.3 us; with 297 workgroups (37984x5120) it lost.
+namespace {
+double round_fill(int64_t workgroups) {  // average / largest workgroups per CU
+  const int64_t rounds = (workgroups + 255) / 256;
+  return rounds > 0 ? (double)workgroups / (256.0 * (double)rounds) : 1.0;
+}
+}  // namespace
+
 int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
   (void)k;
   const int64_t P = panels_of(n);
   const bool uneven = P >= 256 && P < 3 * 256 && P % 256 >= 16;
   if (fmt == kFmtNvfp4) {
     if (m <= 2) return uneven ? 4 : 1;
+    if (P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02) return 13;
     return 2;
   }
   if (m <= 4) return uneven ? 5 : 1;

@@ -213,7 +213,7 @@ def test_lmhead_verify_every_accept_length(n, k):
             assert np.array_equal(host(am), am0)
             assert tuple(int(v) for v in host(res)) == oracle.greedy_verify(am0, d) == \
                 (L, int(am0[L])), f"m={m} L={L}"
-    # the argmax these rounds were judged on, against the oracle
+    # the argmax these verify rounds were decided on, against the oracle
     if n * k <= 4099 * 1024:
         codes, scales, g = oracle.pack_nvfp4(w)
         y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
