@@ -604,13 +604,14 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 //     one workgroup per CU, each owning up to five panels (three wavefronts
 //     per panel) that share one staged slice.  FP8 at m > 4 does best with
 //     two panels per workgroup and a deep (10 k-step) prefetch.
-//   NVFP4 m > 2 with many panels (lm_head-sized N): eight panels per
+//   NVFP4 m >= 2 with many panels (lm_head-sized N): eight panels per
 //     workgroup with two wavefronts each stage the slice once for 8 panels
 //     instead of 5 (a third less slice traffic).  It is used when the
 //     workgroups it gives fill whole rounds of 256 about as well as the
 //     five-panel plan's (0.927 against 0.928 at 151936x5120): 151936x5120
 //     M=8 went from 88.6 to 75.8 us, M=4 from 78.4 to 69.0 us, 65536x5120
-//     M=8 from 42.3 to 34.3 us; with 297 workgroups (37984x5120) it lost.
+//     M=8 from 42.3 to 34.3 us, and at M=2 151936x5120 from 72.0 to 67.1 us;
+//     with 297 workgroups (37984x5120) it lost, and at M=1 it ties plan 1.
 namespace {
 double round_fill(int64_t workgroups) {  // average / largest workgroups per CU
   const int64_t rounds = (workgroups + 255) / 256;
@@ -623,8 +624,9 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
   const int64_t P = panels_of(n);
   const bool uneven = P >= 256 && P < 3 * 256 && P % 256 >= 16;
   if (fmt == kFmtNvfp4) {
+    if (m >= 2 && P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02)
+      return 13;
     if (m <= 2) return uneven ? 4 : 1;
-    if (P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02) return 13;
     return 2;
   }
   if (m <= 4) return uneven ? 5 : 1;
