@@ -476,14 +476,19 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
 __global__ __launch_bounds__(kLanes * kMaxM) void argmax_finalize_kernel(
     uint64_t* __restrict__ keys, int m, int32_t* __restrict__ argmax,
     const int32_t* __restrict__ draft, int32_t* __restrict__ result) {
-  static_assert(kArgmaxSlots == kLanes, "one slot per lane");
+  static_assert(kArgmaxSlots % kLanes == 0, "whole slots per lane");
   __shared__ int32_t best_index[kMaxM];
   const int r = threadIdx.x / kLanes;
   const int lane = threadIdx.x % kLanes;
   if (r < m) {
     uint64_t* row = keys + (int64_t)r * kArgmaxSlots;
-    uint64_t best = row[lane];
-    row[lane] = 0;  // leave the workspace all zeros
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = lane; i < kArgmaxSlots; i += kLanes) {
+      const uint64_t v = row[i];
+      best = v > best ? v : best;
+      row[i] = 0;  // leave the workspace all zeros
+    }
 #pragma unroll
     for (int off = kLanes / 2; off > 0; off >>= 1) {
       const uint64_t o = shfl_xor_u64(best, off);

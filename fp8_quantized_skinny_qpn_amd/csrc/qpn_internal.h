@@ -71,8 +71,11 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
 
 // Argmax key slots per activation row: panel p folds its key into slot
 // p % kArgmaxSlots with a 64-bit atomic max, so the final pass reads a few
-// keys per row instead of one per panel.
-constexpr int kArgmaxSlots = 64;
+// keys per row instead of one per panel.  The 151936-row lm_head folds
+// ~37 panels into each of 256 slots; with 64 slots (~148 per slot) the
+// atomics on one address queued behind each other and the M=8 lm_head took
+// 3.2 us longer, and with 1024 slots the final pass's reads cost as much.
+constexpr int kArgmaxSlots = 256;
 
 // Launch the GEMM (and, with `argmax`, the per-panel argmax keys).
 hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmLaunch& l);

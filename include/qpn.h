@@ -105,7 +105,7 @@ QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
 /* Workspace bytes a call of kind `op` (QPN_OP_*) with these sizes uses for
  * its preferred launch plan: 0 when that plan does not split K (the GEMMs
  * then accept a NULL workspace), else room for per-split FP32 partial tiles
- * and per-panel-group counters; the lm_head needs at least 8 * m * 64
+ * and per-panel-group counters; the lm_head needs at least 8 * m * 256
  * bytes for its argmax keys plus any split-K room.  A call
  * given less workspace than this still runs, with fewer K splits, as long as
  * the fewest splits whose activation slice (m * K / splits FP16 values) fits
@@ -222,7 +222,7 @@ QPN_API int qpn_gemm_prefill_fp8(const void *packed, const uint16_t *x, uint16_t
  * qpn_gemm_nvfp4 and, per row m, argmax[m] = the lowest index n whose FP16
  * logit equals the row maximum (values compared as numbers: -0 == +0).
  * n >= 1 is required.  workspace: zero-filled device memory of at least
- * 8 * m * 64 bytes (qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4, m, n, k) for
+ * 8 * m * 256 bytes (qpn_workspace_bytes(QPN_OP_LMHEAD_NVFP4, m, n, k) for
  * the preferred plan).  Two kernels on `stream`. */
 QPN_API int qpn_lmhead_nvfp4(const void *packed, const uint16_t *x, uint16_t *logits,
                      int32_t *argmax, int m, int64_t n, int64_t k,

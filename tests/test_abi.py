@@ -135,8 +135,8 @@ def test_workspace_sizes(qpn):
         assert qpn.workspace_bytes(op, m, n, k) == _split_ws(qpn.gemm_plan(op, m, n, k))
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 1, 17408, 5120) == 0
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 5120, 17408) > 0   # K is split
-    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 8, 151936, 5120) == 8 * 8 * 64
-    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 1, 17, 16) == 8 * 64
+    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 8, 151936, 5120) == 8 * 8 * 256
+    assert qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, 1, 17, 16) == 8 * 256
     assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 0, 16, 16) == 0
     big = ctypes.c_size_t(-1).value
     assert qpn.workspace_bytes(99, 1, 16, 16) == big
@@ -187,8 +187,8 @@ def test_lmhead_argument_errors(qpn):
     assert call(n=0) == 2
     assert call(am=A16 + 2) == 3
     assert call(ws=A16 + 4) == 3
-    assert call(wsb=8 * 1 * 64 - 1) == 4                      # workspace too small
-    assert call(m=8, n=160, wsb=8 * 8 * 64 - 8) == 4
+    assert call(wsb=8 * 1 * 256 - 1) == 4                      # workspace too small
+    assert call(m=8, n=160, wsb=8 * 8 * 256 - 8) == 4
     assert call(m=0) == 0
 
 
@@ -196,7 +196,7 @@ def test_lmhead_verify_argument_errors(qpn):
     L = qpn.lib
     v = ctypes.c_void_p
 
-    def call(dr=A16, res=A16, m=2, n=16, k=16, am=A16, ws=A16, wsb=8 * 8 * 64):
+    def call(dr=A16, res=A16, m=2, n=16, k=16, am=A16, ws=A16, wsb=8 * 8 * 256):
         return L.qpn_lmhead_verify_nvfp4(v(A256), v(A16), v(A16), v(am), v(dr), v(res), m, n, k,
                                          v(ws), wsb, None)
 
@@ -206,7 +206,7 @@ def test_lmhead_verify_argument_errors(qpn):
     assert call(dr=A16 + 1) == 3
     assert call(am=0) == 1                                    # the lm_head's own checks follow
     assert call(n=0) == 2
-    assert call(wsb=8 * 2 * 64 - 1) == 4
+    assert call(wsb=8 * 2 * 256 - 1) == 4
     assert call(m=0, dr=0, res=0) == 0                        # nothing to do
     assert call(m=9) == 2
 
