@@ -555,9 +555,9 @@ hipError_t launch_mb(const GemmArgs& a, const GemmLaunch& l) {
 // automatic choice never uses them.
 constexpr GemmPlan kPlans[] = {
     {0, 0, 0, 0, 0},          // 0: automatic
-    {4, 1, 4, 0, 256},        // 1
-    {3, 5, 4, 0, 256},        // 2
-    {4, 2, 10, 0, 256},       // 3
+    {4, 1, 4, 0, 128},        // 1
+    {3, 5, 4, 0, 192},        // 2
+    {4, 2, 10, 0, 192},       // 3
     {8, 1, 3, 2, 256},        // 4
     {4, 1, 4, 2, 256},        // 5
     {4, 1, 10, 0, 256},       // 6
@@ -565,8 +565,8 @@ constexpr GemmPlan kPlans[] = {
     {3, 5, 14, 0, 256},       // 8
     {4, 4, 10, 0, 256},       // 9
     {3, 4, 4, 2, 256},        // 10
-    {3, 5, 4, 0, 256, 1},     // 11: plan 2, VALU dot
-    {4, 1, 4, 0, 256, 1},     // 12: plan 1, VALU dot
+    {3, 5, 4, 0, 192, 1},     // 11: plan 2, VALU dot
+    {4, 1, 4, 0, 128, 1},     // 12: plan 1, VALU dot
     {2, 8, 4, 0, 256},        // 13
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
@@ -599,7 +599,11 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 // sweeps on MI355X (NVFP4 17408x5120 and 5120x17408, FP8 6144x5120, warm
 // clocks):
 //   m <= 2 (FP8: m <= 4): one panel per workgroup, its k-steps interleaved
-//     over the wavefronts; activations are a few KiB and cost little.  When
+//     over the wavefronts; activations are a few KiB and cost little.  K is
+//     split only until there are 128 workgroups: a split-K fix-up costs
+//     more than the CUs it would add (2048x2048 M=1: 128 workgroups 3.75 us
+//     against 256 with two splits 5.71 us; FP8 3072x5120 M=1: 5.9 against
+//     7.45 us).  When
 //     there are 1-3 panels per CU with a remainder (e.g. 320 panels), whole
 //     panels alone would leave some CUs with twice the bytes of others, so
 //     placement 2 splits only the remainder panels in K (8 wavefronts per
@@ -608,7 +612,12 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 //     all workgroups read the same lines, so the slice traffic must be cut:
 //     one workgroup per CU, each owning up to five panels (three wavefronts
 //     per panel) that share one staged slice.  FP8 at m > 4 does best with
-//     two panels per workgroup and a deep (10 k-step) prefetch.
+//     two panels per workgroup and a deep (10 k-step) prefetch.  Both aim
+//     at 192 workgroups rather than one per CU: spreading panels thinner
+//     to occupy all 256 CUs costs more slice staging than the extra CUs
+//     bring (17408x5120 M=8: 218 workgroups of 5 panels 13.9 us against 256
+//     of ~4.25 panels 14.8 us; FP8 1792x5120 M=8: 224 workgroups, 2 splits,
+//     8.4 us against 336 workgroups, 3 splits, 10.7 us).
 //   NVFP4 m >= 2 with many panels (lm_head-sized N): eight panels per
 //     workgroup with two wavefronts each stage the slice once for 8 panels
 //     instead of 5 (a third less slice traffic).  It is used when the
