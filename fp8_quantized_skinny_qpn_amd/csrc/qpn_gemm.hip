@@ -634,16 +634,30 @@ double round_fill(int64_t workgroups) {  // average / largest workgroups per CU
 }  // namespace
 
 int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
-  (void)k;
   const int64_t P = panels_of(n);
-  const bool uneven = P >= 256 && P < 3 * 256 && P % 256 >= 16;
+  // The remainder split pays off over a long K (at least 64 k-steps): at 136
+  // k-steps (NVFP4 5120x17408 M=1) it saves 1.3 us.  Over a short K it pays
+  // off only with two or more panels per CU, where the remainder is a small
+  // share, and then with four wavefronts per panel (NVFP4 10240x5120 M=1:
+  // 7.9 against 8.4-8.5 us); with ~1.25 panels per CU its fix-up cost more
+  // than the balance gained (FP8 5120x1280 M=4: 6.05 against 4.80 us with
+  // whole panels; NVFP4 5120x5120 M=1: 7.1 against 6.2).
+  const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
+  const bool remainder = P >= 256 && P < 3 * 256 && P % 256 >= 16;
+  const bool uneven = remainder && J >= 64;
+  const bool uneven_short = remainder && J < 64 && P >= 2 * 256;
+  // fewer panels than CUs: one panel per workgroup at any m (the slice of a
+  // few panels is cheap to stage, and sharing it costs parallelism):
+  // 2048x2048 M=8 4.8 us against 7.7 us with five-panel workgroups,
+  // NVFP4 1792x5120 M=4 6.6 against 8.2 us, FP8 1792x5120 M=8 7.4 against 8.4
+  if (P < 256) return 1;
   if (fmt == kFmtNvfp4) {
     if (m >= 2 && P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02)
       return 13;
-    if (m <= 2) return uneven ? 4 : 1;
+    if (m <= 2) return uneven ? 4 : uneven_short ? 5 : 1;
     return 2;
   }
-  if (m <= 4) return uneven ? 5 : 1;
+  if (m <= 4) return uneven || uneven_short ? 5 : 1;
   return 3;
 }
 
