@@ -280,8 +280,9 @@ QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
                          uint16_t *out, void *stream);
 
 /* Diagnostic: forces the launch plan (wavefronts per panel, panels per
- * workgroup, prefetch depth, contraction; ids 1..12, where 11 and 12 repeat
- * 2 and 1 with VALU dot products in place of the MFMA) of every later GEMM and lm_head call
+ * workgroup, prefetch depth, contraction; ids 1..13, where 11 and 12 repeat
+ * 2 and 1 with VALU dot products in place of the MFMA and 13 is the
+ * eight-panel plan of large-N calls) of every later GEMM and lm_head call
  * in this process, for A/B timing of configurations on identical inputs.
  * 0 restores the automatic choice.  Returns QPN_ERR_SHAPE for an unknown id
  * (nothing changes).  Not for concurrent use with other calls. */
