@@ -118,6 +118,11 @@ size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
     if (m < 0 || m > kMaxPrefillM) return (size_t)-1;
     if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return (size_t)-1;
     if (m == 0 || n == 0) return 0;
+    if (m <= kPrefillSkinnyRows) {
+      GemmLaunch g;
+      if (gemm_launch_for(fmt, m, n, k, 0, (size_t)-1, 0, &g) != kGemmLaunchOk) return (size_t)-1;
+      return g.splits > 1 ? g.ws_needed : 0;
+    }
     PrefillLaunch l;
     if (prefill_launch_for(fmt, m, n, k, (size_t)-1, &l) != kGemmLaunchOk) return (size_t)-1;
     return l.ws_needed;
@@ -153,6 +158,20 @@ int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int*
     const uint32_t fmt = op == QPN_OP_PREFILL_NVFP4 ? kFmtNvfp4 : kFmtFp8;
     if (m < 0 || m > kMaxPrefillM) return QPN_ERR_SHAPE;
     if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
+    if (m <= kPrefillSkinnyRows) {  // the skinny kernel's plan (given the workspace asked for)
+      GemmLaunch g;
+      if (gemm_launch_for(fmt, m > 0 ? m : 1, n, k, 0, (size_t)-1, 0, &g) != kGemmLaunchOk)
+        return QPN_ERR_SHAPE;
+      if (workgroups) *workgroups = g.workgroups;
+      if (waves_per_panel) *waves_per_panel = g.waves_per_panel;
+      if (panels_per_workgroup) *panels_per_workgroup = g.panels_per_workgroup;
+      if (prefetch_depth) *prefetch_depth = g.depth;
+      if (splits) *splits = g.splits;
+      if (activation_rows) *activation_rows = gemm_activation_rows(m > 0 ? m : 1);
+      if (split_workgroups) *split_workgroups = g.split_wgs;
+      if (valu_dot) *valu_dot = g.valu_dot;
+      return QPN_OK;
+    }
     PrefillLaunch l;
     if (prefill_launch_for(fmt, m > 0 ? m : 1, n, k, (size_t)-1, &l) != kGemmLaunchOk)
       return QPN_ERR_SHAPE;
@@ -253,10 +272,17 @@ int prefill_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t*
   if (workspace && !aligned(workspace, 16)) return QPN_ERR_ALIGN;
   int rc = device_check();
   if (rc != QPN_OK) return rc;
+  GemmArgs a{packed, x, y, m, n, k, nullptr, workspace, stream};
+  if (m <= kPrefillSkinnyRows) {
+    // the skinny kernel with a 16-row tile, when the workspace holds the K
+    // splits it needs; otherwise the tiled kernel below (which runs with any)
+    GemmLaunch g;
+    if (gemm_launch_for(fmt, m, n, k, 0, workspace ? workspace_bytes : 0, 0, &g) == kGemmLaunchOk)
+      return launch_status(launch_gemm(fmt, false, a, g));
+  }
   PrefillLaunch l;
   if (prefill_launch_for(fmt, m, n, k, workspace ? workspace_bytes : 0, &l) != kGemmLaunchOk)
     return QPN_ERR_BUFFER;
-  GemmArgs a{packed, x, y, m, n, k, nullptr, workspace, stream};
   return launch_status(launch_prefill(fmt, a, l));
 }
 

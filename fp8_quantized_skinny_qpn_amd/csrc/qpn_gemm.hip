@@ -148,14 +148,18 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
   // Order of a k-step's activation units in LDS.  Unit xunit(t, kg, mm)
   // feeds MFMA t of lane (mm, kg), i.e. X[mm][kg * KS / 4 + 8 t, + 8).  The
   // plain order (t, kg, mm) makes one 64-lane staging load cover whole
-  // 128-byte lines of every row except for NVFP4 at 8 rows, where it would
+  // 128-byte lines of every row up to 4 rows.  For NVFP4 at 8 rows it would
   // take half of 16 lines (each line then read by two loads); there the
   // order (kg / 2, t, kg % 2, mm) gives each load the first or second 64 K
-  // of the k-step, one whole line per row.
-  constexpr bool XLINE = FMT == kFmtNvfp4 && MB == 8;
-  constexpr int XT = XLINE ? 2 * MB : 4 * MB;  // units between MFMA t and t + 1
+  // of the k-step, one whole line per row.  At 16 rows the order
+  // (kg, t, mm) gives each load 64 contiguous bytes of every row.
+  constexpr int XORD = FMT == kFmtNvfp4 && MB == 8 ? 1 : MB == 16 ? 2 : 0;
+  constexpr bool XLINE = XORD != 0;
+  constexpr int XT = XORD == 1 ? 2 * MB : XORD == 2 ? MB : 4 * MB;  // units between MFMA t and t + 1
   auto xunit = [](int t, int kg, int mm) {
-    return XLINE ? (((kg >> 1) * GR + t) * 2 + (kg & 1)) * MB + mm : (t * 4 + kg) * MB + mm;
+    return XORD == 1   ? (((kg >> 1) * GR + t) * 2 + (kg & 1)) * MB + mm
+           : XORD == 2 ? (kg * GR + t) * MB + mm
+                       : (t * 4 + kg) * MB + mm;
   };
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -254,10 +258,14 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
       const int mm = u % MB;
       const int rest = u / MB;
       int kpos;
-      if constexpr (XLINE) {
+      if constexpr (XORD == 1) {
         const int jl = u / XSTEP;
         const int r = rest % (XSTEP / MB);
         kpos = (j0 + jl) * KS + (2 * (r / (2 * GR)) + (r & 1)) * (KS / 4) + 8 * ((r / 2) % GR);
+      } else if constexpr (XORD == 2) {
+        const int jl = u / XSTEP;
+        const int r = rest % (XSTEP / MB);
+        kpos = (j0 + jl) * KS + (r / GR) * (KS / 4) + 8 * (r % GR);
       } else {
         const int jl = rest / (4 * GR);
         kpos = (j0 + jl) * KS + (rest % 4) * (KS / 4) + 8 * ((rest / 4) % GR);
@@ -546,7 +554,10 @@ hipError_t launch_mb(const GemmArgs& a, const GemmLaunch& l) {
     case 1: return launch_t<FMT, W, G, D, 1, ARGMAX, VDOT>(a, l);
     case 2: return launch_t<FMT, W, G, D, 2, ARGMAX, VDOT>(a, l);
     case 4: return launch_t<FMT, W, G, D, 4, ARGMAX, VDOT>(a, l);
-    default: return launch_t<FMT, W, G, D, 8, ARGMAX, VDOT>(a, l);
+    case 8: return launch_t<FMT, W, G, D, 8, ARGMAX, VDOT>(a, l);
+    default:  // 16 rows: prefill-sized calls of 9..16 rows, never the lm_head
+      if constexpr (ARGMAX) return hipErrorInvalidValue;
+      else return launch_t<FMT, W, G, D, 16, false, VDOT>(a, l);
   }
 }
 
@@ -593,7 +604,7 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
 
 }  // namespace
 
-int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
+int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16; }
 
 // Automatic plan: a pure function of (format, m, n, k).  From kernel-duration
 // sweeps on MI355X (NVFP4 17408x5120 and 5120x17408, FP8 6144x5120, warm

@@ -88,7 +88,12 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 
 // Prefill-sized activation blocks (9 <= m <= 256): one launch of the tiled
 // MFMA kernel, 128 output channels by 32 mt activation rows per workgroup.
+// Calls of up to kPrefillSkinnyRows rows run the skinny kernel instead, with
+// a 16-row activation tile that fills the MFMA's B operand exactly (the
+// weights stream once, as at m <= 8), unless the workspace given is too
+// small for the K splits its LDS budget needs.
 constexpr int kMaxPrefillM = 256;
+constexpr int kPrefillSkinnyRows = 16;
 struct PrefillLaunch {
   int mt;               // 16-row activation tiles per wavefront (workgroup rows = 32 mt)
   int depth;            // k-steps of weight loads in flight per wavefront

@@ -202,8 +202,11 @@ QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int
  * phase that the old card loses).  The same product as qpn_gemm_nvfp4 /
  * qpn_gemm_fp8 for 0 <= m <= 256 activation rows: Y[m, n] = FP16_RNE(scale *
  * sum_k X[m, k] * W[n, k]), FP32 accumulation, weights decoded in registers,
- * no dequantised copy.  Meant for m > 8 (for m <= 8 the skinny entry points
- * are faster).  x: [m, k] FP16, 16-byte aligned; y: [m, n] FP16.
+ * no dequantised copy.  Up to 16 rows it runs the skinny kernel of
+ * qpn_gemm_nvfp4 / qpn_gemm_fp8 with a 16-row activation tile (the weights
+ * stream once); from 17 rows, or when the workspace given cannot hold the K
+ * splits the skinny kernel needs, a tiled MFMA kernel.  Both reach the same
+ * parity bar.  x: [m, k] FP16, 16-byte aligned; y: [m, n] FP16.
  * workspace: zero-filled device memory, 16-byte aligned, of
  * qpn_workspace_bytes(QPN_OP_PREFILL_*, m, n, k) bytes for the preferred K
  * split (NULL with 0 bytes is valid and runs without splitting K); every

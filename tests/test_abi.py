@@ -233,9 +233,18 @@ def test_requant_argument_errors(qpn):
 
 def test_prefill_queries(qpn):
     for op in (qpn.OP_PREFILL_NVFP4, qpn.OP_PREFILL_FP8):
-        for m, n, k in [(9, 17408, 5120), (64, 5120, 17408), (256, 17408, 5120), (256, 5120, 17408),
-                        (130, 200, 1024), (1, 16, 64), (256, 6144, 5120)]:
+        for m, n, k in [(9, 17408, 5120), (16, 5120, 17408), (17, 17408, 5120), (64, 5120, 17408),
+                        (256, 17408, 5120), (256, 5120, 17408), (130, 200, 1024), (1, 16, 64),
+                        (256, 6144, 5120)]:
             pl = qpn.gemm_plan(op, m, n, k)
+            ws = qpn.workspace_bytes(op, m, n, k)
+            if m <= 16:
+                # up to 16 rows run the skinny kernel (a 16-row tile above 8 rows)
+                assert pl.activation_rows in (1, 2, 4, 8, 16)
+                assert m <= pl.activation_rows < 2 * max(m, 1)
+                assert pl.split_workgroups % pl.splits == 0 and pl.split_workgroups <= pl.workgroups
+                assert (ws == 0) == (pl.splits == 1)
+                continue
             ks = 128 if op == qpn.OP_PREFILL_NVFP4 else 64
             J = -(-k // ks)
             blocks = -(-n // 128)
@@ -246,7 +255,6 @@ def test_prefill_queries(qpn):
             # every split has at least one k-step and together they cover K
             steps = -(-J // pl.splits)
             assert (pl.splits - 1) * steps < J <= pl.splits * steps
-            ws = qpn.workspace_bytes(op, m, n, k)
             assert (ws == 0) == (pl.splits == 1)
             if pl.splits > 1:   # counters, then S partial tiles of 128 x rows FP32 per block
                 cnt = -(-blocks * 4 // 256) * 256

@@ -1,5 +1,9 @@
 """Prefill-sized activation blocks (9 <= m <= 256) against the oracle.
 
+Up to 16 rows the call runs the skinny kernel with a 16-row activation tile
+(the tiled kernel when no workspace is given and K needs splitting); from 17
+rows the tiled MFMA kernel.  Both paths are covered below.
+
 The same parity bar as the skinny GEMM: per element |err| <= 1e-2 rms(ref)
 + 1e-3 and relative Frobenius error <= 2e-3 against the FP64 oracle product
 of the canonical codes.  Shapes span several 128-channel blocks, ragged N
@@ -16,7 +20,7 @@ from gpu_util import dev, host, log, need_gpu, parity
 
 pytestmark = pytest.mark.gpu
 
-MS = (9, 16, 31, 33, 64, 100, 128, 129, 200, 256)
+MS = (9, 12, 16, 17, 31, 33, 64, 100, 128, 129, 200, 256)
 
 
 def _prefill_one_range(qpn, pw, xd):
