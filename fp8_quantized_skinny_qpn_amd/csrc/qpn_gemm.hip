@@ -567,7 +567,7 @@ hipError_t launch_mb(const GemmArgs& a, const GemmLaunch& l) {
 constexpr GemmPlan kPlans[] = {
     {0, 0, 0, 0, 0},          // 0: automatic
     {4, 1, 4, 0, 128},        // 1
-    {3, 5, 4, 0, 192},        // 2
+    {3, 5, 3, 0, 192},        // 2
     {4, 2, 10, 0, 192},       // 3
     {8, 1, 3, 2, 256},        // 4
     {4, 1, 4, 2, 256},        // 5
@@ -576,7 +576,7 @@ constexpr GemmPlan kPlans[] = {
     {3, 5, 14, 0, 256},       // 8
     {4, 4, 10, 0, 256},       // 9
     {3, 4, 4, 2, 256},        // 10
-    {3, 5, 4, 0, 192, 1},     // 11: plan 2, VALU dot
+    {3, 5, 3, 0, 192, 1},     // 11: plan 2, VALU dot
     {4, 1, 4, 0, 128, 1},     // 12: plan 1, VALU dot
     {2, 8, 4, 0, 256},        // 13
 };
@@ -586,7 +586,7 @@ template <uint32_t FMT, bool ARGMAX>
 hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
   switch (l.plan) {
     case 1: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
-    case 2: return launch_mb<FMT, 3, 5, 4, ARGMAX>(a, l);
+    case 2: return launch_mb<FMT, 3, 5, 3, ARGMAX>(a, l);
     case 3: return launch_mb<FMT, 4, 2, 10, ARGMAX>(a, l);
     case 4: return launch_mb<FMT, 8, 1, 3, ARGMAX>(a, l);
     case 5: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
@@ -595,7 +595,7 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
     case 8: return launch_mb<FMT, 3, 5, 14, ARGMAX>(a, l);
     case 9: return launch_mb<FMT, 4, 4, 10, ARGMAX>(a, l);
     case 10: return launch_mb<FMT, 3, 4, 4, ARGMAX>(a, l);
-    case 11: return launch_mb<FMT, 3, 5, 4, ARGMAX, true>(a, l);
+    case 11: return launch_mb<FMT, 3, 5, 3, ARGMAX, true>(a, l);
     case 12: return launch_mb<FMT, 4, 1, 4, ARGMAX, true>(a, l);
     case 13: return launch_mb<FMT, 2, 8, 4, ARGMAX>(a, l);
     default: return hipErrorInvalidValue;
@@ -622,7 +622,8 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 //   m > 2: every workgroup reads all of its activation slice from L2, and
 //     all workgroups read the same lines, so the slice traffic must be cut:
 //     one workgroup per CU, each owning up to five panels (three wavefronts
-//     per panel) that share one staged slice.  FP8 at m > 4 does best with
+//     per panel, three k-steps in flight each: 0.2-0.4 us faster than four
+//     on every 5-panel headline call) that share one staged slice.  FP8 at m > 4 does best with
 //     two panels per workgroup and a deep (10 k-step) prefetch.  Both aim
 //     at 192 workgroups rather than one per CU: spreading panels thinner
 //     to occupy all 256 CUs costs more slice staging than the extra CUs
