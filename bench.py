@@ -29,6 +29,7 @@ until about ten seconds of CPU time have been spent.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
     python bench.py --traffic-workload | --contraction-ab | --prefill-workload   (profiling)
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV   (profiles/traffic.json from the PMC passes)
+    python bench.py --summarize-sq AB_CSV AB_JSON HEAD_CSV BENCH_JSON   (SQ counter tables)
 """
 import argparse
 import hashlib
@@ -334,6 +335,48 @@ def summarize_traffic(fetch_csv, write_csv):
     print("\n".join(lines))
 
 
+SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES")
+
+
+def summarize_sq(counter_csv, rows):
+    """Per-call SQ counter averages from a rocprofv3 PMC pass: the GEMM
+    dispatches form one contiguous run per row of `rows` (call, kernel, us),
+    in order; counters are averaged over a run's dispatches.  Busy fractions
+    use the row's time at the 2.4 GHz engine clock: VALU busy =
+    SQ_ACTIVE_INST_VALU / (256 CUs x cycles), MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles).  Returns markdown lines."""
+    import csv
+    per = {}
+    with open(counter_csv) as fh:
+        for r in csv.DictReader(fh):
+            d = per.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    runs = []
+    for did in sorted(per):
+        d = per[did]
+        if "skinny_gemm_kernel" not in d["kernel"]:
+            continue
+        if runs and runs[-1][0] == d["kernel"]:
+            runs[-1][1].append(d)
+        else:
+            runs.append((d["kernel"], [d]))
+    if len(runs) != len(rows):
+        raise SystemExit(f"{len(runs)} GEMM dispatch runs for {len(rows)} calls")
+    out = ["| call | contraction | kernel | us | VALU insts / launch | MFMA insts / launch | VALU busy % | MFMA busy % |",
+           "|---|---|---|---:|---:|---:|---:|---:|"]
+    for (kname, ds), row in zip(runs, rows):
+        short = kname.split("(")[0].replace("void ", "")
+        if short != row["kernel"]:
+            raise SystemExit(f"dispatch run {short} does not match {row['kernel']}")
+        avg = {c: float(np.mean([d.get(c, 0.0) for d in ds])) for c in SQ_COUNTERS}
+        cycles = row["us"] * 1e-6 * 2.4e9
+        out.append(f"| {row['call']} | {row.get('contraction', 'mfma')} | `{short}` | {row['us']:.2f} | "
+                   f"{avg['SQ_INSTS_VALU']:,.0f} | {avg['SQ_INSTS_MFMA']:,.0f} | "
+                   f"{100 * avg['SQ_ACTIVE_INST_VALU'] / (256 * cycles):.1f} | "
+                   f"{100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cycles):.1f} |")
+    return out
+
+
 # The contraction A/B: plans 1 and 2 (MFMA) against plans 12 and 11, the same
 # launch shapes contracting with VALU dot products instead.
 CONTRACTION_AB = ((1, 1, 12), (8, 2, 11))  # (M, MFMA plan, VALU-dot plan)
@@ -393,6 +436,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two PMC passes of --traffic-workload")
+    ap.add_argument("--summarize-sq", nargs=4, metavar=("AB_CSV", "AB_JSON", "HEAD_CSV", "BENCH_JSON"),
+                    help="SQ counter tables from the PMC passes of --contraction-ab and "
+                         "--traffic-workload and the JSON lines of --contraction-ab and bench.py")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
     ap.add_argument("--prefill-workload", action="store_true",
@@ -403,6 +449,14 @@ def main():
 
     if args.summarize_traffic:  # host only: post-processes rocprofv3 output
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_sq:  # host only: post-processes rocprofv3 output
+        ab_csv, ab_json, head_csv, bench_json = args.summarize_sq
+        ab = json.loads(open(ab_json).read().strip().splitlines()[-1])["contraction_ab"]
+        bl = json.loads(open(bench_json).read().strip().splitlines()[-1])["breakdown"]
+        head = [{"call": c, "kernel": v["kernel"], "us": v["us"]} for c, v in bl.items()]
+        print("\n".join(["MFMA against VALU dot:"] + summarize_sq(ab_csv, ab) +
+                        ["", "Headline calls:"] + summarize_sq(head_csv, head)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}): the QPN skinny "
