@@ -568,7 +568,7 @@ constexpr GemmPlan kPlans[] = {
     {0, 0, 0, 0, 0},          // 0: automatic
     {4, 1, 4, 0, 128},        // 1
     {3, 5, 3, 0, 192},        // 2
-    {4, 2, 10, 0, 192},       // 3
+    {4, 2, 6, 0, 192},        // 3
     {8, 1, 3, 2, 256},        // 4
     {4, 1, 4, 2, 256},        // 5
     {4, 1, 10, 0, 256},       // 6
@@ -587,7 +587,7 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
   switch (l.plan) {
     case 1: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
     case 2: return launch_mb<FMT, 3, 5, 3, ARGMAX>(a, l);
-    case 3: return launch_mb<FMT, 4, 2, 10, ARGMAX>(a, l);
+    case 3: return launch_mb<FMT, 4, 2, 6, ARGMAX>(a, l);
     case 4: return launch_mb<FMT, 8, 1, 3, ARGMAX>(a, l);
     case 5: return launch_mb<FMT, 4, 1, 4, ARGMAX>(a, l);
     case 6: return launch_mb<FMT, 4, 1, 10, ARGMAX>(a, l);
@@ -624,7 +624,8 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 //     one workgroup per CU, each owning up to five panels (three wavefronts
 //     per panel, three k-steps in flight each: 0.2-0.4 us faster than four
 //     on every 5-panel headline call) that share one staged slice.  FP8 at m > 4 does best with
-//     two panels per workgroup and a deep (10 k-step) prefetch.  Both aim
+//     two panels per workgroup and a six k-step prefetch (0.35-0.4 us
+//     faster than ten at 5120-7168x5120 M=8).  Both aim
 //     at 192 workgroups rather than one per CU: spreading panels thinner
 //     to occupy all 256 CUs costs more slice staging than the extra CUs
 //     bring (17408x5120 M=8: 218 workgroups of 5 panels 13.9 us against 256
