@@ -57,6 +57,24 @@ def test_prefill_small(fmt, n, k):
         parity(host(_prefill_one_range(qpn, pw, xd)), y_ref, f"prefill {fmt} {n}x{k} m={m} one K range")
 
 
+@pytest.mark.parametrize("fmt,n,k,ppw,splits", [("nvfp4", 4100, 1280, 5, 1), ("nvfp4", 4100, 3328, 5, 2),
+                                               ("fp8", 4100, 3328, 2, 2), ("nvfp4", 65536, 256, 8, 1)])
+def test_prefill_16_rows_multi_panel(fmt, n, k, ppw, splits):
+    """9-16 rows through the skinny kernel's shared-slice plans (five and
+    eight NVFP4 panels or two FP8 panels per workgroup, the 16-row staging
+    order, with and without K splits), ragged N, every output checked."""
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=n + 3 * k)
+    x = synth.activations(16, k, seed=n + 3 * k, m_max=16)
+    pw, ref = _pack(qpn, fmt, w)
+    op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+    for m in (9, 16):
+        pl = qpn.gemm_plan(op, m, n, k)
+        assert (pl.activation_rows, pl.panels_per_workgroup, pl.splits) == (16, ppw, splits)
+        log(f"prefill 16-row tile {fmt} {n}x{k} m={m}: {pl.workgroups} workgroups")
+        parity(host(qpn.prefill(pw, dev(x[:m]))), ref(x[:m]), f"prefill {fmt} {n}x{k} m={m} (16-row tile)")
+
+
 @pytest.mark.parametrize("fmt,n,k", [("nvfp4", 17408, 5120), ("nvfp4", 5120, 17408),
                                      ("fp8", 6144, 5120), ("fp8", 7168, 5120)])
 def test_prefill_full_size_sampled(fmt, n, k):
