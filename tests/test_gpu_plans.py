@@ -1,0 +1,82 @@
+"""Every branch of the automatic launch-plan choice, on a shape that selects
+it, against the oracle (every output element).
+
+The branches: one panel per workgroup below 256 panels at any m; the
+remainder split (256 to 767 panels with a remainder of 16 or more) over a
+long K (64 or more k-steps; eight wavefronts per panel for NVFP4, four for
+FP8) and over a short K with 512 or more panels (four wavefronts); whole
+panels for a short K below 512 panels; five NVFP4 panels or two FP8 panels
+per workgroup above 2 (NVFP4) or 4 (FP8) rows; eight NVFP4 panels per
+workgroup for 2048 or more panels when they fill whole rounds of 256 CUs.
+The plan fields reported through the C ABI are asserted first, so each case
+covers the branch it names.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_quantized_skinny_qpn_amd import synth
+from gpu_util import dev, host, log, need_gpu, parity
+
+pytestmark = pytest.mark.gpu
+
+# (fmt, n, k, m, waves_per_panel, panels_per_workgroup, whole-panel workgroups present, branch)
+CASES = [
+    ("nvfp4", 2000, 1024, 1, 4, 1, False, "one panel per workgroup, < 256 panels"),
+    ("nvfp4", 2000, 1024, 8, 4, 1, False, "one panel per workgroup, < 256 panels, 8 rows"),
+    ("fp8", 2000, 1024, 8, 4, 1, False, "one panel per workgroup, < 256 panels, FP8 8 rows"),
+    ("nvfp4", 5120, 8192, 1, 8, 1, True, "remainder split, long K, NVFP4"),
+    ("nvfp4", 5120, 8192, 2, 8, 1, True, "remainder split, long K, NVFP4, 2 rows"),
+    ("fp8", 5120, 4096, 3, 4, 1, True, "remainder split, long K, FP8"),
+    ("nvfp4", 8704, 2048, 1, 4, 1, True, "remainder split, short K, >= 512 panels"),
+    ("nvfp4", 5120, 2048, 1, 4, 1, False, "whole panels, short K, < 512 panels"),
+    ("nvfp4", 4100, 2048, 5, 3, 5, False, "five panels per workgroup"),
+    ("fp8", 4100, 2048, 6, 4, 2, False, "two FP8 panels per workgroup"),
+    ("nvfp4", 32768, 512, 2, 2, 8, False, "eight panels per workgroup, 2 rows"),
+    ("nvfp4", 32768, 512, 8, 2, 8, False, "eight panels per workgroup, 8 rows"),
+]
+
+
+def _pack(qpn, fmt, w):
+    if fmt == "nvfp4":
+        codes, scales, g = oracle.pack_nvfp4(w)
+        return qpn.pack_nvfp4(dev(w)), lambda x: oracle.gemm_nvfp4(codes, scales, g, x)
+    codes, rs = oracle.pack_fp8(w)
+    return qpn.pack_fp8(dev(w)), lambda x: oracle.gemm_fp8(codes, rs, x)
+
+
+@pytest.mark.parametrize("fmt,n,k,m,wpp,ppw,whole,branch", CASES, ids=[c[-1] for c in CASES])
+def test_automatic_plan_branch(fmt, n, k, m, wpp, ppw, whole, branch):
+    qpn = need_gpu()
+    op = qpn.OP_GEMM_NVFP4 if fmt == "nvfp4" else qpn.OP_GEMM_FP8
+    pl = qpn.gemm_plan(op, m, n, k)
+    assert (pl.waves_per_panel, pl.panels_per_workgroup) == (wpp, ppw), (branch, pl)
+    assert (pl.workgroups > pl.split_workgroups) == whole, (branch, pl)
+    w = synth.weights(n, k, seed=n + k + m)
+    x = synth.activations(m, k, seed=n + k + m)
+    pw, ref = _pack(qpn, fmt, w)
+    log(f"plan branch '{branch}': {fmt} {n}x{k} m={m}, {pl.workgroups} workgroups, {pl.splits} splits")
+    parity(host(qpn.gemm(pw, dev(x))), ref(x), f"{branch}: {fmt} {n}x{k} m={m}")
+
+
+def test_lmhead_eight_panel_plan():
+    """The lm_head (argmax fused) through the eight-panel plan: logits within
+    the parity bar and the argmax equal to the argmax of the returned
+    logits and to the oracle's on rows whose top two logits are apart."""
+    qpn = need_gpu()
+    n, k, m = 32768, 512, 8
+    pl = qpn.gemm_plan(qpn.OP_LMHEAD_NVFP4, m, n, k)
+    assert (pl.waves_per_panel, pl.panels_per_workgroup) == (2, 8)
+    w = synth.weights(n, k, seed=11)
+    x = synth.activations(m, k, seed=11)
+    pw, ref = _pack(qpn, "nvfp4", w)
+    lg, am = qpn.lmhead_nvfp4(pw, dev(x))
+    lg, am = host(lg), host(am)
+    y_ref = ref(x)
+    parity(lg, y_ref, "lm_head eight-panel plan")
+    assert np.array_equal(am, np.argmax(lg, axis=1))
+    ref_am = oracle.argmax_f16(oracle.round_f16(y_ref))
+    srt = np.sort(y_ref, axis=1)
+    apart = (srt[:, -1] - srt[:, -2]) > 1e-2
+    assert apart.sum() >= m // 2
+    assert np.array_equal(am[apart], ref_am[apart])
