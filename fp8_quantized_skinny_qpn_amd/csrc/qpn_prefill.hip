@@ -372,8 +372,8 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
 
 int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; }
 
-// K splits.  With 32 or 64 rows the call is HBM-bound: enough workgroups for
-// every CU, and few splits (their partial tiles are extra traffic).  With
+// K splits.  With 32 or 64 rows the call is HBM-bound: up to 200 workgroups
+// (not one per CU: each split adds a fix-up and partial-tile traffic).  With
 // 128 or 256 rows the matrix unit bounds it and one workgroup fills a CU
 // (its slice stages take 128 KiB of LDS): the split count minimises whole
 // waves of 256 workgroups times k-steps per workgroup (about 0.107 us of
@@ -393,7 +393,12 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   };
   int64_t S = 1;
   if (blocks > 0 && mt <= 2) {
-    S = std::min<int64_t>((256 + blocks - 1) / blocks, smax);
+    // HBM-bound: the most K splits that keep at most 200 workgroups.  Filling
+    // every CU with more splits cost more in split-K fix-ups than the CUs
+    // brought: at m = 64, 17408x5120 went from 62 to 43.6 us (one split, 136
+    // workgroups), 5120x17408 from 65.4 to 47.5 us (five splits, 200) and
+    // FP8 6144x5120 from 41.2 to 30.3 us (four splits, 192).
+    S = std::min<int64_t>(std::max<int64_t>(1, 200 / blocks), smax);
   } else if (blocks > 0) {
     double best = 0.0;
     for (int64_t s = 1; s <= std::min<int64_t>(smax, 16); ++s) {
