@@ -377,8 +377,8 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 // 128 or 256 rows the matrix unit bounds it and one workgroup fills a CU
 // (its slice stages take 128 KiB of LDS): the split count minimises whole
 // waves of 256 workgroups times k-steps per workgroup (about 0.107 us of
-// MFMA work per activation tile and k-step) plus the partial tiles'
-// write-and-read traffic at ~5 TB/s.
+// MFMA work per activation tile and NVFP4 k-step, half that per FP8 k-step)
+// plus the partial tiles' write-and-read traffic at ~5 TB/s.
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out) {
   const int mt = prefill_tiles(m);
@@ -400,10 +400,15 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
     // FP8 6144x5120 from 41.2 to 30.3 us (four splits, 192).
     S = std::min<int64_t>(std::max<int64_t>(1, 200 / blocks), smax);
   } else if (blocks > 0) {
+    // MFMA time of one activation tile and k-step: an FP8 k-step is 64 K,
+    // half the work of an NVFP4 one (charging it the NVFP4 time chose five
+    // splits where four measured 83.6 against 90.3-91.1 us at FP8 6144x5120
+    // m = 256)
+    const double step_us = fmt == kFmtNvfp4 ? 0.107 : 0.0535;
     double best = 0.0;
     for (int64_t s = 1; s <= std::min<int64_t>(smax, 16); ++s) {
       const double waves = (double)((blocks * s + 255) / 256);
-      const double cost = waves * (double)((J + s - 1) / s) * 0.107 * mt +
+      const double cost = waves * (double)((J + s - 1) / s) * step_us * mt +
                           2.0 * (double)need(s) / 5e6;  // us
       if (s == 1 || cost < best) {
         best = cost;
