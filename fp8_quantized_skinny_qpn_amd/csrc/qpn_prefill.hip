@@ -426,7 +426,7 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   // the partial area is addressed with 32-bit offsets
   if (need(S) >= ((size_t)1 << 31)) return kGemmNoWorkspace;
   out->mt = mt;
-  out->depth = mt >= 4 ? 3 : 5;  // as compiled below
+  out->depth = 3;  // as compiled below
   out->blocks = blocks;
   out->splits = (int)S;
   out->split_steps = (int)steps;
@@ -455,8 +455,10 @@ hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
 template <uint32_t FMT>
 hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
   switch (l.mt) {
-    case 1: return launch_pf<FMT, 1, 5, 6>(a, l);
-    case 2: return launch_pf<FMT, 2, 5, 6>(a, l);
+    // up to 64 rows: 3 k-steps ahead in 4 slice stages measured 3-6% faster
+    // than 5 ahead in 6 stages at every 17-64-row decoder shape
+    case 1: return launch_pf<FMT, 1, 3, 4>(a, l);
+    case 2: return launch_pf<FMT, 2, 3, 4>(a, l);
     case 4: return launch_pf<FMT, 4, 3, 4>(a, l);
     default: return launch_pf<FMT, 8, 3, 2>(a, l);
   }
