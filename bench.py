@@ -16,6 +16,14 @@ host launch overhead stays out of the measurement; the graph holds exactly
 value = algorithmic weight bytes of one step (codes + UE4M3 scales + the
 4-byte tensor scale of each call) / wall time of one step, in GB/s (1e9 B/s).
 
+breakdown: each headline call's launch time (median, p10 and p90 over 15
+replays of a graph of 44 back-to-back launches), GB/s and % of 8 TB/s.
+configs: the metric's other configurations, timed the same way in every run
+and not part of `value`: NVFP4 2048x2048 at M=1; FP8 K=5120 -> N=6144 and
+N=5120 at M = 1, 2, 4; one decoder layer at M=8 (QKV and O FP8, gate/up and
+down NVFP4), each GEMM and the four back to back; the 151936-row NVFP4
+lm_head with its fused argmax at M = 1 and 8.
+
 roofline: the dominant kernel (largest share of the step).  Its average
 launch duration is timed with HIP events around a graph of back-to-back
 launches of that call (rotating copies) on the launch stream; achieved =
@@ -23,13 +31,15 @@ its algorithmic bytes per launch / that average.  traffic comes from the
 committed rocprofv3 PMC summary when it matches the current kernel source.
 
 cpu_baseline: the FP64 oracle (test infrastructure, C with OpenMP over rows)
-computing one complete headline step (all six calls, every row), repeated
-until about ten seconds of CPU time have been spent.
+computing complete headline steps (all six calls, every row) on every thread
+for about eight seconds, then a bounded one-thread sample; with the host CPU
+model.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
     python bench.py --traffic-workload | --contraction-ab | --prefill-workload   (profiling)
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV   (profiles/traffic.json from the PMC passes)
     python bench.py --summarize-sq AB_CSV AB_JSON HEAD_CSV BENCH_JSON   (SQ counter tables)
+    python bench.py --summarize-trace KERNEL_TRACE_CSV   (per-kernel median / p10 / p90 durations)
 """
 import argparse
 import hashlib
@@ -55,19 +65,26 @@ HEADLINE = [  # (name, n, k, format)
 ]
 HEADLINE_M = (1, 4, 8)
 
-EXTRA = [  # measured only with --extra (the other configurations' timings)
-    ("cfg1_K2048_N2048", 2048, 2048, "nvfp4", (1,)),
-    ("fp8_K5120_N6144", 6144, 5120, "fp8", (1, 2, 4, 8)),
-    ("fp8_K5120_N5120", 5120, 5120, "fp8", (1, 2, 4, 8)),
-    ("layer_qkv_fp8_K5120_N7168", 7168, 5120, "fp8", (8,)),
-    ("layer_gateup_nvfp4_K5120_N34816", 34816, 5120, "nvfp4", (8,)),
+# The other configurations of the metric, timed in every run and reported
+# under "configs" (the headline value is the NVFP4 step above):
+# the small NVFP4 GEMV, the FP8 skinny GEMMs, one decoder layer at M = 8 and
+# the lm_head with its fused argmax.
+CONFIGS = [
+    ("cfg1_nvfp4_K2048_N2048", 2048, 2048, "nvfp4", (1,)),
+    ("cfg3_fp8_K5120_N6144", 6144, 5120, "fp8", (1, 2, 4)),
+    ("cfg3_fp8_K5120_N5120", 5120, 5120, "fp8", (1, 2, 4)),
 ]
-LMHEAD = ("lmhead_nvfp4_K5120_N151936", 151936, 5120)
+LMHEAD = ("cfg5_lmhead_nvfp4_K5120_N151936", 151936, 5120)
 # One decoder layer's four projections at M = 8, back to back: QKV and O in
-# FP8, gate/up and down in NVFP4 (213,368,840 weight bytes per layer).
+# FP8, gate/up and down in NVFP4 (213,368,840 weight bytes per layer).  Each
+# GEMM draws its weights with its own seed (0, 1, 2, 3 in this order).
 LAYER = [("qkv_fp8_K5120_N7168", 7168, 5120, "fp8"), ("o_fp8_K5120_N5120", 5120, 5120, "fp8"),
          ("gateup_nvfp4_K5120_N34816", 34816, 5120, "nvfp4"),
          ("down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4")]
+EXTRA = [  # measured only with --extra
+    ("fp8_K5120_N6144", 6144, 5120, "fp8", (8,)),
+    ("fp8_K5120_N5120", 5120, 5120, "fp8", (8,)),
+]
 # The same layer with its FP8 projections converted to NVFP4 (all-FP4, the
 # derived-checkpoint variant: 0.5625 instead of 1 byte per QKV/O weight).
 LAYER_ALLFP4 = [("qkv_fp8>nvfp4_K5120_N7168", 7168, 5120, "fp8>nvfp4"),
@@ -165,9 +182,11 @@ def time_graph(torch, g, reps):
     return out
 
 
-def time_call(qpn, torch, s, m, batch=BATCH, reps=5):
-    """Average launch time (s) of one (shape, M) call in back-to-back graphs."""
-    g = capture(torch, lambda: [qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws) for _ in range(batch)])
+def time_call(qpn, torch, s, m, batch=BATCH, reps=15, plan=0):
+    """Average launch time (s) of one (shape, M) call in each of `reps`
+    replays of a graph of `batch` back-to-back launches (rotating copies)."""
+    g = capture(torch, lambda: [qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws, plan=plan)
+                                for _ in range(batch)])
     g.replay()
     torch.cuda.synchronize()
     per = [t / batch for t in time_graph(torch, g, reps)]
@@ -175,8 +194,38 @@ def time_call(qpn, torch, s, m, batch=BATCH, reps=5):
     return per
 
 
-def cpu_baseline(min_seconds=10.0):
-    """FP64 oracle computing whole headline steps (CPU leg only)."""
+def call_stats(per, nbytes):
+    """Per-call figures from per-replay averages: median, p10 and p90 (over
+    the replays), effective weight GB/s and % of 8 TB/s at the median."""
+    med = float(np.median(per))
+    return {"us": round(med * 1e6, 3),
+            "us_p10": round(float(np.percentile(per, 10)) * 1e6, 3),
+            "us_p90": round(float(np.percentile(per, 90)) * 1e6, 3),
+            "GBps": round(nbytes / med / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / med / 1e9 / HBM_PEAK_GBPS, 1),
+            "weight_bytes": nbytes}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# rows of each headline weight the 1-thread oracle sample computes
+CPU_1T_ROWS = 512
+
+
+def cpu_baseline(min_seconds=8.0):
+    """The FP64 oracle (test infrastructure, C, OpenMP over output rows):
+    complete headline steps on every thread of this process, repeated until
+    about min_seconds of wall time, then a bounded one-thread sample (the
+    first CPU_1T_ROWS output rows of each of the six headline calls, scaled
+    by their weight bytes)."""
     import oracle
     from fp8_quantized_skinny_qpn_amd import synth
     packed = []
@@ -185,6 +234,7 @@ def cpu_baseline(min_seconds=10.0):
         codes, scales, g = oracle.pack_nvfp4(w)
         del w
         packed.append((name, n, k, codes, scales, g, synth.activations(8, k, seed=0)))
+    threads = oracle.threads()
     steps, total_t = 0, 0.0
     while total_t < min_seconds or steps == 0:
         for name, n, k, codes, scales, g, x8 in packed:
@@ -194,13 +244,32 @@ def cpu_baseline(min_seconds=10.0):
                 total_t += time.perf_counter() - t
         steps += 1
     step_bytes = sum(algo_bytes(n, k, "nvfp4") for _, n, k, *_ in packed) * len(HEADLINE_M)
+    # one thread, a row sample of every call
+    oracle.set_threads(1)
+    t1, b1 = 0.0, 0
+    try:
+        for name, n, k, codes, scales, g, x8 in packed:
+            r = min(CPU_1T_ROWS, n)
+            c, sc = np.ascontiguousarray(codes[:r]), np.ascontiguousarray(scales[:r])
+            for m in HEADLINE_M:
+                t = time.perf_counter()
+                oracle.gemm_nvfp4(c, sc, g, x8[:m])
+                t1 += time.perf_counter() - t
+                b1 += r * k // 2 + r * k // 16
+    finally:
+        oracle.set_threads(threads)
     return {
         "value": round(step_bytes * steps / total_t / 1e9, 6),
         "unit": "GB/s",
-        "cores": oracle.threads(),
+        "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{steps} complete headline step(s) (6 calls, every row) on the FP64 oracle "
-                   f"(C, OpenMP over rows), {total_t:.1f} s of wall time; packing untimed"),
+                   f"(C, OpenMP over rows, {threads} threads), {total_t:.1f} s of wall time; "
+                   f"packing untimed"),
+        "value_1thread": round(b1 / t1 / 1e9, 6),
+        "sample_1thread": (f"the first {CPU_1T_ROWS} output rows of each of the 6 headline calls "
+                           f"on one thread, {t1:.1f} s, weight bytes of those rows"),
     }
 
 
@@ -335,6 +404,28 @@ def summarize_traffic(fetch_csv, write_csv):
     print("\n".join(lines))
 
 
+def summarize_trace(trace_csv):
+    """Per-kernel launch durations from a rocprofv3 kernel-trace CSV: count,
+    mean, median, p10, p90, min and max in microseconds, as markdown lines,
+    longest total time first."""
+    import csv
+    per = {}
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            name = (r["Kernel_Name"].replace("(anonymous namespace)", "{anon}")
+                    .split("(")[0].replace("void ", ""))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            per.setdefault(name, []).append(dur)
+    out = ["| kernel | launches | mean us | median us | p10 us | p90 us | min us | max us |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(d)
+        out.append(f"| `{name}` | {a.size} | {a.mean():.3f} | {np.median(a):.3f} | "
+                   f"{np.percentile(a, 10):.3f} | {np.percentile(a, 90):.3f} | {a.min():.3f} | "
+                   f"{a.max():.3f} |")
+    return out
+
+
 SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES")
 
 
@@ -387,25 +478,25 @@ def contraction_ab(qpn, torch):
     twin: six launches each (for the PMC passes), then the time of each in
     back-to-back graphs.  Prints one JSON line."""
     rows = []
-    try:
-        for name, n, k, fmt in HEADLINE:
-            s = Shape(qpn, torch, name, n, k, fmt, (1, 8))
-            for m, p_mfma, p_vdot in CONTRACTION_AB:
-                for plan in (p_mfma, p_vdot):
-                    qpn.debug_set_plan(plan)
-                    for _ in range(6):
-                        qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws)
-                    torch.cuda.synchronize()
-                    med = float(np.median(time_call(qpn, torch, s, m)))
-                    kname = qpn.kernel_name(fmt, m, n, k)
-                    log(f"{name} M={m} plan {plan}: {med * 1e6:.2f} us  {kname}")
-                    rows.append({"call": f"{name}_M{m}", "plan": plan, "kernel": kname,
-                                 "contraction": "valu_dot" if plan == p_vdot else "mfma",
-                                 "us": round(med * 1e6, 3), "GBps": round(s.bytes / med / 1e9, 1)})
-            del s
-            torch.cuda.empty_cache()
-    finally:
-        qpn.debug_set_plan(0)
+    for name, n, k, fmt in HEADLINE:
+        s = Shape(qpn, torch, name, n, k, fmt, (1, 8))
+        # room for every forced plan's K splits
+        s.ws = torch.zeros(max(qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, m, n, k, plan=p)
+                               for m, a, b in CONTRACTION_AB for p in (a, b)) + 256,
+                           dtype=torch.uint8, device="cuda")
+        for m, p_mfma, p_vdot in CONTRACTION_AB:
+            for plan in (p_mfma, p_vdot):
+                for _ in range(6):
+                    qpn.gemm(s.next_copy(), s.xm[m], out=s.y[m], ws=s.ws, plan=plan)
+                torch.cuda.synchronize()
+                med = float(np.median(time_call(qpn, torch, s, m, plan=plan)))
+                kname = qpn.kernel_name(fmt, m, n, k, plan=plan)
+                log(f"{name} M={m} plan {plan}: {med * 1e6:.2f} us  {kname}")
+                rows.append({"call": f"{name}_M{m}", "plan": plan, "kernel": kname,
+                             "contraction": "valu_dot" if plan == p_vdot else "mfma",
+                             "us": round(med * 1e6, 3), "GBps": round(s.bytes / med / 1e9, 1)})
+        del s
+        torch.cuda.empty_cache()
     print(json.dumps({"contraction_ab": rows}), flush=True)
 
 
@@ -439,6 +530,8 @@ def main():
     ap.add_argument("--summarize-sq", nargs=4, metavar=("AB_CSV", "AB_JSON", "HEAD_CSV", "BENCH_JSON"),
                     help="SQ counter tables from the PMC passes of --contraction-ab and "
                          "--traffic-workload and the JSON lines of --contraction-ab and bench.py")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="per-kernel duration statistics from a rocprofv3 kernel trace")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
     ap.add_argument("--prefill-workload", action="store_true",
@@ -449,6 +542,9 @@ def main():
 
     if args.summarize_traffic:  # host only: post-processes rocprofv3 output
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_trace:  # host only: post-processes rocprofv3 output
+        print("\n".join(summarize_trace(args.summarize_trace)))
         return
     if args.summarize_sq:  # host only: post-processes rocprofv3 output
         ab_csv, ab_json, head_csv, bench_json = args.summarize_sq
@@ -500,20 +596,14 @@ def main():
     step_bytes = sum(s.bytes * len(s.ms) for s in shapes)
     value = step_bytes / step_s / 1e9
 
-    # per-call launch times
+    # per-call launch times of the headline calls
     breakdown, per_kernel = {}, {}
     for s in shapes:
         for m in s.ms:
             per = time_call(qpn, torch, s, m)
-            med = float(np.median(per))
             kname = qpn.kernel_name(s.fmt, m, s.n, s.k, lmhead=False)
-            breakdown[f"{s.name}_M{m}"] = {
-                "kernel": kname, "us": round(med * 1e6, 3),
-                "us_min": round(min(per) * 1e6, 3), "us_max": round(max(per) * 1e6, 3),
-                "GBps": round(s.bytes / med / 1e9, 1),
-                "pct_hbm_peak": round(100 * s.bytes / med / 1e9 / HBM_PEAK_GBPS, 1),
-                "weight_bytes": s.bytes, "rotated_copies": len(s.copies),
-            }
+            breakdown[f"{s.name}_M{m}"] = {"kernel": kname, **call_stats(per, s.bytes),
+                                           "rotated_copies": len(s.copies)}
             k = per_kernel.setdefault(kname, {"t": [], "bytes": s.bytes, "calls": []})
             k["t"] += per
             k["calls"].append(f"{s.name}_M{m}")
@@ -521,118 +611,11 @@ def main():
     dk = per_kernel[dom]
     avg_s = float(np.mean(dk["t"]))
     achieved = dk["bytes"] / avg_s / 1e9
+    del shapes
+    torch.cuda.empty_cache()
 
-    extra = {}
-    if args.extra:
-        for name, n, k, fmt, ms in EXTRA:
-            log(f"extra: {name}")
-            sh = Shape(qpn, torch, name, n, k, fmt, ms)
-            for m in ms:
-                per = time_call(qpn, torch, sh, m)
-                med = float(np.median(per))
-                extra[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k), "us": round(med * 1e6, 3),
-                                         "GBps": round(sh.bytes / med / 1e9, 1),
-                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
-            del sh
-            torch.cuda.empty_cache()
-        from fp8_quantized_skinny_qpn_amd import synth
-        name, n, k = LMHEAD
-        log(f"extra: {name}")
-        w = torch.from_numpy(synth.weights(n, k, seed=0)).cuda()
-        pw = qpn.pack_nvfp4(w)
-        del w
-        torch.cuda.empty_cache()
-        copies = [pw] + [pw.clone() for _ in range(2)]
-        x8 = torch.from_numpy(synth.activations(8, k, seed=0)).cuda()
-        b = algo_bytes(n, k, "nvfp4")
-        for m in (1, 8):
-            xm = x8[:m].contiguous()
-            lg = torch.empty((m, n), dtype=torch.float16, device="cuda")
-            am = torch.empty((m,), dtype=torch.int32, device="cuda")
-            ws = torch.zeros(qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, m, n, k), dtype=torch.uint8, device="cuda")
-            qpn.lmhead_nvfp4(copies[0], xm, lg, am, ws)
-            g = capture(torch, lambda: [qpn.lmhead_nvfp4(copies[i % 3], xm, lg, am, ws) for i in range(12)])
-            per = [t / 12 for t in time_graph(torch, g, 5)]
-            del g
-            med = float(np.median(per))
-            extra[f"{name}_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
-                                     "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
-            # the same weights through the plain GEMM (no argmax), for the argmax's share
-            g = capture(torch, lambda: [qpn.gemm(copies[i % 3], xm, out=lg) for i in range(12)])
-            per = [t / 12 for t in time_graph(torch, g, 5)]
-            del g
-            med = float(np.median(per))
-            extra[f"{name}_gemm_only_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
-                                               "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
-            # the lm_head of a k = m - 1 draft verify round, acceptance fused
-            if m > 1:
-                draft = torch.zeros((m - 1,), dtype=torch.int32, device="cuda")
-                res = torch.empty((2,), dtype=torch.int32, device="cuda")
-                qpn.lmhead_verify_nvfp4(copies[0], xm, draft, lg, am, res, ws)
-                g = capture(torch, lambda: [qpn.lmhead_verify_nvfp4(copies[i % 3], xm, draft, lg, am, res, ws)
-                                            for i in range(12)])
-                per = [t / 12 for t in time_graph(torch, g, 5)]
-                del g
-                med = float(np.median(per))
-                extra[f"{name}_verify_M{m}"] = {"us": round(med * 1e6, 3), "GBps": round(b / med / 1e9, 1),
-                                                "pct_hbm_peak": round(100 * b / med / 1e9 / HBM_PEAK_GBPS, 1)}
-        del copies, pw
-        torch.cuda.empty_cache()
-        # per-rank (TP=4) shard shapes, one call at a time
-        for name, n, k, fmt in TP4 + [TP4_LMHEAD]:
-            log(f"extra: {name}")
-            sh = Shape(qpn, torch, name, n, k, fmt, (1, 8))
-            for m in (1, 8):
-                per = time_call(qpn, torch, sh, m)
-                med = float(np.median(per))
-                extra[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k), "us": round(med * 1e6, 3),
-                                         "GBps": round(sh.bytes / med / 1e9, 1),
-                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
-            del sh
-            torch.cuda.empty_cache()
-        # prefill-sized blocks: time, matrix-unit rate and weight rate
-        for name, n, k, fmt, ms in PREFILL:
-            log(f"extra: {name}")
-            sh = Shape(qpn, torch, name, n, k, fmt, ())
-            xs = torch.from_numpy(synth.activations(256, k, seed=0, m_max=256)).cuda()
-            op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
-            ws = torch.zeros(max(256, max(qpn.workspace_bytes(op, m, n, k) for m in ms)),
-                             dtype=torch.uint8, device="cuda")
-            for m in ms:
-                xm = xs[:m].contiguous()
-                ym = torch.empty((m, n), dtype=torch.float16, device="cuda")
-                qpn.prefill(sh.next_copy(), xm, out=ym, ws=ws)
-                g = capture(torch, lambda: [qpn.prefill(sh.next_copy(), xm, out=ym, ws=ws) for _ in range(16)])
-                per = [t / 16 for t in time_graph(torch, g, 5)]
-                del g
-                med = float(np.median(per))
-                tf = 2.0 * m * n * k / med / 1e12
-                pl = qpn.gemm_plan(op, m, n, k)
-                extra[f"{name}_M{m}"] = {"us": round(med * 1e6, 3), "TFLOPs": round(tf, 1),
-                                         "pct_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
-                                         "GBps": round(sh.bytes / med / 1e9, 1),
-                                         "pct_hbm_peak": round(100 * sh.bytes / med / 1e9 / HBM_PEAK_GBPS, 1),
-                                         "workgroups": pl.workgroups, "splits": pl.splits}
-            del sh, xs, ws
-            torch.cuda.empty_cache()
-        # whole layers at M = 8: the four projections back to back (full and per-rank)
-        for lname, layer in (("layer_M8", LAYER), ("layer_allfp4_M8", LAYER_ALLFP4),
-                             ("tp4_layer_M8", TP4)):
-            log(f"extra: {lname}")
-            lshapes = [Shape(qpn, torch, name, n, k, fmt, (8,)) for name, n, k, fmt in layer]
-            lbytes = sum(sh.bytes for sh in lshapes)
-            g = capture(torch, lambda: [qpn.gemm(sh.next_copy(), sh.xm[8], out=sh.y[8], ws=sh.ws)
-                                        for _ in range(BATCH // 4) for sh in lshapes])
-            g.replay()
-            torch.cuda.synchronize()
-            per = [t / (BATCH // 4) for t in time_graph(torch, g, 5)]
-            del g
-            med = float(np.median(per))
-            extra[lname] = {"calls": [sh.name for sh in lshapes], "us": round(med * 1e6, 3),
-                            "weight_bytes": lbytes, "GBps": round(lbytes / med / 1e9, 1),
-                            "pct_hbm_peak": round(100 * lbytes / med / 1e9 / HBM_PEAK_GBPS, 1)}
-            del lshapes
-            torch.cuda.empty_cache()
+    configs = time_configs(qpn, torch)
+    extra = time_extra(qpn, torch) if args.extra else {}
 
     ceiling = read_ceiling(qpn, torch)
     call_s, call_b = read_ceiling_call(qpn, torch, dk["bytes"])
@@ -660,14 +643,15 @@ def main():
         "pct_read_ceiling": round(100 * value / ceiling, 1),
         "config": {
             "workload": "nvfp4_skinny_gemm K5120->N17408 and K17408->N5120, M in {1,4,8}",
-            "calls_per_step": len(shapes) * len(HEADLINE_M),
+            "calls_per_step": len(HEADLINE) * len(HEADLINE_M),
             "weights": "NVFP4 (E2M1 codes, UE4M3 per 16-K block, FP32 tensor scale) packed from N(0,0.02) fp32, seed 0",
             "activations": "fp16 N(0,1), seed 0",
             "step_weight_bytes": step_bytes,
-            "rotated_copies_per_shape": [len(s.copies) for s in shapes],
             "timing": "HIP graph of exactly `steps` steps, replayed once between device synchronisations",
-            "plans": {f"{s.name}_M{m}": qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, s.n, s.k).__dict__
-                      for s in shapes for m in s.ms},
+            "per_call_timing": (f"median, p10 and p90 over 15 replays of a graph of {BATCH} back-to-back "
+                                "launches on rotating copies (>= 1 GiB per shape)"),
+            "plans": {f"{name}_M{m}": qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, n, k).__dict__
+                      for name, n, k, _ in HEADLINE for m in HEADLINE_M},
         },
         "roofline": {
             "bound": "hbm",
@@ -690,10 +674,164 @@ def main():
         },
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "configs": configs,
     }
     if extra:
         out["extra_configs"] = extra
     print(json.dumps(out), flush=True)
+
+
+def time_configs(qpn, torch):
+    """The other configurations of the metric, timed in every run: the small
+    NVFP4 GEMV, the FP8 calls, one decoder layer at M = 8 (each GEMM and the
+    four back to back) and the lm_head with its fused argmax at M = 1 and 8."""
+    from fp8_quantized_skinny_qpn_amd import synth
+    out = {}
+    for name, n, k, fmt, ms in CONFIGS:
+        log(f"config: {name}")
+        sh = Shape(qpn, torch, name, n, k, fmt, ms)
+        for m in ms:
+            out[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k),
+                                   **call_stats(time_call(qpn, torch, sh, m), sh.bytes)}
+        del sh
+        torch.cuda.empty_cache()
+    # cfg4: the layer, each GEMM alone and the four back to back
+    log("config: cfg4 layer at M=8")
+    lshapes = [Shape(qpn, torch, name, n, k, fmt, (8,), seed=i)
+               for i, (name, n, k, fmt) in enumerate(LAYER)]
+    for sh in lshapes:
+        out[f"cfg4_{sh.name}_M8"] = {"kernel": qpn.kernel_name(sh.fmt, 8, sh.n, sh.k),
+                                     **call_stats(time_call(qpn, torch, sh, 8), sh.bytes)}
+    out["cfg4_layer_M8"] = {"calls": [sh.name for sh in lshapes],
+                            **call_stats(time_layer(qpn, torch, lshapes), sum(sh.bytes for sh in lshapes))}
+    del lshapes
+    torch.cuda.empty_cache()
+    # cfg5: the lm_head with the fused argmax
+    name, n, k = LMHEAD
+    log(f"config: {name}")
+    w = torch.from_numpy(synth.weights(n, k, seed=0)).cuda()
+    pw = qpn.pack_nvfp4(w)
+    del w
+    torch.cuda.empty_cache()
+    copies = [pw] + [pw.clone() for _ in range(2)]
+    x8 = torch.from_numpy(synth.activations(8, k, seed=0)).cuda()
+    b = algo_bytes(n, k, "nvfp4")
+    for m in (1, 8):
+        xm = x8[:m].contiguous()
+        lg = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        am = torch.empty((m,), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, m, n, k), dtype=torch.uint8, device="cuda")
+        qpn.lmhead_nvfp4(copies[0], xm, lg, am, ws)
+        g = capture(torch, lambda: [qpn.lmhead_nvfp4(copies[i % 3], xm, lg, am, ws) for i in range(12)])
+        per = [t / 12 for t in time_graph(torch, g, 15)]
+        del g
+        out[f"{name}_M{m}"] = {"kernels": [qpn.kernel_name("nvfp4", m, n, k, lmhead=True),
+                                           "qpn::argmax_finalize_kernel"],
+                               **call_stats(per, b)}
+    del copies, pw
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_layer(qpn, torch, lshapes, reps=15):
+    """Per-replay average time (s) of one layer: the GEMMs of lshapes back
+    to back at M = 8, in graphs of BATCH // 4 layers on rotating copies."""
+    g = capture(torch, lambda: [qpn.gemm(sh.next_copy(), sh.xm[8], out=sh.y[8], ws=sh.ws)
+                                for _ in range(BATCH // 4) for sh in lshapes])
+    g.replay()
+    torch.cuda.synchronize()
+    per = [t / (BATCH // 4) for t in time_graph(torch, g, reps)]
+    del g
+    return per
+
+
+def time_extra(qpn, torch):
+    """--extra: FP8 at M = 8, the lm_head without argmax and with the fused
+    verification, the per-rank shard shapes under 4-way tensor parallelism,
+    prefill-sized blocks and the all-FP4 layer."""
+    from fp8_quantized_skinny_qpn_amd import synth
+    extra = {}
+    for name, n, k, fmt, ms in EXTRA:
+        log(f"extra: {name}")
+        sh = Shape(qpn, torch, name, n, k, fmt, ms)
+        for m in ms:
+            extra[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k),
+                                     **call_stats(time_call(qpn, torch, sh, m), sh.bytes)}
+        del sh
+        torch.cuda.empty_cache()
+    name, n, k = LMHEAD
+    log(f"extra: {name}")
+    w = torch.from_numpy(synth.weights(n, k, seed=0)).cuda()
+    pw = qpn.pack_nvfp4(w)
+    del w
+    torch.cuda.empty_cache()
+    copies = [pw] + [pw.clone() for _ in range(2)]
+    x8 = torch.from_numpy(synth.activations(8, k, seed=0)).cuda()
+    b = algo_bytes(n, k, "nvfp4")
+    for m in (1, 8):
+        xm = x8[:m].contiguous()
+        lg = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        am = torch.empty((m,), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(qpn.workspace_bytes(qpn.OP_LMHEAD_NVFP4, m, n, k), dtype=torch.uint8, device="cuda")
+        # the same weights through the plain GEMM (no argmax), for the argmax's share
+        g = capture(torch, lambda: [qpn.gemm(copies[i % 3], xm, out=lg) for i in range(12)])
+        per = [t / 12 for t in time_graph(torch, g, 5)]
+        del g
+        extra[f"{name}_gemm_only_M{m}"] = call_stats(per, b)
+        # the lm_head of a k = m - 1 draft verify round, acceptance fused
+        if m > 1:
+            draft = torch.zeros((m - 1,), dtype=torch.int32, device="cuda")
+            res = torch.empty((2,), dtype=torch.int32, device="cuda")
+            qpn.lmhead_verify_nvfp4(copies[0], xm, draft, lg, am, res, ws)
+            g = capture(torch, lambda: [qpn.lmhead_verify_nvfp4(copies[i % 3], xm, draft, lg, am, res, ws)
+                                        for i in range(12)])
+            per = [t / 12 for t in time_graph(torch, g, 5)]
+            del g
+            extra[f"{name}_verify_M{m}"] = call_stats(per, b)
+    del copies, pw
+    torch.cuda.empty_cache()
+    # per-rank (TP=4) shard shapes, one call at a time
+    for name, n, k, fmt in TP4 + [TP4_LMHEAD]:
+        log(f"extra: {name}")
+        sh = Shape(qpn, torch, name, n, k, fmt, (1, 8))
+        for m in (1, 8):
+            extra[f"{name}_M{m}"] = {"kernel": qpn.kernel_name(fmt, m, n, k),
+                                     **call_stats(time_call(qpn, torch, sh, m, reps=5), sh.bytes)}
+        del sh
+        torch.cuda.empty_cache()
+    # prefill-sized blocks: time, matrix-unit rate and weight rate
+    for name, n, k, fmt, ms in PREFILL:
+        log(f"extra: {name}")
+        sh = Shape(qpn, torch, name, n, k, fmt, ())
+        xs = torch.from_numpy(synth.activations(256, k, seed=0, m_max=256)).cuda()
+        op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+        ws = torch.zeros(max(256, max(qpn.workspace_bytes(op, m, n, k) for m in ms)),
+                         dtype=torch.uint8, device="cuda")
+        for m in ms:
+            xm = xs[:m].contiguous()
+            ym = torch.empty((m, n), dtype=torch.float16, device="cuda")
+            qpn.prefill(sh.next_copy(), xm, out=ym, ws=ws)
+            g = capture(torch, lambda: [qpn.prefill(sh.next_copy(), xm, out=ym, ws=ws) for _ in range(16)])
+            per = [t / 16 for t in time_graph(torch, g, 5)]
+            del g
+            med = float(np.median(per))
+            tf = 2.0 * m * n * k / med / 1e12
+            pl = qpn.gemm_plan(op, m, n, k)
+            extra[f"{name}_M{m}"] = {**call_stats(per, sh.bytes), "TFLOPs": round(tf, 1),
+                                     "pct_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
+                                     "workgroups": pl.workgroups, "splits": pl.splits}
+        del sh, xs, ws
+        torch.cuda.empty_cache()
+    # whole layers at M = 8: the all-FP4 variant and the per-rank shards
+    for lname, layer in (("layer_allfp4_M8", LAYER_ALLFP4), ("tp4_layer_M8", TP4)):
+        log(f"extra: {lname}")
+        lshapes = [Shape(qpn, torch, name, n, k, fmt, (8,), seed=i)
+                   for i, (name, n, k, fmt) in enumerate(layer)]
+        extra[lname] = {"calls": [sh.name for sh in lshapes],
+                        **call_stats(time_layer(qpn, torch, lshapes, reps=5), sum(sh.bytes for sh in lshapes))}
+        del lshapes
+        torch.cuda.empty_cache()
+    return extra
 
 
 if __name__ == "__main__":

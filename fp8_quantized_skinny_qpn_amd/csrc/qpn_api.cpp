@@ -6,7 +6,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
-#include <atomic>
 #include <mutex>
 
 #include "qpn_common.h"
@@ -45,11 +44,6 @@ int device_check() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QPN_OK : QPN_ERR_LAUNCH; }
 
-// Plan override for A/B measurements (qpn_debug_set_plan): 0 = automatic.
-std::atomic<int> g_plan{0};
-
-int forced_plan() { return g_plan.load(std::memory_order_relaxed); }
-
 // Bytes of lm_head argmax keys at the start of its workspace, and where the
 // split-K area starts after them.
 size_t lmhead_keys_bytes(int m, int64_t n) {
@@ -68,8 +62,9 @@ int gemm_common_checks(uint32_t fmt, const void* packed, const uint16_t* x, cons
   return QPN_OK;
 }
 
-int gemm_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
-               int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+// plan: 0 = the automatic choice; otherwise a compiled plan id (diagnostics).
+int gemm_entry(uint32_t fmt, int plan, const void* packed, const uint16_t* x, uint16_t* y, int m,
+               int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = gemm_common_checks(fmt, packed, x, y, m, n, k);
   if (rc != QPN_OK) return rc;
   if (m == 0 || n == 0) return QPN_OK;
@@ -77,7 +72,7 @@ int gemm_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y,
   rc = device_check();
   if (rc != QPN_OK) return rc;
   GemmLaunch l;
-  const int lr = gemm_launch_for(fmt, m, n, k, forced_plan(), workspace ? workspace_bytes : 0, 0, &l);
+  const int lr = gemm_launch_for(fmt, m, n, k, plan, workspace ? workspace_bytes : 0, 0, &l);
   if (lr != kGemmLaunchOk) return lr == kGemmNoWorkspace ? QPN_ERR_BUFFER : QPN_ERR_SHAPE;
   GemmArgs a{packed, x, y, m, n, k, nullptr, workspace, stream};
   return launch_status(launch_gemm(fmt, false, a, l));
@@ -112,77 +107,64 @@ size_t qpn_fp8_packed_bytes(int64_t n, int64_t k) {
   return (size_t)f8_blob_bytes(n, k);
 }
 
-size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
-  if (op == QPN_OP_PREFILL_NVFP4 || op == QPN_OP_PREFILL_FP8) {
-    const uint32_t fmt = op == QPN_OP_PREFILL_NVFP4 ? kFmtNvfp4 : kFmtFp8;
-    if (m < 0 || m > kMaxPrefillM) return (size_t)-1;
-    if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return (size_t)-1;
-    if (m == 0 || n == 0) return 0;
-    if (m <= kPrefillSkinnyRows) {
-      GemmLaunch g;
-      if (gemm_launch_for(fmt, m, n, k, 0, (size_t)-1, 0, &g) != kGemmLaunchOk) return (size_t)-1;
-      return g.splits > 1 ? g.ws_needed : 0;
-    }
-    PrefillLaunch l;
-    if (prefill_launch_for(fmt, m, n, k, (size_t)-1, &l) != kGemmLaunchOk) return (size_t)-1;
-    return l.ws_needed;
-  }
-  if (m < 0 || m > kMaxM) return (size_t)-1;
-  uint32_t fmt;
-  switch (op) {
-    case QPN_OP_GEMM_NVFP4:
-    case QPN_OP_LMHEAD_NVFP4:
-      if (!nv_shape_ok(n, k)) return (size_t)-1;
-      fmt = kFmtNvfp4;
-      break;
-    case QPN_OP_GEMM_FP8:
-      if (!f8_shape_ok(n, k)) return (size_t)-1;
-      fmt = kFmtFp8;
-      break;
-    default: return (size_t)-1;
-  }
-  if (m == 0 || n == 0) return 0;
-  const bool lm = op == QPN_OP_LMHEAD_NVFP4;
-  GemmLaunch l;
-  if (gemm_launch_for(fmt, m, n, k, forced_plan(), (size_t)-1, lm ? lmhead_split_offset(m, n) : 0,
-                      &l) != kGemmLaunchOk)
-    return (size_t)-1;
-  if (l.splits <= 1) return lm ? lmhead_keys_bytes(m, n) : 0;
-  return l.ws_needed;
+}  // extern "C"
+
+namespace {
+
+// Launch plan and workspace of one call, as the plan queries report them.
+struct PlanInfo {
+  int64_t workgroups;
+  int waves_per_panel;
+  int panels_per_workgroup;
+  int depth;
+  int splits;
+  int activation_rows;
+  int64_t split_wgs;
+  int valu_dot;
+  size_t ws_bytes;  // workspace the call uses for this plan (0 = none needed)
+};
+
+void fill_skinny(const GemmLaunch& g, int m, PlanInfo* o) {
+  o->workgroups = g.workgroups;
+  o->waves_per_panel = g.waves_per_panel;
+  o->panels_per_workgroup = g.panels_per_workgroup;
+  o->depth = g.depth;
+  o->splits = g.splits;
+  o->activation_rows = gemm_activation_rows(m > 0 ? m : 1);
+  o->split_wgs = g.split_wgs;
+  o->valu_dot = g.valu_dot;
 }
 
-int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
-                  int* panels_per_workgroup, int* prefetch_depth, int* splits,
-                  int* activation_rows, int64_t* split_workgroups, int* valu_dot) {
+// The plan a call of kind `op` uses for (m, n, k) given all the workspace it
+// asks for; `plan` 0 is the automatic choice, 1.. a compiled plan (skinny
+// ops only).  A pure function of its arguments.  QPN_OK or QPN_ERR_SHAPE.
+int plan_query(int op, int plan, int m, int64_t n, int64_t k, PlanInfo* o) {
+  GemmPlan pl;
+  if (plan != 0 && !gemm_plan_info(plan, &pl)) return QPN_ERR_SHAPE;
   if (op == QPN_OP_PREFILL_NVFP4 || op == QPN_OP_PREFILL_FP8) {
     const uint32_t fmt = op == QPN_OP_PREFILL_NVFP4 ? kFmtNvfp4 : kFmtFp8;
+    if (plan != 0) return QPN_ERR_SHAPE;
     if (m < 0 || m > kMaxPrefillM) return QPN_ERR_SHAPE;
     if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
-    if (m <= kPrefillSkinnyRows) {  // the skinny kernel's plan (given the workspace asked for)
+    if (m <= kPrefillSkinnyRows) {  // the skinny kernel (a 16-row tile above 8 rows)
       GemmLaunch g;
       if (gemm_launch_for(fmt, m > 0 ? m : 1, n, k, 0, (size_t)-1, 0, &g) != kGemmLaunchOk)
         return QPN_ERR_SHAPE;
-      if (workgroups) *workgroups = g.workgroups;
-      if (waves_per_panel) *waves_per_panel = g.waves_per_panel;
-      if (panels_per_workgroup) *panels_per_workgroup = g.panels_per_workgroup;
-      if (prefetch_depth) *prefetch_depth = g.depth;
-      if (splits) *splits = g.splits;
-      if (activation_rows) *activation_rows = gemm_activation_rows(m > 0 ? m : 1);
-      if (split_workgroups) *split_workgroups = g.split_wgs;
-      if (valu_dot) *valu_dot = g.valu_dot;
+      fill_skinny(g, m, o);
+      o->ws_bytes = (m == 0 || n == 0 || g.splits <= 1) ? 0 : g.ws_needed;
       return QPN_OK;
     }
     PrefillLaunch l;
-    if (prefill_launch_for(fmt, m > 0 ? m : 1, n, k, (size_t)-1, &l) != kGemmLaunchOk)
-      return QPN_ERR_SHAPE;
-    if (workgroups) *workgroups = l.workgroups;
-    if (waves_per_panel) *waves_per_panel = 2;  // two wavefronts, one per half of the rows
-    if (panels_per_workgroup) *panels_per_workgroup = 8;
-    if (prefetch_depth) *prefetch_depth = l.depth;
-    if (splits) *splits = l.splits;
-    if (activation_rows) *activation_rows = 32 * l.mt;
-    if (split_workgroups) *split_workgroups = l.workgroups;
-    if (valu_dot) *valu_dot = 0;
+    if (prefill_launch_for(fmt, m, n, k, (size_t)-1, &l) != kGemmLaunchOk) return QPN_ERR_SHAPE;
+    o->workgroups = l.workgroups;
+    o->waves_per_panel = 2;  // two wavefronts, one per half of the rows
+    o->panels_per_workgroup = 8;
+    o->depth = l.depth;
+    o->splits = l.splits;
+    o->activation_rows = 32 * l.mt;
+    o->split_wgs = l.workgroups;
+    o->valu_dot = 0;
+    o->ws_bytes = n == 0 ? 0 : l.ws_needed;
     return QPN_OK;
   }
   if (m < 0 || m > kMaxM) return QPN_ERR_SHAPE;
@@ -201,17 +183,43 @@ int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int*
   }
   const bool lm = op == QPN_OP_LMHEAD_NVFP4;
   GemmLaunch l;
-  if (gemm_launch_for(fmt, m, n, k, forced_plan(), (size_t)-1, lm ? lmhead_split_offset(m, n) : 0,
-                      &l) != kGemmLaunchOk)
+  if (gemm_launch_for(fmt, m > 0 ? m : 1, n, k, plan, (size_t)-1,
+                      lm ? lmhead_split_offset(m, n) : 0, &l) != kGemmLaunchOk)
     return QPN_ERR_SHAPE;
-  if (workgroups) *workgroups = l.workgroups;
-  if (waves_per_panel) *waves_per_panel = l.waves_per_panel;
-  if (panels_per_workgroup) *panels_per_workgroup = l.panels_per_workgroup;
-  if (prefetch_depth) *prefetch_depth = l.depth;
-  if (splits) *splits = l.splits;
-  if (activation_rows) *activation_rows = gemm_activation_rows(m);
-  if (split_workgroups) *split_workgroups = l.split_wgs;
-  if (valu_dot) *valu_dot = l.valu_dot;
+  fill_skinny(l, m, o);
+  if (m == 0 || n == 0) o->ws_bytes = 0;
+  else if (l.splits <= 1) o->ws_bytes = lm ? lmhead_keys_bytes(m, n) : 0;
+  else o->ws_bytes = l.ws_needed;
+  return QPN_OK;
+}
+
+template <class T>
+void put(T* dst, T v) {
+  if (dst) *dst = v;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k) {
+  PlanInfo o;
+  return plan_query(op, 0, m, n, k, &o) == QPN_OK ? o.ws_bytes : (size_t)-1;
+}
+
+int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t* workgroups, int* waves_per_panel,
+                  int* panels_per_workgroup, int* prefetch_depth, int* splits,
+                  int* activation_rows, int64_t* split_workgroups) {
+  PlanInfo o;
+  const int rc = plan_query(op, 0, m, n, k, &o);
+  if (rc != QPN_OK) return rc;
+  put(workgroups, o.workgroups);
+  put(waves_per_panel, o.waves_per_panel);
+  put(panels_per_workgroup, o.panels_per_workgroup);
+  put(prefetch_depth, o.depth);
+  put(splits, o.splits);
+  put(activation_rows, o.activation_rows);
+  put(split_workgroups, o.split_wgs);
   return QPN_OK;
 }
 
@@ -252,12 +260,12 @@ int qpn_requant_fp8_to_nvfp4(const void* fp8_packed, size_t fp8_bytes, int64_t n
 
 int qpn_gemm_nvfp4(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
                    int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_entry(kFmtNvfp4, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+  return gemm_entry(kFmtNvfp4, 0, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
 }
 
 int qpn_gemm_fp8(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n, int64_t k,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_entry(kFmtFp8, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+  return gemm_entry(kFmtFp8, 0, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -286,9 +294,9 @@ int prefill_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t*
   return launch_status(launch_prefill(fmt, a, l));
 }
 
-int lmhead_common(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
-                  const int32_t* draft, int32_t* result, int m, int64_t n, int64_t k,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+int lmhead_common(int plan, const void* packed, const uint16_t* x, uint16_t* logits,
+                  int32_t* argmax, const int32_t* draft, int32_t* result, int m, int64_t n,
+                  int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
   if (n < 1) return QPN_ERR_SHAPE;
   int rc = gemm_common_checks(kFmtNvfp4, packed, x, logits, m, n, k);
   if (rc != QPN_OK) return rc;
@@ -301,7 +309,7 @@ int lmhead_common(const void* packed, const uint16_t* x, uint16_t* logits, int32
   rc = device_check();
   if (rc != QPN_OK) return rc;
   GemmLaunch l;
-  const int lr = gemm_launch_for(kFmtNvfp4, m, n, k, forced_plan(), workspace_bytes,
+  const int lr = gemm_launch_for(kFmtNvfp4, m, n, k, plan, workspace_bytes,
                                  lmhead_split_offset(m, n), &l);
   if (lr != kGemmLaunchOk) return lr == kGemmNoWorkspace ? QPN_ERR_BUFFER : QPN_ERR_SHAPE;
   GemmArgs a{packed, x, logits, m, n, k, (uint64_t*)workspace, workspace, stream};
@@ -325,7 +333,7 @@ int qpn_gemm_prefill_fp8(const void* packed, const uint16_t* x, uint16_t* y, int
 int qpn_lmhead_nvfp4(const void* packed, const uint16_t* x, uint16_t* logits, int32_t* argmax,
                      int m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  return lmhead_common(packed, x, logits, argmax, nullptr, nullptr, m, n, k, workspace,
+  return lmhead_common(0, packed, x, logits, argmax, nullptr, nullptr, m, n, k, workspace,
                        workspace_bytes, stream);
 }
 
@@ -337,7 +345,7 @@ int qpn_lmhead_verify_nvfp4(const void* packed, const uint16_t* x, uint16_t* log
     if (!result || (m > 1 && !draft)) return QPN_ERR_NULL;
     if (!aligned(result, 4) || (draft && !aligned(draft, 4))) return QPN_ERR_ALIGN;
   }
-  return lmhead_common(packed, x, logits, argmax, m > 1 ? draft : nullptr, result, m, n, k,
+  return lmhead_common(0, packed, x, logits, argmax, m > 1 ? draft : nullptr, result, m, n, k,
                        workspace, workspace_bytes, stream);
 }
 
@@ -383,11 +391,42 @@ int qpn_debug_decode_fp8(const uint8_t* codes16, int64_t count, uint16_t* out, v
   return launch_status(launch_decode_fp8(codes16, count, out, stream));
 }
 
-int qpn_debug_set_plan(int plan) {
+int qpn_debug_plan(int op, int plan, int m, int64_t n, int64_t k, int64_t* workgroups,
+                   int* waves_per_panel, int* panels_per_workgroup, int* prefetch_depth,
+                   int* splits, int* activation_rows, int64_t* split_workgroups, int* valu_dot,
+                   size_t* workspace_bytes) {
+  if (op != QPN_OP_GEMM_NVFP4 && op != QPN_OP_GEMM_FP8 && op != QPN_OP_LMHEAD_NVFP4)
+    return QPN_ERR_SHAPE;
+  PlanInfo o;
+  const int rc = plan_query(op, plan, m, n, k, &o);
+  if (rc != QPN_OK) return rc;
+  put(workgroups, o.workgroups);
+  put(waves_per_panel, o.waves_per_panel);
+  put(panels_per_workgroup, o.panels_per_workgroup);
+  put(prefetch_depth, o.depth);
+  put(splits, o.splits);
+  put(activation_rows, o.activation_rows);
+  put(split_workgroups, o.split_wgs);
+  put(valu_dot, o.valu_dot);
+  put(workspace_bytes, o.ws_bytes);
+  return QPN_OK;
+}
+
+int qpn_debug_run_plan(int op, int plan, const void* packed, const uint16_t* x, uint16_t* y,
+                       int32_t* argmax, int m, int64_t n, int64_t k, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   GemmPlan pl;
   if (plan != 0 && !gemm_plan_info(plan, &pl)) return QPN_ERR_SHAPE;
-  g_plan.store(plan, std::memory_order_relaxed);
-  return QPN_OK;
+  switch (op) {
+    case QPN_OP_GEMM_NVFP4:
+      return gemm_entry(kFmtNvfp4, plan, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+    case QPN_OP_GEMM_FP8:
+      return gemm_entry(kFmtFp8, plan, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+    case QPN_OP_LMHEAD_NVFP4:
+      return lmhead_common(plan, packed, x, y, argmax, nullptr, nullptr, m, n, k, workspace,
+                           workspace_bytes, stream);
+    default: return QPN_ERR_SHAPE;
+  }
 }
 
 int qpn_debug_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

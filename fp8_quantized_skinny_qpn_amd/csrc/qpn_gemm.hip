@@ -708,6 +708,12 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
     const size_t counters = ((size_t)g * 4 + 255) / 256 * 256;
     return counters + (size_t)s * g * pl.panels_per_workgroup * kLanes * 16;
   };
+  // the kernel addresses the workspace with 32-bit offsets: a split launch
+  // must fit below 2^31 bytes (and the given workspace)
+  auto fits = [&](int64_t s, int64_t g) {
+    const size_t need = ws_offset + need_for(s, g);
+    return s <= 1 || (need <= ws_bytes && need < ((size_t)1 << 31));
+  };
   // Placement 2: every wanted workgroup slot (one per CU) gets the same
   // number of whole panels, and the remainder panels are split in K into
   // about one more workgroup per slot, so that every CU streams the same
@@ -723,7 +729,7 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
       s0 = std::min<int64_t>(s0, std::max<int64_t>(1, J / (2 * pl.waves_per_panel)));
       const int64_t st0 = steps_of(s0);
       s0 = (J + st0 - 1) / st0;
-      if (ws_offset + need_for(s0, gs) <= ws_bytes) {
+      if (fits(s0, gs)) {
         out->plan = id;
         out->waves_per_panel = pl.waves_per_panel;
         out->panels_per_workgroup = pl.panels_per_workgroup;
@@ -750,8 +756,8 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   if (groups < 1) groups = 1;
   while (groups * S < want && (J + S) / (S + 1) >= 2 * pl.waves_per_panel) ++S;
   auto need = [&](int64_t s) -> size_t { return need_for(s, groups); };
-  while (S > smin && ws_offset + need(S) > ws_bytes) --S;
-  if (S > 1 && ws_offset + need(S) > ws_bytes) return kGemmNoWorkspace;
+  while (S > smin && !fits(S, groups)) --S;
+  if (!fits(S, groups)) return kGemmNoWorkspace;
   const int64_t steps = steps_of(S);
   S = J > 0 ? (J + steps - 1) / steps : 1;  // drop empty trailing ranges
   out->plan = id;

@@ -45,7 +45,7 @@ def _load():
         "qpn_nvfp4_packed_bytes": ([i64, i64], sz),
         "qpn_fp8_packed_bytes": ([i64, i64], sz),
         "qpn_workspace_bytes": ([i32, i32, i64, i64], sz),
-        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "qpn_gemm_plan": ([i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
         "qpn_pack_nvfp4": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_pack_fp8": ([vp, i64, i64, vp, sz, vp], i32),
         "qpn_requant_fp8_to_nvfp4": ([vp, sz, i64, i64, vp, sz, vp], i32),
@@ -60,7 +60,8 @@ def _load():
         "qpn_debug_decode_nvfp4": ([vp, vp, i64, vp, vp], i32),
         "qpn_debug_decode_fp8": ([vp, i64, vp, vp], i32),
         "qpn_debug_read_ceiling": ([vp, sz, vp, vp], i32),
-        "qpn_debug_set_plan": ([i32], i32),
+        "qpn_debug_plan": ([i32, i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "qpn_debug_run_plan": ([i32, i32, vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -79,7 +80,7 @@ EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
             "qpn_debug_unpack_nvfp4",
             "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",
-            "qpn_debug_read_ceiling", "qpn_debug_set_plan")
+            "qpn_debug_read_ceiling", "qpn_debug_plan", "qpn_debug_run_plan")
 
 
 def status_string(rc: int) -> str:
@@ -95,10 +96,12 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _torch_stream(stream=None):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream=None):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
 
 
 def nvfp4_packed_bytes(n: int, k: int) -> int:
@@ -109,8 +112,13 @@ def fp8_packed_bytes(n: int, k: int) -> int:
     return int(lib.qpn_fp8_packed_bytes(n, k))
 
 
-def workspace_bytes(op: int, m: int, n: int, k: int) -> int:
-    return int(lib.qpn_workspace_bytes(op, m, n, k))
+def workspace_bytes(op: int, m: int, n: int, k: int, plan: int = 0) -> int:
+    """Workspace a call uses; `plan` > 0 asks for a forced (diagnostic) plan."""
+    if plan == 0:
+        return int(lib.qpn_workspace_bytes(op, m, n, k))
+    out = ctypes.c_size_t()
+    check(lib.qpn_debug_plan(op, plan, m, n, k, *([None] * 8), ctypes.byref(out)))
+    return int(out.value)
 
 
 @dataclass(frozen=True)
@@ -130,22 +138,36 @@ class Plan:
         return self.waves_per_panel * self.panels_per_workgroup
 
 
-def gemm_plan(op: int, m: int, n: int, k: int) -> Plan:
+def gemm_plan(op: int, m: int, n: int, k: int, plan: int = 0) -> Plan:
     """The launch plan the library uses for a call of kind `op` (given the
-    workspace qpn_workspace_bytes asks for)."""
+    workspace qpn_workspace_bytes asks for); `plan` > 0 reports a forced
+    (diagnostic) plan through qpn_debug_plan."""
     wg = ctypes.c_int64()
     swg = ctypes.c_int64()
     outs = [ctypes.c_int() for _ in range(5)]
     vd = ctypes.c_int()
-    check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *[ctypes.byref(o) for o in outs],
-                            ctypes.byref(swg), ctypes.byref(vd)))
+    refs = [ctypes.byref(o) for o in outs]
+    if plan == 0:
+        check(lib.qpn_gemm_plan(op, m, n, k, ctypes.byref(wg), *refs, ctypes.byref(swg)))
+    else:
+        check(lib.qpn_debug_plan(op, plan, m, n, k, ctypes.byref(wg), *refs, ctypes.byref(swg),
+                                 ctypes.byref(vd), None))
     return Plan(wg.value, *[o.value for o in outs], swg.value, vd.value)
 
 
-def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:
+def plan_ids():
+    """Every compiled launch plan id (probed through qpn_debug_plan)."""
+    ids = []
+    for i in range(1, 65):
+        if lib.qpn_debug_plan(OP_GEMM_NVFP4, i, 1, 16, 16, *([None] * 9)) == QPN_OK:
+            ids.append(i)
+    return ids
+
+
+def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False, plan: int = 0) -> str:
     """Demangled name (template part) of the GEMM kernel a call launches."""
     op = OP_LMHEAD_NVFP4 if lmhead else (OP_GEMM_NVFP4 if fmt == FMT_NVFP4 else OP_GEMM_FP8)
-    pl = gemm_plan(op, m, n, k)
+    pl = gemm_plan(op, m, n, k, plan)
     f = 1 if fmt == FMT_NVFP4 else 2
     return (f"qpn::skinny_gemm_kernel<{f}u, {pl.waves_per_panel}, {pl.panels_per_workgroup}, "
             f"{pl.prefetch_depth}, {pl.activation_rows}, {'true' if lmhead else 'false'}, "
@@ -155,15 +177,23 @@ def kernel_name(fmt: str, m: int, n: int, k: int, lmhead: bool = False) -> str:
 # Zero-initialised workspaces, one per (device, stream): the library leaves a
 # workspace's split-K counters at zero after every call, so a workspace is
 # zeroed once, when it is allocated, and then reused by calls on its stream.
+# It is allocated and zeroed on that stream, so the zero-fill is ordered
+# before every kernel that uses it, and a replaced buffer is kept alive
+# until the work already queued on the stream is done.
 _workspaces = {}
 
 
-def workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
-    key = (torch.device(device).index, stream_handle)
+def workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """The cached zero-filled workspace of at least nbytes for `stream` (a
+    torch stream) on `device`."""
+    key = (torch.device(device).index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+        with torch.cuda.stream(stream):
+            new = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if ws is not None:
+            ws.record_stream(stream)
+        _workspaces[key] = ws = new
     return ws
 
 
@@ -231,21 +261,27 @@ def _x_check(x, k):
 
 
 def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=None,
-         ws: torch.Tensor = None) -> torch.Tensor:
-    """Y = X * What^T through qpn_gemm_nvfp4 / qpn_gemm_fp8.  `ws` (zero-filled
+         ws: torch.Tensor = None, plan: int = 0) -> torch.Tensor:
+    """Y = X * What^T through qpn_gemm_nvfp4 / qpn_gemm_fp8 (through
+    qpn_debug_run_plan with a forced plan when `plan` > 0).  `ws` (zero-filled
     before its first use) defaults to a cached per-stream workspace."""
     _x_check(x, pw.k)
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
     op = OP_GEMM_NVFP4 if pw.fmt == FMT_NVFP4 else OP_GEMM_FP8
-    fn = lib.qpn_gemm_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_fp8
-    st = _stream(stream)
-    need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
+    ts = _torch_stream(stream)
+    st = _stream(ts)
+    need = workspace_bytes(op, m, pw.n, pw.k, plan) if m > 0 else 0
     if ws is None and need > 0:
-        ws = workspace(need, x.device, st.value or 0)
-    check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k,
-             _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, st))
+        ws = workspace(need, x.device, ts)
+    wp, wn = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
+    if plan == 0:
+        fn = lib.qpn_gemm_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_fp8
+        check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k, wp, wn, st))
+    else:
+        check(lib.qpn_debug_run_plan(op, plan, _ptr(pw.blob), _ptr(x), _ptr(out), None, m, pw.n,
+                                     pw.k, wp, wn, st))
     return out
 
 
@@ -260,18 +296,20 @@ def prefill(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=
         out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
     op = OP_PREFILL_NVFP4 if pw.fmt == FMT_NVFP4 else OP_PREFILL_FP8
     fn = lib.qpn_gemm_prefill_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_prefill_fp8
-    st = _stream(stream)
+    ts = _torch_stream(stream)
+    st = _stream(ts)
     need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
     if ws is None and need > 0:
-        ws = workspace(need, x.device, st.value or 0)
+        ws = workspace(need, x.device, ts)
     check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k,
              _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, st))
     return out
 
 
 def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, workspace_=None,
-                 stream=None):
-    """(logits fp16 [m, n], argmax int32 [m]) through qpn_lmhead_nvfp4."""
+                 stream=None, plan: int = 0):
+    """(logits fp16 [m, n], argmax int32 [m]) through qpn_lmhead_nvfp4 (through
+    qpn_debug_run_plan with a forced plan when `plan` > 0)."""
     if pw.fmt != FMT_NVFP4:
         raise ValueError("lm_head needs an NVFP4 blob")
     _x_check(x, pw.k)
@@ -280,11 +318,16 @@ def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, wo
         logits = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
     if argmax is None:
         argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
-    st = _stream(stream)
-    need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k)
-    ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, st.value or 0)
-    check(lib.qpn_lmhead_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax), m, pw.n, pw.k,
-                               _ptr(ws), ws.numel(), st))
+    ts = _torch_stream(stream)
+    st = _stream(ts)
+    need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k, plan)
+    ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, ts)
+    if plan == 0:
+        check(lib.qpn_lmhead_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax), m, pw.n,
+                                   pw.k, _ptr(ws), ws.numel(), st))
+    else:
+        check(lib.qpn_debug_run_plan(OP_LMHEAD_NVFP4, plan, _ptr(pw.blob), _ptr(x), _ptr(logits),
+                                     _ptr(argmax), m, pw.n, pw.k, _ptr(ws), ws.numel(), st))
     return logits, argmax
 
 
@@ -306,9 +349,10 @@ def lmhead_verify_nvfp4(pw: PackedWeight, x: torch.Tensor, draft: torch.Tensor, 
         argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
     if result is None:
         result = torch.empty((2,), dtype=torch.int32, device=x.device)
-    st = _stream(stream)
+    ts = _torch_stream(stream)
+    st = _stream(ts)
     need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k)
-    ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, st.value or 0)
+    ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, ts)
     check(lib.qpn_lmhead_verify_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax),
                                       _ptr(draft) if draft.numel() else None, _ptr(result), m,
                                       pw.n, pw.k, _ptr(ws), ws.numel(), st))
@@ -354,8 +398,3 @@ def debug_read_ceiling(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     """One streaming read of `buf` (the measured read ceiling kernel)."""
     check(lib.qpn_debug_read_ceiling(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                      _stream(stream)))
-
-
-def debug_set_plan(plan: int):
-    """Force the launch plan of later calls (0 = automatic)."""
-    check(lib.qpn_debug_set_plan(int(plan)))

@@ -125,19 +125,16 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * split_workgroups, the workgroups that work on K ranges (split_workgroups
  * / splits panel groups of the last panels, dispatched first).  The other
  * workgroups - 0 unless the plan balances whole panels per CU - each take
- * panels_per_workgroup whole panels.  valu_dot is 1 for the diagnostic
- * plans that contract with VALU dot products instead of the MFMA (only when
- * forced with qpn_debug_set_plan).  For the prefill ops: every workgroup
+ * panels_per_workgroup whole panels.  For the prefill ops: every workgroup
  * covers 8 panels (two wavefronts per panel, one per half of the activation
  * rows), activation_rows is the 32, 64, 128 or 256 rows a workgroup takes,
- * and split_workgroups equals workgroups.  A pure function of the shape (and of
- * a plan forced with qpn_debug_set_plan), independent of any declared
- * maximum.  Any output pointer may be NULL.  Returns QPN_OK or
- * QPN_ERR_SHAPE.  Pure host. */
+ * and split_workgroups equals workgroups.  A pure function of its
+ * arguments, independent of any declared maximum.  Any output pointer may
+ * be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
                           int *waves_per_panel, int *panels_per_workgroup,
                           int *prefetch_depth, int *splits, int *activation_rows,
-                          int64_t *split_workgroups, int *valu_dot);
+                          int64_t *split_workgroups);
 
 /* NVFP4 pack ("pure round" quantisation, lcz.me quantisation-option table,
  * NVFP4-NVIDIA row; format per the lcz.me NVFP4 support table).
@@ -282,14 +279,35 @@ QPN_API int qpn_debug_decode_nvfp4(const uint8_t *codes16, const uint8_t *scales
 QPN_API int qpn_debug_decode_fp8(const uint8_t *codes16, int64_t count,
                          uint16_t *out, void *stream);
 
-/* Diagnostic: forces the launch plan (wavefronts per panel, panels per
- * workgroup, prefetch depth, contraction; ids 1..13, where 11 and 12 repeat
- * 2 and 1 with VALU dot products in place of the MFMA and 13 is the
- * eight-panel plan of large-N calls) of every later GEMM and lm_head call
- * in this process, for A/B timing of configurations on identical inputs.
- * 0 restores the automatic choice.  Returns QPN_ERR_SHAPE for an unknown id
- * (nothing changes).  Not for concurrent use with other calls. */
-QPN_API int qpn_debug_set_plan(int plan);
+/* Diagnostic: the launch plan compiled plan `plan` gives a call of kind
+ * `op` (QPN_OP_GEMM_NVFP4, QPN_OP_GEMM_FP8 or QPN_OP_LMHEAD_NVFP4) with
+ * (m, n, k), given all the workspace it asks for.  Plan ids 1..13 select a
+ * fixed (wavefronts per panel, panels per workgroup, prefetch depth,
+ * contraction) configuration; 11 and 12 repeat 2 and 1 with VALU dot
+ * products in place of the MFMA (valu_dot = 1), 13 is the eight-panel plan
+ * of large-N calls; 0 is the automatic choice (the same answer as
+ * qpn_gemm_plan).  The outputs are those of qpn_gemm_plan plus valu_dot and
+ * workspace_bytes, the workspace the call uses with that plan (as
+ * qpn_workspace_bytes does for the automatic one).  Any output pointer may
+ * be NULL.  QPN_ERR_SHAPE for an unknown op or plan id or an invalid shape.
+ * A pure function of its arguments; pure host. */
+QPN_API int qpn_debug_plan(int op, int plan, int m, int64_t n, int64_t k,
+                           int64_t *workgroups, int *waves_per_panel,
+                           int *panels_per_workgroup, int *prefetch_depth, int *splits,
+                           int *activation_rows, int64_t *split_workgroups, int *valu_dot,
+                           size_t *workspace_bytes);
+
+/* Diagnostic: qpn_gemm_nvfp4 (op QPN_OP_GEMM_NVFP4), qpn_gemm_fp8
+ * (QPN_OP_GEMM_FP8) or qpn_lmhead_nvfp4 (QPN_OP_LMHEAD_NVFP4, `y` being the
+ * logits and `argmax` its argmax output) run with compiled launch plan
+ * `plan` instead of the automatic choice (0 = automatic), for A/B timing and
+ * parity tests of every configuration on identical inputs.  `argmax` is
+ * ignored by the GEMM ops.  Arguments, workspace rules and failure
+ * behaviour as the entry point it runs; QPN_ERR_SHAPE for an unknown op or
+ * plan id.  Touches no state outside its arguments. */
+QPN_API int qpn_debug_run_plan(int op, int plan, const void *packed, const uint16_t *x,
+                               uint16_t *y, int32_t *argmax, int m, int64_t n, int64_t k,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Diagnostic: reads `bytes` (a multiple of 16, at most 2^40) of device
  * memory at `buf` once with the same nontemporal 16-byte loads the GEMM

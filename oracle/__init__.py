@@ -68,6 +68,8 @@ def lib():
         L.qpn_oracle_round_f16_array.restype = None
         L.qpn_oracle_threads.argtypes = []
         L.qpn_oracle_threads.restype = c.c_int
+        L.qpn_oracle_set_threads.argtypes = [c.c_int]
+        L.qpn_oracle_set_threads.restype = None
         _LIB = L
     return _LIB
 
@@ -75,6 +77,11 @@ def lib():
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().qpn_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of later parallel loops (results do not depend on it)."""
+    lib().qpn_oracle_set_threads(int(n))
 
 
 def _p(a):

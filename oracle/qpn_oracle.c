@@ -457,6 +457,15 @@ ORACLE_API void qpn_oracle_argmax_f16(const uint16_t *logits, int m, int64_t n,
 /* Threads the OpenMP loops above run with (reported by the CPU baseline). */
 ORACLE_API int qpn_oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the threads of later parallel loops (the CPU baseline also times the
+ * oracle on one thread).  Results do not depend on it: every loop is
+ * parallel over output rows only. */
+ORACLE_API void qpn_oracle_set_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
 /* Round an FP64 result array to FP16 bit patterns (the returned logits). */
 ORACLE_API void qpn_oracle_round_f16_array(const double *y, int64_t count,
                                            uint16_t *out)

@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(qpn):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     lib = ctypes.CDLL(qpn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -93,21 +93,24 @@ def test_gemm_plan(qpn):
         name = qpn.kernel_name(qpn.FMT_NVFP4 if op != 2 else qpn.FMT_FP8, m, n, k, lmhead=op == 3)
         assert name.startswith("qpn::skinny_gemm_kernel<") and name.endswith(", false>")
         assert pl.valu_dot == 0                               # automatic plans use the MFMA
+        # plan 0 of the diagnostic query is the automatic choice
+        assert qpn.gemm_plan(op, m, n, k, plan=0) == pl
+        assert qpn.workspace_bytes(op, m, n, k, plan=0) == ws
     # 320 panels on 256 CUs: 256 whole panels plus the last 64 split four ways
     pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)
     assert (pl.workgroups, pl.split_workgroups, pl.splits) == (512, 256, 4)
     # the VALU-dot diagnostic plans repeat plans 2 and 1 with the other contraction
-    try:
-        for vd, base in ((11, 2), (12, 1)):
-            qpn.debug_set_plan(base)
-            a = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
-            qpn.debug_set_plan(vd)
-            b = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
-            assert (a.valu_dot, b.valu_dot) == (0, 1)
-            assert dataclasses.replace(a, valu_dot=1) == b
-            assert qpn.kernel_name(qpn.FMT_NVFP4, 8, 17408, 5120).endswith("false, true>")
-    finally:
-        qpn.debug_set_plan(0)
+    auto = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
+    for vd, base in ((11, 2), (12, 1)):
+        a = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120, plan=base)
+        b = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120, plan=vd)
+        assert (a.valu_dot, b.valu_dot) == (0, 1)
+        assert dataclasses.replace(a, valu_dot=1) == b
+        assert qpn.kernel_name(qpn.FMT_NVFP4, 8, 17408, 5120, plan=vd).endswith("false, true>")
+        assert qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 17408, 5120, plan=vd) == \
+            qpn.workspace_bytes(qpn.OP_GEMM_NVFP4, 8, 17408, 5120, plan=base)
+    # asking about a forced plan changes nothing for later calls
+    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120) == auto
     # K = 2^20 at M = 8 cannot be staged whole: it is split
     assert qpn.gemm_plan(1, 8, 64, 1 << 20).splits > 1
     with pytest.raises(qpn.QpnError):
@@ -116,12 +119,45 @@ def test_gemm_plan(qpn):
         qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 9, 16, 32)
 
 
-def test_plan_override_rejects_unknown_ids(qpn):
+def test_forced_plans_reject_unknown_ids(qpn):
+    v = ctypes.c_void_p
+    assert qpn.plan_ids() == list(range(1, 14))
+    for bad in (10 ** 6, -1, 14):
+        with pytest.raises(qpn.QpnError):
+            qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 16, 16, plan=bad)
+        # the run entry point checks the plan before anything else
+        assert qpn.lib.qpn_debug_run_plan(qpn.OP_GEMM_NVFP4, bad, v(A256), v(A16), v(A16), None,
+                                          1, 16, 16, None, 0, None) == 2
+    # prefill ops have no forced plans; unknown ops are rejected
     with pytest.raises(qpn.QpnError):
-        qpn.debug_set_plan(10 ** 6)
-    with pytest.raises(qpn.QpnError):
-        qpn.debug_set_plan(-1)
-    qpn.debug_set_plan(0)
+        qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 32, 16, 16, plan=1)
+    assert qpn.lib.qpn_debug_run_plan(qpn.OP_PREFILL_NVFP4, 1, v(A256), v(A16), v(A16), None,
+                                      1, 16, 16, None, 0, None) == 2
+    # argument checks of the entry point a forced plan runs
+    assert qpn.lib.qpn_debug_run_plan(qpn.OP_GEMM_FP8, 3, v(0), v(A16), v(A16), None,
+                                      1, 16, 16, None, 0, None) == 1
+    assert qpn.lib.qpn_debug_run_plan(qpn.OP_LMHEAD_NVFP4, 13, v(A256), v(A16), v(A16), v(0),
+                                      1, 16, 16, v(A16), 4096, None) == 1
+
+
+def test_workspace_stays_below_2_31(qpn):
+    """Split-K partials are addressed with 32-bit offsets: no plan asks for
+    2^31 bytes or more, down to the documented maximum sizes."""
+    big = ctypes.c_size_t(-1).value
+    for op in (qpn.OP_GEMM_NVFP4, qpn.OP_GEMM_FP8, qpn.OP_LMHEAD_NVFP4, qpn.OP_PREFILL_NVFP4,
+               qpn.OP_PREFILL_FP8):
+        ms = (1, 2, 4, 8) if op <= 3 else (1, 8, 9, 16, 17, 64, 256)
+        for m in ms:
+            for n, k in [(1 << 24, 1 << 20), (524288, 524288), (1 << 24, 16), (48, 1 << 20),
+                         (151936, 5120), (5120, 17408), (262144, 1 << 20)]:
+                ws = qpn.workspace_bytes(op, m, n, k)
+                assert ws == big or ws < (1 << 31), (op, m, n, k, ws)
+                for plan in (qpn.plan_ids() if op <= 3 else ()):
+                    try:
+                        wsp = qpn.workspace_bytes(op, m, n, k, plan=plan)
+                    except qpn.QpnError:   # that plan cannot run this shape at all
+                        continue
+                    assert wsp < (1 << 31), (op, m, n, k, plan, wsp)
 
 
 def _split_ws(pl):

@@ -214,42 +214,34 @@ PLAN_IDS = plan_ids()
 @pytest.mark.parametrize("plan", PLAN_IDS)
 def test_every_plan_against_oracle(plan):
     qpn = need_gpu()
-    try:
-        qpn.debug_set_plan(plan)
-        for n, k in PLAN_SHAPES:
-            w = synth.weights(n, k, seed=7 * n + k)
-            x8 = synth.activations(8, k, seed=7 * n + k)
-            pw4, pw8 = qpn.pack_nvfp4(dev(w)), qpn.pack_fp8(dev(w))
-            codes, scales, g = oracle.pack_nvfp4(w)
-            c8, rs = oracle.pack_fp8(w)
-            for m in (1, 2, 3, 4, 5, 8):
-                log(f"plan {plan}: {n}x{k} m={m}")
-                parity(host(qpn.gemm(pw4, dev(x8[:m]))), oracle.gemm_nvfp4(codes, scales, g, x8[:m]),
-                       f"plan {plan} nvfp4 {n}x{k} m={m}")
-                parity(host(qpn.gemm(pw8, dev(x8[:m]))), oracle.gemm_fp8(c8, rs, x8[:m]),
-                       f"plan {plan} fp8 {n}x{k} m={m}")
-    finally:
-        qpn.debug_set_plan(0)
+    for n, k in PLAN_SHAPES:
+        w = synth.weights(n, k, seed=7 * n + k)
+        x8 = synth.activations(8, k, seed=7 * n + k)
+        pw4, pw8 = qpn.pack_nvfp4(dev(w)), qpn.pack_fp8(dev(w))
+        codes, scales, g = oracle.pack_nvfp4(w)
+        c8, rs = oracle.pack_fp8(w)
+        for m in (1, 2, 3, 4, 5, 8):
+            log(f"plan {plan}: {n}x{k} m={m}")
+            parity(host(qpn.gemm(pw4, dev(x8[:m]), plan=plan)),
+                   oracle.gemm_nvfp4(codes, scales, g, x8[:m]), f"plan {plan} nvfp4 {n}x{k} m={m}")
+            parity(host(qpn.gemm(pw8, dev(x8[:m]), plan=plan)), oracle.gemm_fp8(c8, rs, x8[:m]),
+                   f"plan {plan} fp8 {n}x{k} m={m}")
 
 
 @pytest.mark.parametrize("plan", PLAN_IDS)
 def test_every_plan_full_size_rows(plan):
     """Full gate/up and down shapes at M=1 and 8 under each plan, sampled rows."""
     qpn = need_gpu()
-    try:
-        qpn.debug_set_plan(plan)
-        for n, k in ((17408, 5120), (5120, 17408)):
-            w = synth.weights(n, k, seed=0)
-            x8 = synth.activations(8, k, seed=0)
-            pw = qpn.pack_nvfp4(dev(w))
-            rows = _sample_rows(n, 96, seed=n + plan)
-            ref = _oracle_nvfp4_rows(w, rows, x8)
-            for m in (1, 8):
-                log(f"plan {plan}: full {n}x{k} m={m}")
-                y = host(qpn.gemm(pw, dev(x8[:m])))
-                parity(y[:, rows], ref[:m], f"plan {plan} nvfp4 {n}x{k} m={m}")
-    finally:
-        qpn.debug_set_plan(0)
+    for n, k in ((17408, 5120), (5120, 17408)):
+        w = synth.weights(n, k, seed=0)
+        x8 = synth.activations(8, k, seed=0)
+        pw = qpn.pack_nvfp4(dev(w))
+        rows = _sample_rows(n, 96, seed=n + plan)
+        ref = _oracle_nvfp4_rows(w, rows, x8)
+        for m in (1, 8):
+            log(f"plan {plan}: full {n}x{k} m={m}")
+            y = host(qpn.gemm(pw, dev(x8[:m]), plan=plan))
+            parity(y[:, rows], ref[:m], f"plan {plan} nvfp4 {n}x{k} m={m}")
 
 
 HYBRID = [("nvfp4", 5120, 17408, (1, 2)), ("nvfp4", 4805, 16000, (1, 2)),

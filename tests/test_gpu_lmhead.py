@@ -1,13 +1,13 @@
 """NVFP4 lm_head with fused argmax against the oracle.
 
-Logits: the GEMM parity bar.  Argmax: bit-exact against the oracle's lowest
-index of the FP16-rounded FP64 logits, with one allowance for a property of
-the arithmetic, not of the code: when two candidates' FP64 logits round to
-FP16 values within the FP32 accumulation error of each other, the GPU's own
-FP16 logits may legitimately order them differently.  Such a row must still
-pick a candidate within 2 FP16 ulps of the true maximum and must equal the
-lowest-index argmax of the GPU's own returned logits; any other mismatch
-fails.
+Logits: the GEMM parity bar.  Argmax: the oracle's lowest index of the
+FP16-rounded FP64 logits, row by row (gpu_util.check_argmax).  A row may
+differ only where a property of the arithmetic, not of the code, allows it:
+the two candidates' FP64 logits lie within the FP32 accumulation error band
+of each other or of an FP16 rounding boundary.  The count of such rows is
+reported in the terminal summary; at the full 151936-row vocabulary with the
+seed-0 inputs it must be zero (every row's top two FP16 logits are 23 or
+more ulps apart there).
 """
 import numpy as np
 import pytest
@@ -15,38 +15,10 @@ import torch
 
 import oracle
 from fp8_quantized_skinny_qpn_amd import synth
+from gpu_util import check_argmax as _check_argmax
 from gpu_util import dev, host, log, need_gpu, parity, plan_ids
 
 pytestmark = pytest.mark.gpu
-
-
-def _ulp16(v):
-    v = abs(float(v))
-    if v < 2.0 ** -14:
-        return 2.0 ** -24
-    return 2.0 ** (np.floor(np.log2(v)) - 10)
-
-
-def _check_argmax(am_gpu, logits_gpu, y_ref, what):
-    lg = np.asarray(logits_gpu)
-    # self-consistency: the returned index is the lowest argmax of the returned logits
-    assert np.array_equal(am_gpu, np.argmax(lg, axis=1).astype(np.int32)), f"{what}: self"
-    am_ref = oracle.argmax_f16(oracle.round_f16(y_ref))
-    ambiguous = 0
-    for mi in range(y_ref.shape[0]):
-        a, b = int(am_gpu[mi]), int(am_ref[mi])
-        if a == b:
-            continue
-        top = float(y_ref[mi, b])
-        assert top - float(y_ref[mi, a]) <= 2 * _ulp16(top), \
-            f"{what}: row {mi} GPU {a} ({y_ref[mi, a]!r}) vs oracle {b} ({top!r})"
-        ambiguous += 1
-    assert ambiguous <= max(1, y_ref.shape[0] // 4), f"{what}: {ambiguous} ambiguous rows"
-    gap = []
-    for mi in range(y_ref.shape[0]):
-        srt = np.sort(oracle.round_f16(y_ref[mi:mi + 1])[0].astype(np.float64))
-        gap.append((srt[-1] - srt[-2]) / _ulp16(srt[-1]))
-    log(f"{what}: top-2 gap in fp16 ulps per row {['%.1f' % g for g in gap]}, ambiguous {ambiguous}")
 
 
 @pytest.mark.parametrize("n,k", [(1000, 256), (4099, 1024), (160, 5120)])
@@ -139,7 +111,9 @@ def test_lmhead_full_vocab(m):
     y_ref = oracle.gemm_nvfp4(codes, scales, g, x)
     rows = np.random.default_rng(0).choice(n, 4096, replace=False)
     parity(lg[:, rows], y_ref[:, rows], f"lmhead full m={m} (sampled logits)")
-    _check_argmax(am, lg, y_ref, f"lmhead full m={m}")
+    # seed 0: no row has a rounding boundary near its top candidates, so the
+    # argmax must equal the oracle's on every row
+    _check_argmax(am, lg, y_ref, f"lmhead full m={m}", max_ambiguous=0)
 
 
 @pytest.mark.parametrize("plan", plan_ids())
@@ -149,18 +123,14 @@ def test_lmhead_every_plan(plan):
     w = synth.weights(n, k, seed=plan)
     x = synth.activations(8, k, seed=plan)
     codes, scales, g = oracle.pack_nvfp4(w)
-    try:
-        qpn.debug_set_plan(plan)
-        pw = qpn.pack_nvfp4(dev(w))
-        for m in (1, 2, 5, 8):
-            log(f"lmhead plan {plan} {n}x{k} m={m}")
-            lg, am = qpn.lmhead_nvfp4(pw, dev(x[:m]))
-            lg, am = host(lg), host(am)
-            y_ref = oracle.gemm_nvfp4(codes, scales, g, x[:m])
-            parity(lg, y_ref, f"lmhead plan {plan} m={m}")
-            _check_argmax(am, lg, y_ref, f"lmhead plan {plan} m={m}")
-    finally:
-        qpn.debug_set_plan(0)
+    pw = qpn.pack_nvfp4(dev(w))
+    for m in (1, 2, 5, 8):
+        log(f"lmhead plan {plan} {n}x{k} m={m}")
+        lg, am = qpn.lmhead_nvfp4(pw, dev(x[:m]), plan=plan)
+        lg, am = host(lg), host(am)
+        y_ref = oracle.gemm_nvfp4(codes, scales, g, x[:m])
+        parity(lg, y_ref, f"lmhead plan {plan} m={m}")
+        _check_argmax(am, lg, y_ref, f"lmhead plan {plan} m={m}")
 
 
 def test_lmhead_leaves_workspace_zeroed():

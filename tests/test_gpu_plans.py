@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from fp8_quantized_skinny_qpn_amd import synth
-from gpu_util import dev, host, log, need_gpu, parity
+from gpu_util import check_argmax, dev, host, log, need_gpu, parity
 
 pytestmark = pytest.mark.gpu
 
@@ -61,8 +61,8 @@ def test_automatic_plan_branch(fmt, n, k, m, wpp, ppw, whole, branch):
 
 def test_lmhead_eight_panel_plan():
     """The lm_head (argmax fused) through the eight-panel plan: logits within
-    the parity bar and the argmax equal to the argmax of the returned
-    logits and to the oracle's on rows whose top two logits are apart."""
+    the parity bar and the argmax equal to the oracle's on every row (apart
+    from rows made ambiguous by FP16 rounding, see gpu_util.check_argmax)."""
     qpn = need_gpu()
     n, k, m = 32768, 512, 8
     pl = qpn.gemm_plan(qpn.OP_LMHEAD_NVFP4, m, n, k)
@@ -74,9 +74,4 @@ def test_lmhead_eight_panel_plan():
     lg, am = host(lg), host(am)
     y_ref = ref(x)
     parity(lg, y_ref, "lm_head eight-panel plan")
-    assert np.array_equal(am, np.argmax(lg, axis=1))
-    ref_am = oracle.argmax_f16(oracle.round_f16(y_ref))
-    srt = np.sort(y_ref, axis=1)
-    apart = (srt[:, -1] - srt[:, -2]) > 1e-2
-    assert apart.sum() >= m // 2
-    assert np.array_equal(am[apart], ref_am[apart])
+    check_argmax(am, lg, y_ref, "lm_head eight-panel plan")
