@@ -24,10 +24,25 @@ bool f8_shape_ok(int64_t n, int64_t k) {
   return n >= 0 && k >= 0 && n <= kMaxN && k <= kMaxK && k % 8 == 0;
 }
 
-// Device check: the current device must be gfx950.  Cached per device id.
+// The library's own scratch for callers that cannot allocate
+// (qpn_gemm_nvfp4_noalloc): split-K partials and counters in a file-scope
+// device array.  Each GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: only the address that
+// hipGetSymbolAddress returns for each device (g_scratch) is passed to
+// kernels.  It starts zero-filled (static storage) and every call leaves it
+// zero-filled, as any workspace.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device check and set-up, once per device id with that device current:
+// the device must be gfx950, and the device address of `scratch` is
+// looked up.  Every entry point runs it before anything is enqueued.
 constexpr int kMaxDevices = 64;
 std::once_flag g_once[kMaxDevices];
 int g_ok[kMaxDevices];
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device (NULL if unknown)
+std::once_flag g_scratch_cleared[kMaxDevices];
 
 int device_check() {
   int dev = -1;
@@ -38,6 +53,12 @@ int device_check() {
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
         std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
       g_ok[dev] = 1;
+    void* p = nullptr;
+    if (g_ok[dev] && hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess &&
+        p != nullptr && ((uintptr_t)p % 256) == 0)
+      g_scratch[dev] = p;
+    else
+      (void)hipGetLastError();  // no scratch: only the no-allocation entry point reports it
   });
   return g_ok[dev] ? QPN_OK : QPN_ERR_DEVICE;
 }
@@ -91,6 +112,8 @@ const char* qpn_status_string(int status) {
     case QPN_ERR_BUFFER: return "QPN_ERR_BUFFER: buffer smaller than required";
     case QPN_ERR_DEVICE: return "QPN_ERR_DEVICE: current device is not a usable gfx950";
     case QPN_ERR_LAUNCH: return "QPN_ERR_LAUNCH: kernel launch failed";
+    case QPN_ERR_SCRATCH:
+      return "QPN_ERR_SCRATCH: the call needs more than the library's static scratch";
     default: return "QPN: unknown status";
   }
 }
@@ -266,6 +289,31 @@ int qpn_gemm_nvfp4(const void* packed, const uint16_t* x, uint16_t* y, int m, in
 int qpn_gemm_fp8(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n, int64_t k,
                  void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_entry(kFmtFp8, 0, packed, x, y, m, n, k, workspace, workspace_bytes, stream);
+}
+
+int qpn_gemm_nvfp4_noalloc(const void* packed, const uint16_t* x, uint16_t* y, int m, int64_t n,
+                           int64_t k, void* stream) {
+  int rc = gemm_common_checks(kFmtNvfp4, packed, x, y, m, n, k);
+  if (rc != QPN_OK) return rc;
+  if (m == 0 || n == 0) return QPN_OK;
+  rc = device_check();
+  if (rc != QPN_OK) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || !g_scratch[dev])
+    return QPN_ERR_DEVICE;
+  void* ws = g_scratch[dev];
+  // the plan qpn_gemm_nvfp4 uses with a workspace of kScratchBytes: the same
+  // kernels, with fewer K splits only where more would not fit
+  GemmLaunch l;
+  const int lr = gemm_launch_for(kFmtNvfp4, m, n, k, 0, kScratchBytes, 0, &l);
+  if (lr != kGemmLaunchOk) return lr == kGemmNoWorkspace ? QPN_ERR_SCRATCH : QPN_ERR_SHAPE;
+  // belt and braces: clear the scratch in stream order before its first use
+  // on this device (it is zero-filled from the start and every call leaves it so)
+  hipError_t fe = hipSuccess;
+  std::call_once(g_scratch_cleared[dev], [&]() { fe = launch_zero_fill(ws, kScratchBytes, stream); });
+  if (fe != hipSuccess) return QPN_ERR_LAUNCH;
+  GemmArgs a{packed, x, y, m, n, k, nullptr, ws, stream};
+  return launch_status(launch_gemm(kFmtNvfp4, false, a, l));
 }
 
 namespace {

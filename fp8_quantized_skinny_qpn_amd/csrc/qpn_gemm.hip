@@ -785,6 +785,23 @@ hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmL
   return launch_plan<kFmtFp8, false>(a, l);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* __restrict__ p, int64_t count16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count16; i += stride)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+}  // namespace
+
+hipError_t launch_zero_fill(void* p, size_t bytes, void* stream) {
+  const int64_t count16 = (int64_t)(bytes / 16);
+  const int64_t blocks = std::min<int64_t>(1024, (count16 + 255) / 256);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (u32x4*)p, count16);
+  return hipGetLastError();
+}
+
 hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const int32_t* draft,
                                   int32_t* result, void* stream) {
   hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(kLanes * m), 0, (hipStream_t)stream,

@@ -77,6 +77,10 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
 // 3.2 us longer, and with 1024 slots the final pass's reads cost as much.
 constexpr int kArgmaxSlots = 256;
 
+// Zero `bytes` (a multiple of 16) of device memory at p (16-byte aligned)
+// with a kernel on `stream`: a plain kernel node when captured into a graph.
+hipError_t launch_zero_fill(void* p, size_t bytes, void* stream);
+
 // Launch the GEMM (and, with `argmax`, the per-panel argmax keys).
 hipError_t launch_gemm(uint32_t fmt, bool argmax, const GemmArgs& a, const GemmLaunch& l);
 

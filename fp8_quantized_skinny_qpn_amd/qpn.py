@@ -51,6 +51,7 @@ def _load():
         "qpn_requant_fp8_to_nvfp4": ([vp, sz, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_gemm_nvfp4_noalloc": ([vp, vp, vp, i32, i64, i64, vp], i32),
         "qpn_gemm_prefill_nvfp4": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_gemm_prefill_fp8": ([vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
         "qpn_lmhead_nvfp4": ([vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
@@ -76,7 +77,7 @@ lib = _load()
 EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_fp8_packed_bytes", "qpn_workspace_bytes", "qpn_gemm_plan", "qpn_pack_nvfp4", "qpn_pack_fp8",
             "qpn_requant_fp8_to_nvfp4",
-            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_gemm_prefill_nvfp4", "qpn_gemm_prefill_fp8",
+            "qpn_gemm_nvfp4", "qpn_gemm_fp8", "qpn_gemm_nvfp4_noalloc", "qpn_gemm_prefill_nvfp4", "qpn_gemm_prefill_fp8",
             "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
             "qpn_debug_unpack_nvfp4",
             "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",

@@ -78,6 +78,7 @@ extern "C" {
 #define QPN_ERR_BUFFER 4 /* packed or workspace buffer smaller than needed */
 #define QPN_ERR_DEVICE 5 /* current device is not gfx950 or not usable     */
 #define QPN_ERR_LAUNCH 6 /* the HIP runtime rejected a kernel launch       */
+#define QPN_ERR_SCRATCH 7 /* needs more than the static scratch (noalloc)  */
 
 /* Formats, for qpn_workspace_bytes. */
 #define QPN_OP_GEMM_NVFP4 1
@@ -184,6 +185,24 @@ QPN_API int qpn_requant_fp8_to_nvfp4(const void *fp8_packed, size_t fp8_bytes, i
 QPN_API int qpn_gemm_nvfp4(const void *packed, const uint16_t *x, uint16_t *y, int m,
                    int64_t n, int64_t k, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/* qpn_gemm_nvfp4 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same product, arguments (minus the workspace), kernels and failure
+ * behaviour as qpn_gemm_nvfp4.  The split-K partials and counters live in
+ * the library's own static device array (4 MiB per GPU, allocated when the
+ * library's code is loaded on that GPU and held until the process ends);
+ * this call allocates nothing, and nothing else is needed from the caller.
+ * The launch plan is the one qpn_gemm_nvfp4 uses when given 4 MiB of
+ * workspace: fewer K splits where more would not fit.  Returns
+ * QPN_ERR_SCRATCH when even the fewest K splits the activation slice needs
+ * exceed 4 MiB (only for very large n * k at m > 4); QPN_ERR_DEVICE when the
+ * scratch could not be located on the current device.  Every call on one
+ * GPU shares that GPU's scratch and leaves it zero-filled: calls that
+ * overlap on one GPU (concurrent streams, or host threads on one device)
+ * race and must be serialised by the caller. */
+QPN_API int qpn_gemm_nvfp4_noalloc(const void *packed, const uint16_t *x, uint16_t *y, int m,
+                                   int64_t n, int64_t k, void *stream);
 
 /* QPN FP8 skinny GEMM (taozi.news section "自研 QPN 内核", the FP8 M=1..4
  * path; section "v1.1 的关键改进" for FP8 regions).
