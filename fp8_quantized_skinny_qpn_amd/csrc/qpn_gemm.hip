@@ -37,16 +37,15 @@
 //     its last k-step a wavefront keeps issuing loads through a descriptor
 //     of size zero (no memory access, zeros back) instead of branching, so
 //     the ring of D loads in flight has static slots and static waits.
-//   * When S > 1, each workgroup writes its FP32 partial tiles to the
-//     workspace and bumps its panel group's counter; the last to arrive sums
-//     the S partials in split order and writes the FP16 result.  Partials
-//     and counters use device-scope relaxed atomics (write-through stores and
-//     coherent loads), ordered by waiting for the stores before the counter
-//     update: no whole-cache write-back or invalidate is needed.
+//   * When S > 1, the S partial tiles of a panel meet pairwise up a fixed
+//     binary tree over the split index, each pair of accumulators inside one
+//     64-bit atomic exchange (step 5): one device-scope round trip per tree
+//     level, no arrival counter, barrier or cache maintenance.
 //
 // The partial tiles of a panel's W wavefronts are summed through LDS in a
-// fixed order and splits in split order, so results are deterministic and
-// independent of where a row sits in the matrix.
+// fixed order and splits by a fixed tree of commutative additions, so
+// results are deterministic and independent of where a row sits in the
+// matrix.
 #include <algorithm>
 
 #include "qpn_common.h"
@@ -123,8 +122,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 struct SplitArgs {
   int splits;            // S: K ranges per panel group
   int split_steps;       // k-steps per K range (the last may be shorter)
-  float* partial;        // [S][groups][G][64 lanes][4] FP32 partial tiles
-  uint32_t* counters;    // [groups] arrivals; zero between calls
+  uint64_t* slots;       // [tree nodes][groups][G][64 lanes][2] exchange slots; zero between calls
   int split_wgs;         // workgroups [0, split_wgs) work on K ranges of panels [full_panels, P)
   int full_panels;       // workgroups from split_wgs on take panels [0, full_panels) whole
 };
@@ -399,51 +397,82 @@ __global__ __launch_bounds__(kLanes * G * W) void skinny_gemm_kernel(
     }
   }
 
-  // ---- 5. split-K: partial tiles, arrival count, last arriver sums ----
-  if (S > 1) {
-    // Partial tiles go through a buffer descriptor with the device-scope
-    // cache policy (sc1: written through to memory, read coherently), one
-    // 16-byte access per lane, so no cache maintenance is needed.
-    constexpr int kDevScope = 16;  // sc1
-    const int64_t tiles = (int64_t)S * groups * G;
-    const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)sp.partial, (short)0, (int)(tiles * kLanes * 16), kRsrcFlags);
-    const int mine = (int)((((int64_t)split * groups + grp) * G + gi) * kLanes + lane) * 16;
-    if (lead)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), pres, mine, 0, kDevScope);
-    wait_vmcnt<0>();  // this wavefront's partial stores are complete at device scope
-    bare_barrier();
-    uint32_t* arrived = reinterpret_cast<uint32_t*>(smem);
-    if (wv == 0 && lane == 0) {
-      const uint32_t before =
-          __hip_atomic_fetch_add(sp.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // the last arrival also re-arms the counter for the next call
-      if (before == (uint32_t)(S - 1))
-        __hip_atomic_store(sp.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *arrived = before;
-    }
-    wait_lgkmcnt0();
-    bare_barrier();
-    if (*arrived != (uint32_t)(S - 1)) return;  // uniform over the workgroup
-    if (lead) {
-      const int per_split = (int)(groups * G * kLanes * 16);
-      const int first = (int)((((int64_t)grp) * G + gi) * kLanes + lane) * 16;
-      acc = float4v{0.f, 0.f, 0.f, 0.f};
-      for (int sx = 0; sx < S; ++sx)
-        acc += __builtin_bit_cast(
-            float4v, __builtin_amdgcn_raw_buffer_load_b128(pres, first + sx * per_split, 0, kDevScope));
-      // this is the only reader: clear the partials so the workspace is all
-      // zeros again when the call ends (whatever layout the next call uses)
-      for (int sx = 0; sx < S; ++sx)
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres, first + sx * per_split, 0, 0);
-    }
-  }
   if (!lead || !active) return;
+  const int mcol = lane & 15;
+  const int64_t n0 = p * kPanelRows + 4 * (lane >> 4);
+
+  // ---- 5. split-K: pairwise exchange up a fixed binary tree ----
+  // The S partial tiles of a panel are summed by a binary tree over the
+  // split index (node (l, i) adds children 2i and 2i + 1 of level l - 1; an
+  // odd last child moves up unchanged).  Each node is one 64-bit slot per
+  // lane and pair of accumulators.  The two children meet with an atomic
+  // exchange of their bit-inverted values: the first to arrive finds the
+  // slot at zero and leaves its value there (it is done with that pair);
+  // the second gets it back, adds it to its own and climbs on.  FP32
+  // addition is commutative, so every node's value, and the result, has the
+  // same bits whatever the arrival order.  The data travels inside the
+  // atomic itself (agent scope), so no store acknowledgement, arrival
+  // counter, barrier or cache maintenance is needed, and every slot is
+  // reset to zero by the partner that read it.  An inverted partial is
+  // never zero: that would need two FP32 values with all bits set, a NaN
+  // pattern no arithmetic produces.
+  if (S > 1) {
+    const int64_t node_stride = groups * G * kLanes * 2;  // slots per tree node
+    uint64_t* const mine = sp.slots + ((int64_t)grp * G + gi) * kLanes * 2 + lane * 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float v0 = acc[2 * q], v1 = acc[2 * q + 1];
+      int idx = split, first = 0, width = S;
+      bool last = true;
+      while (width > 1) {
+        const int parents = (width + 1) >> 1;
+        if ((idx ^ 1) < width) {
+          uint64_t* slot = mine + (int64_t)(first + (idx >> 1)) * node_stride + q;
+          const uint64_t val =
+              ~(((uint64_t)__builtin_bit_cast(uint32_t, v1) << 32) | __builtin_bit_cast(uint32_t, v0));
+          const uint64_t old =
+              __hip_atomic_exchange(slot, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (old == 0) {
+            last = false;
+            break;
+          }
+          const uint64_t o = ~old;
+          v0 = __builtin_bit_cast(float, (uint32_t)o) + v0;
+          v1 = __builtin_bit_cast(float, (uint32_t)(o >> 32)) + v1;
+          __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        idx >>= 1;
+        first += parents;
+        width = parents;
+      }
+      if (!last) continue;
+      // this lane holds the sums of panel rows 4 (lane >> 4) + 2 q + e
+      uint16_t hq[2];
+      uint64_t best = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int v = 2 * q + e;
+        const int64_t nn = n0 + v;
+        const float sc = FMT == kFmtNvfp4 ? h_scale : row_scale[v];
+        const _Float16 o = valid ? (_Float16)(sc * (e ? v1 : v0)) : (_Float16)__builtin_nanf("");
+        hq[e] = __builtin_bit_cast(uint16_t, o);
+        if (mcol < m && nn < n) y[(int64_t)mcol * n + nn] = hq[e];
+        if (ARGMAX && nn < n) {
+          const uint64_t key = argmax_key(hq[e], (uint32_t)nn);
+          best = key > best ? key : best;
+        }
+      }
+      if constexpr (ARGMAX) {
+        if (mcol < m && best != 0)
+          __hip_atomic_fetch_max(keys + (int64_t)mcol * kArgmaxSlots + (int)(p % kArgmaxSlots), best,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
 
   // ---- 6. epilogue.  Lane holds D[i][j] for j = lane & 15 (activation
   // row) and i = 4 (lane >> 4) + v (panel row). ----
-  const int mcol = lane & 15;
-  const int64_t n0 = p * kPanelRows + 4 * (lane >> 4);
   uint16_t h[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -536,11 +565,8 @@ hipError_t launch_t(const GemmArgs& a, const GemmLaunch& l) {
   const int xbytes = ((l.slice_steps * (Fmt<FMT>::kKStep / 8) * MB + 63) / 64) * 1024;
   const int red = G * W * kLanes * 16;
   const size_t lds = (size_t)(xbytes > red ? xbytes : red);
-  SplitArgs sp{l.splits, l.split_steps, nullptr, nullptr, (int)l.split_wgs, (int)l.full_panels};
-  if (l.splits > 1) {
-    sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
-    sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
-  }
+  SplitArgs sp{l.splits, l.split_steps, nullptr, (int)l.split_wgs, (int)l.full_panels};
+  if (l.splits > 1) sp.slots = reinterpret_cast<uint64_t*>((uint8_t*)a.ws + l.ws_slots_offset);
   hipLaunchKernelGGL((skinny_gemm_kernel<FMT, W, G, D, MB, ARGMAX, VDOT>),
                      dim3((unsigned)l.workgroups), dim3(kLanes * G * W), lds,
                      (hipStream_t)a.stream, (const uint8_t*)a.packed, a.x, a.y, a.m, a.n, a.k, sp,
@@ -603,6 +629,12 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
 }
 
 }  // namespace
+
+int split_tree_nodes(int s) {
+  int nodes = 0;
+  for (int width = s; width > 1; width = (width + 1) / 2) nodes += (width + 1) / 2;
+  return nodes;
+}
 
 int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16; }
 
@@ -703,10 +735,11 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   if (smin < 1) smin = 1;
   if (smin > J && J > 0) smin = J;
   int64_t S = smin;
+  // exchange slots: one 1 KiB tile (64 lanes x two 64-bit slots) per panel
+  // per node of the split tree
   auto need_for = [&](int64_t s, int64_t g) -> size_t {
     if (s <= 1) return 0;
-    const size_t counters = ((size_t)g * 4 + 255) / 256 * 256;
-    return counters + (size_t)s * g * pl.panels_per_workgroup * kLanes * 16;
+    return (size_t)split_tree_nodes((int)s) * g * pl.panels_per_workgroup * kLanes * 16;
   };
   // the kernel addresses the workspace with 32-bit offsets: a split launch
   // must fit below 2^31 bytes (and the given workspace)
@@ -742,8 +775,7 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
         out->full_panels = full;
         out->workgroups = gs * s0 + full / G;
         out->slice_steps = (int)J;
-        out->ws_counters_offset = ws_offset;
-        out->ws_partial_offset = ws_offset + (((size_t)gs * 4 + 255) / 256 * 256);
+        out->ws_slots_offset = ws_offset;
         out->ws_needed = ws_offset + need_for(s0, gs);
         return kGemmLaunchOk;
       }
@@ -772,8 +804,7 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   out->full_panels = 0;
   out->workgroups = groups * S;
   out->slice_steps = (int)steps;
-  out->ws_counters_offset = ws_offset;
-  out->ws_partial_offset = ws_offset + (((size_t)groups * 4 + 255) / 256 * 256);
+  out->ws_slots_offset = ws_offset;
   out->ws_needed = ws_offset + need(S);
   return kGemmLaunchOk;
 }

@@ -47,10 +47,13 @@ struct GemmLaunch {
   int64_t full_panels;  // panels [0, full_panels) taken whole by the other workgroups
   int64_t workgroups;   // grid size
   int slice_steps;      // k-steps of the largest activation slice a workgroup stages
-  size_t ws_counters_offset;
-  size_t ws_partial_offset;
+  size_t ws_slots_offset;  // split-K exchange slots (zero between calls)
   size_t ws_needed;     // bytes of workspace this launch uses (from offset 0)
 };
+
+// Nodes of the binary tree that sums s split partials pairwise (an odd last
+// child moves up a level unchanged): sum over levels of ceil(width / 2).
+int split_tree_nodes(int s);
 
 // Activation rows staged per LDS slice for m rows (1, 2, 4 or 8).
 int gemm_activation_rows(int m);

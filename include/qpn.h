@@ -39,8 +39,8 @@
  *     it records its own n, k and scales, so GEMM calls need no host reads.
  *     A GEMM reads at most qpn_*_packed_bytes(n, k) bytes of `packed` for
  *     its own format; passing a smaller buffer is undefined behaviour.
- *   - Workspace (split-K partial sums and arrival counters, lm_head argmax
- *     keys) must be zero-filled before its first use; every call leaves it
+ *   - Workspace (split-K exchange slots, prefill partial sums and arrival
+ *     counters, lm_head argmax keys) must be zero-filled before its first use; every call leaves it
  *     zero-filled again, so a workspace is zeroed once and then reused.
  *     Calls that share a workspace must not overlap.
  *   - Argument checks run on the host before anything is enqueued; on any
@@ -105,8 +105,9 @@ QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
 
 /* Workspace bytes a call of kind `op` (QPN_OP_*) with these sizes uses for
  * its preferred launch plan: 0 when that plan does not split K (the GEMMs
- * then accept a NULL workspace), else room for per-split FP32 partial tiles
- * and per-panel-group counters; the lm_head needs at least 8 * m * 256
+ * then accept a NULL workspace), else room for the slots in which the K
+ * splits' partial sums meet (1 KiB per 16-row panel per node of the
+ * pairwise tree over the splits); the lm_head needs at least 8 * m * 256
  * bytes for its argmax keys plus any split-K room.  A call
  * given less workspace than this still runs, with fewer K splits, as long as
  * the fewest splits whose activation slice (m * K / splits FP16 values) fits

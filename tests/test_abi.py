@@ -160,9 +160,23 @@ def test_workspace_stays_below_2_31(qpn):
                     assert wsp < (1 << 31), (op, m, n, k, plan, wsp)
 
 
+def _tree_nodes(s):
+    """Nodes of the pairwise tree that sums s split partials."""
+    nodes, width = 0, s
+    while width > 1:
+        nodes += (width + 1) // 2
+        width = (width + 1) // 2
+    return nodes
+
+
 def _split_ws(pl):
+    """One 1 KiB exchange tile per panel per node of the split tree."""
     groups = pl.split_workgroups // pl.splits
-    return 0 if pl.splits == 1 else -(-groups * 4 // 256) * 256 + pl.splits * groups * pl.panels_per_workgroup * 1024
+    return 0 if pl.splits == 1 else _tree_nodes(pl.splits) * groups * pl.panels_per_workgroup * 1024
+
+
+def test_split_tree_nodes():
+    assert [_tree_nodes(s) for s in (1, 2, 3, 4, 5, 7, 8)] == [0, 1, 3, 3, 6, 7, 7]
 
 
 def test_workspace_sizes(qpn):
