@@ -12,7 +12,10 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqpn.so")
+# QPN_SANITIZED_BUILD=1 loads the host-sanitized copy of the library
+# (build(sanitize=True), used only by tests/run_sanitized.py on the CPU).
+LIB_PATH = (os.path.join(os.path.dirname(_HERE), "_build", "sanitize", "libqpn.so")
+            if os.environ.get("QPN_SANITIZED_BUILD") == "1" else os.path.join(_HERE, "libqpn.so"))
 
 QPN_OK = 0
 OP_GEMM_NVFP4 = 1

@@ -21,9 +21,11 @@ def lib():
     """Load the oracle library, compiling it first if it is not built."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        # QPN_SANITIZED_BUILD=1: the ASan/UBSan copy (tests/run_sanitized.py)
+        path = _build.SANITIZED_LIB if os.environ.get("QPN_SANITIZED_BUILD") == "1" else _build.LIB
+        if not os.path.exists(path):
+            _build.build(sanitize=path != _build.LIB)
+        L = ctypes.CDLL(path)
         c = ctypes
         L.qpn_oracle_e2m1_value.argtypes = [c.c_int]
         L.qpn_oracle_e2m1_value.restype = c.c_double

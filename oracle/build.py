@@ -2,6 +2,10 @@
 
 Plain gcc, C11, FP64 arithmetic with contraction off so every FP32 pack step
 is a single IEEE round-to-nearest operation, OpenMP over output rows only.
+
+build(sanitize=True) builds it with AddressSanitizer and
+UndefinedBehaviorSanitizer into _build/sanitize/libqpn_oracle.so for the CPU
+test suite (tests/run_sanitized.py); it never replaces the normal library.
 """
 import os
 import subprocess
@@ -10,6 +14,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qpn_oracle.c")
 LIB = os.path.join(HERE, "libqpn_oracle.so")
+SANITIZED_LIB = os.path.join(os.path.dirname(HERE), "_build", "sanitize", "libqpn_oracle.so")
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g"]
 
 CFLAGS = [
     "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp",
@@ -18,17 +25,19 @@ CFLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     """Compile the oracle unconditionally; return the library path."""
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    lib = SANITIZED_LIB if sanitize else LIB
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    tmp = lib + ".tmp"
+    cmd = ["gcc", *CFLAGS, *(SANITIZE if sanitize else []), SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv)
     sys.exit(0)
