@@ -12,7 +12,9 @@
 //
 // Work split.  A workgroup of four wavefronts owns 8 consecutive 16-row
 // panels (128 output channels) and all BM = 32 MT activation rows, over one
-// K range ("split").  Wavefront (wn, wm) decodes panels 4 wn .. 4 wn + 3 and
+// K range ("split").  The activation slice of a k-step reaches LDS through
+// loads of whole 128-byte lines, swizzled so that the MFMA operand reads are
+// free of bank conflicts (see issue_x).  Wavefront (wn, wm) decodes panels 4 wn .. 4 wn + 3 and
 // multiplies them against activation tiles MT wm .. MT wm + MT - 1, so each
 // decoded weight fragment feeds MT MFMAs and each activation fragment read
 // from LDS feeds 4.
@@ -184,25 +186,49 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     }
   };
 
-  // ---- activation slice of step c -> LDS: load q = t * MTW + tile fills
-  // 1 KiB; lane (kg, col) takes X[16 tile + col][K .. K + 8), K = (j0 + c) KS
-  // + kg KS / 4 + 8 t.  Rows >= m and K >= k read zeros. ----
+  // ---- activation slice of step c -> LDS.  Each direct-to-LDS load reads
+  // eight whole 128-byte lines: 8 rows x 128 bytes of the step's K.  Load q
+  // (1 KiB of LDS) covers rows 8 g .. 8 g + 7 and the h-th 128-byte part of
+  // their k-step (g = q / H, h = q % H).  A lane lands at 16 lane bytes of its
+  // load; lane 16 qq + slot holds piece e = 2 qq + ((slot - g) & 1) (16 bytes
+  // of K) of row 8 g + r, where slot = (2 r + (g & 1) + e) mod 16.  The MFMA
+  // operand of lane (col, kg) then sits at a slot that differs for the 16
+  // lanes of every read group, so the fragment reads are free of bank
+  // conflicts, and each load touches 8 lines instead of 32 (an MFMA fragment
+  // itself spans 16 rows and four 16-byte pieces 64 bytes apart).  Rows >= m
+  // and K >= k read zeros. ----
+  constexpr int H = KS / 64;  // 128-byte parts of a row's k-step
+  static_assert(XQ * kWaves == 4 * MT * H, "one load per 8 rows and 128 bytes");
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrc);
   const int col = lane & 15, kg = lane >> 4;
+  const int lq = lane >> 4, lslot = lane & 15;
   auto issue_x = [&](int c, uint8_t* buf) {
 #pragma unroll
     for (int i = 0; i < XQ; ++i) {
       const int q = wv + kWaves * i;
-      const int t = q / MTW, tile = q % MTW;
-      const int row = tile * 16 + col;
-      const int64_t kpos = (int64_t)(j0 + c) * KS + kg * (KS / 4) + 8 * t;
+      const int g = q / H, h = q % H;
+      const int e = 2 * lq + ((lslot - g) & 1);
+      const int row = 8 * g + (((lslot - (g & 1) - e) & 15) >> 1);
+      const int64_t kpos = (int64_t)(j0 + c) * KS + (h * 8 + e) * 8;
       const bool ok = c < nj && row < m && kpos < k;
       const int off = ok ? (int)(((int64_t)row * k + kpos) * 2) : 0x7FFFFFF0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16, off, 0, 0, 0);
     }
   };
+  // This lane's B operand of MFMA group t in the wave's first activation
+  // tile: row 16 (MT wm) + col, piece kg KS / 32 + t of the k-step; the
+  // next tile is 2 H loads further (two more row groups, same parity).
+  int xoff[GR];
+#pragma unroll
+  for (int t = 0; t < GR; ++t) {
+    const int eg = kg * (KS / 32) + t;
+    const int h = eg >> 3, e = eg & 7;
+    const int g = 2 * (wm * MT) + (col >> 3);
+    const int slot = (2 * (col & 7) + (g & 1) + e) & 15;
+    xoff[t] = (g * H + h) * 1024 + (16 * (e >> 1) + slot) * 16;
+  }
 
   float4v acc[4][MT];
 #pragma unroll
@@ -242,18 +268,18 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       else
         decode_fp8_fragment(cur[i].codes, a[i]);
     }
-    const uint8_t* xs = xread + (wm * MT) * 1024 + lane * 16;
     // the activation fragments of group t + 1 are read while group t's
     // MFMAs run
     half8 b[2][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) b[0][mt] = *reinterpret_cast<const half8*>(xs + mt * 1024);
+    for (int mt = 0; mt < MT; ++mt)
+      b[0][mt] = *reinterpret_cast<const half8*>(xread + xoff[0] + mt * 2048 * H);
 #pragma unroll
     for (int t = 0; t < GR; ++t) {
       if (t + 1 < GR) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          b[(t + 1) & 1][mt] = *reinterpret_cast<const half8*>(xs + ((t + 1) * MTW + mt) * 1024);
+          b[(t + 1) & 1][mt] = *reinterpret_cast<const half8*>(xread + xoff[t + 1] + mt * 2048 * H);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
