@@ -40,6 +40,7 @@ model.
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV   (profiles/traffic.json from the PMC passes)
     python bench.py --summarize-sq AB_CSV AB_JSON HEAD_CSV BENCH_JSON   (SQ counter tables)
     python bench.py --summarize-trace KERNEL_TRACE_CSV   (per-kernel median / p10 / p90 durations)
+    python bench.py --summarize-pmc COUNTER_CSV [MATCH]   (per-kernel counter averages)
 """
 import argparse
 import hashlib
@@ -426,6 +427,33 @@ def summarize_trace(trace_csv):
     return out
 
 
+def summarize_pmc(counter_csv, match=""):
+    """Per-kernel averages of every counter in a rocprofv3 PMC pass (one
+    row per kernel name and grid size whose name contains `match`), as
+    markdown lines."""
+    import csv
+    per, order = {}, []
+    with open(counter_csv) as fh:
+        for r in csv.DictReader(fh):
+            name = (r["Kernel_Name"].replace("(anonymous namespace)", "{anon}")
+                    .split("(")[0].replace("void ", ""))
+            if match not in name:
+                continue
+            key = (name, int(r["Grid_Size"]))
+            if key not in per:
+                per[key] = {}
+                order.append(key)
+            per[key].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    counters = sorted({c for d in per.values() for c in d})
+    out = ["| kernel | grid threads | " + " | ".join(counters) + " |",
+           "|---|---:|" + "---:|" * len(counters)]
+    for key in order:
+        d = per[key]
+        vals = [f"{np.mean(d[c]):,.0f}" if c in d else "" for c in counters]
+        out.append(f"| `{key[0]}` | {key[1]} | " + " | ".join(vals) + " |")
+    return out
+
+
 SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES")
 
 
@@ -532,6 +560,9 @@ def main():
                          "--traffic-workload and the JSON lines of --contraction-ab and bench.py")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel duration statistics from a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar=("COUNTER_CSV", "MATCH"),
+                    help="per-kernel counter averages from a rocprofv3 PMC pass (optionally only "
+                         "kernels whose name contains MATCH)")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
     ap.add_argument("--prefill-workload", action="store_true",
@@ -542,6 +573,9 @@ def main():
 
     if args.summarize_traffic:  # host only: post-processes rocprofv3 output
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_pmc:  # host only: post-processes rocprofv3 output
+        print("\n".join(summarize_pmc(*args.summarize_pmc[:2])))
         return
     if args.summarize_trace:  # host only: post-processes rocprofv3 output
         print("\n".join(summarize_trace(args.summarize_trace)))
