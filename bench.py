@@ -406,9 +406,9 @@ def summarize_traffic(fetch_csv, write_csv):
 
 
 def summarize_trace(trace_csv):
-    """Per-kernel launch durations from a rocprofv3 kernel-trace CSV: count,
-    mean, median, p10, p90, min and max in microseconds, as markdown lines,
-    longest total time first."""
+    """Launch durations from a rocprofv3 kernel-trace CSV per kernel and grid
+    size (one call shape): count, mean, median, p10, p90, min and max in
+    microseconds, as markdown lines, longest total time first."""
     import csv
     per = {}
     with open(trace_csv) as fh:
@@ -416,12 +416,12 @@ def summarize_trace(trace_csv):
             name = (r["Kernel_Name"].replace("(anonymous namespace)", "{anon}")
                     .split("(")[0].replace("void ", ""))
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
-            per.setdefault(name, []).append(dur)
-    out = ["| kernel | launches | mean us | median us | p10 us | p90 us | min us | max us |",
-           "|---|---:|---:|---:|---:|---:|---:|---:|"]
-    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            per.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
+    out = ["| kernel | grid threads | launches | mean us | median us | p10 us | p90 us | min us | max us |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (name, grid), d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         a = np.array(d)
-        out.append(f"| `{name}` | {a.size} | {a.mean():.3f} | {np.median(a):.3f} | "
+        out.append(f"| `{name}` | {grid} | {a.size} | {a.mean():.3f} | {np.median(a):.3f} | "
                    f"{np.percentile(a, 10):.3f} | {np.percentile(a, 90):.3f} | {a.min():.3f} | "
                    f"{a.max():.3f} |")
     return out
