@@ -180,11 +180,12 @@ int plan_query(int op, int plan, int m, int64_t n, int64_t k, PlanInfo* o) {
     PrefillLaunch l;
     if (prefill_launch_for(fmt, m, n, k, (size_t)-1, &l) != kGemmLaunchOk) return QPN_ERR_SHAPE;
     o->workgroups = l.workgroups;
-    o->waves_per_panel = 2;  // two wavefronts, one per half of the rows
-    o->panels_per_workgroup = 8;
+    // narrow: two wavefronts per panel (one per half of the rows); wide: one
+    o->waves_per_panel = l.wide ? 1 : 2;
+    o->panels_per_workgroup = l.wide ? 16 : 8;
     o->depth = l.depth;
     o->splits = l.splits;
-    o->activation_rows = 32 * l.mt;
+    o->activation_rows = l.wide ? 128 : 32 * l.mt;  // rows per workgroup
     o->split_wgs = l.workgroups;
     o->valu_dot = 0;
     o->ws_bytes = n == 0 ? 0 : l.ws_needed;

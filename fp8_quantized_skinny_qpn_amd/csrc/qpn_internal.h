@@ -94,7 +94,8 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
                                   int32_t* result, void* stream);
 
 // Prefill-sized activation blocks (9 <= m <= 256): one launch of the tiled
-// MFMA kernel, 128 output channels by 32 mt activation rows per workgroup.
+// MFMA kernel, 128 output channels by 32 mt activation rows per workgroup up
+// to 128 rows, 256 channels by 128 rows above.
 // Calls of up to kPrefillSkinnyRows rows run the skinny kernel instead, with
 // a 16-row activation tile that fills the MFMA's B operand exactly (the
 // weights stream once, as at m <= 8), unless the workspace given is too
@@ -102,7 +103,9 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 constexpr int kMaxPrefillM = 256;
 constexpr int kPrefillSkinnyRows = 16;
 struct PrefillLaunch {
-  int mt;               // 16-row activation tiles per wavefront (workgroup rows = 32 mt)
+  int mt;               // 16-row activation tiles per wavefront (workgroup rows: 32 mt, wide 16 mt)
+  bool wide;            // above 128 rows: 256 channels x 128 rows per workgroup
+  int row_blocks;       // blocks of 128 rows (wide), else 1
   int depth;            // k-steps of weight loads in flight per wavefront
   int64_t blocks;       // 128-channel blocks
   int splits;           // K ranges per block

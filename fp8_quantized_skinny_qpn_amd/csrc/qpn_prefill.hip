@@ -10,14 +10,24 @@
 // At 2M flops per weight the work turns from HBM-bound (M below ~90 on
 // MI355X) to matrix-unit-bound.
 //
-// Work split.  A workgroup of four wavefronts owns 8 consecutive 16-row
-// panels (128 output channels) and all BM = 32 MT activation rows, over one
-// K range ("split").  The activation slice of a k-step reaches LDS through
-// loads of whole 128-byte lines, swizzled so that the MFMA operand reads are
-// free of bank conflicts (see issue_x).  Wavefront (wn, wm) decodes panels 4 wn .. 4 wn + 3 and
-// multiplies them against activation tiles MT wm .. MT wm + MT - 1, so each
-// decoded weight fragment feeds MT MFMAs and each activation fragment read
-// from LDS feeds 4.
+// Work split.  Up to 128 rows, a workgroup of four wavefronts owns 8
+// consecutive 16-row panels (128 output channels) and all BM = 32 MT
+// activation rows, over one K range ("split"); wavefront (wn, wm) decodes
+// panels 4 wn .. 4 wn + 3 and multiplies them against activation tiles MT wm
+// .. MT wm + MT - 1, so each decoded weight fragment feeds MT MFMAs and each
+// activation fragment read from LDS feeds 4.  Above 128 rows (WIDE) a
+// workgroup owns 16 panels (256 channels) and one block of 128 rows, the
+// four wavefronts side by side (wavefront w: panels 4 w .. 4 w + 3, all 8
+// tiles of the block), so that every wavefront loads only its own weights
+// and the 32 KiB activation slice of a k-step serves twice the channels.  A
+// CU pulls only ~25-30 GB/s from L2 and beyond on MI355X, so the bytes a
+// workgroup fetches per k-step set the pace: 32 KiB of activations and 18
+// KiB of weights per 256 x 128 x 128 x 2 flops here, against 64 KiB and 18
+// KiB (every panel loaded by two wavefronts) per 128 x 256 x 128 x 2 for the
+// narrow tile at 256 rows: 17408x5120 at 256 rows went from 108.5 to 87 us.
+// The activation slice of a k-step reaches LDS through loads of whole
+// 128-byte lines, swizzled so that the MFMA operand reads are free of bank
+// conflicts (see issue_x).
 //
 // Pipeline per k-step c (static wait counts; loads of a wavefront complete
 // in order):
@@ -61,7 +71,8 @@ struct PFmt<kFmtFp8> {
 };
 
 constexpr int kRsrc = 0x00020000;  // raw dword access
-constexpr int kPanelsPerBlock = 8;  // 128 output channels per workgroup
+constexpr int kPanelsPerBlock = 8;       // narrow tile: 128 output channels per workgroup
+constexpr int kWidePanelsPerBlock = 16;  // wide tile: 256 output channels per workgroup
 constexpr int kWaves = 4;
 
 template <int N>
@@ -95,20 +106,24 @@ __device__ __forceinline__ uint8_t* slice_stage() {
 struct PrefillSplit {
   int splits;
   int split_steps;
-  float* partial;      // [S][blocks][4 MT tiles][256 threads] float4 partials
-  uint32_t* counters;  // [blocks] arrivals; zero between calls
+  int row_blocks;      // blocks of activation rows (WIDE only; 1 otherwise)
+  float* partial;      // [S][tiles][4 MT fragments][256 threads] float4 partials
+  uint32_t* counters;  // [tiles] arrivals; zero between calls
 };
 
 // D: k-steps of weights in flight (ring R = D + 1); NS: activation slice
-// stages in LDS (2, or R when they fit), the slice being sent NS - 1 steps ahead.
-template <uint32_t FMT, int MT, int D, int NS>
+// stages in LDS (2, or R when they fit), the slice being sent NS - 1 steps
+// ahead; WIDE: 16 panels x 16 MT rows per workgroup instead of 8 x 32 MT.
+template <uint32_t FMT, int MT, int D, int NS, bool WIDE>
 __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     int m, int64_t n, int64_t k, PrefillSplit sp) {
   using F = PFmt<FMT>;
   constexpr int KS = F::kKStep;
   constexpr int GR = F::kGroups;
-  constexpr int MTW = 2 * MT;                        // 16-row activation tiles per workgroup
+  constexpr int WNN = WIDE ? 4 : 2;                  // wavefronts across panels
+  constexpr int PPB = 4 * WNN;                       // panels per workgroup
+  constexpr int MTW = (kWaves / WNN) * MT;           // 16-row activation tiles per workgroup
   constexpr int STAGE = GR * MTW * 1024;             // LDS bytes of one step's slice
   constexpr int XQ = GR * MTW / kWaves;              // slice loads per wavefront per step
   constexpr int LPS = FMT == kFmtNvfp4 ? 2 : 1;      // weight loads per chunk
@@ -138,15 +153,17 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-  const int wn = wv & 1, wm = wv >> 1;
+  const int wn = wv % WNN, wm = wv / WNN;
   const int S = sp.splits;
-  const int64_t blk = blockIdx.x / S;
+  const int64_t blk = blockIdx.x / S;  // output tile: (channel block, row block)
   const int split = blockIdx.x % S;
+  const int64_t cblk = blk / sp.row_blocks;
+  const int row0 = (int)(blk % sp.row_blocks) * 16 * MTW;
   const int64_t P = panels_of(n);
   const int J = (int)((k + KS - 1) / KS);
   const int j0 = split * sp.split_steps;
   const int nj = max(0, min(J - j0, sp.split_steps));
-  const int64_t pbase = blk * kPanelsPerBlock + 4 * wn;  // first of this wavefront's 4 panels
+  const int64_t pbase = cblk * PPB + 4 * wn;  // first of this wavefront's 4 panels
 
   // ---- header (and FP8 row scales): used in the epilogue ----
   const __amdgpu_buffer_rsrc_t hres =
@@ -198,7 +215,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
   // itself spans 16 rows and four 16-byte pieces 64 bytes apart).  Rows >= m
   // and K >= k read zeros. ----
   constexpr int H = KS / 64;  // 128-byte parts of a row's k-step
-  static_assert(XQ * kWaves == 4 * MT * H, "one load per 8 rows and 128 bytes");
+  static_assert(XQ * kWaves == 2 * MTW * H, "one load per 8 rows and 128 bytes");
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrc);
   const int col = lane & 15, kg = lane >> 4;
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       const int q = wv + kWaves * i;
       const int g = q / H, h = q % H;
       const int e = 2 * lq + ((lslot - g) & 1);
-      const int row = 8 * g + (((lslot - (g & 1) - e) & 15) >> 1);
+      const int row = row0 + 8 * g + (((lslot - (g & 1) - e) & 15) >> 1);
       const int64_t kpos = (int64_t)(j0 + c) * KS + (h * 8 + e) * 8;
       const bool ok = c < nj && row < m && kpos < k;
       const int off = ok ? (int)(((int64_t)row * k + kpos) * 2) : 0x7FFFFFF0;
@@ -362,7 +379,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
   }
 
   // ---- epilogue: lane holds, for panel i and tile t, output channels
-  // 16 p + 4 (lane >> 4) + v (v < 4) of activation row 16 (MT wm + t) + (lane & 15) ----
+  // 16 p + 4 (lane >> 4) + v (v < 4) of activation row row0 + 16 (MT wm + t) + (lane & 15) ----
   const bool vec = (n & 3) == 0 && (((uintptr_t)y) & 7) == 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -370,7 +387,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     if (n0 >= n) continue;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const int row = (wm * MT + t) * 16 + col;
+      const int row = row0 + (wm * MT + t) * 16 + col;
       if (row >= m) continue;
       uint16_t h[4];
 #pragma unroll
@@ -400,16 +417,24 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 
 // K splits.  With 32 or 64 rows the call is HBM-bound: up to 200 workgroups
 // (not one per CU: each split adds a fix-up and partial-tile traffic).  With
-// 128 or 256 rows the matrix unit bounds it and one workgroup fills a CU
-// (its slice stages take 128 KiB of LDS): the split count minimises whole
-// waves of 256 workgroups times k-steps per workgroup (about 0.107 us of
-// MFMA work per activation tile and NVFP4 k-step, half that per FP8 k-step)
-// plus the partial tiles' write-and-read traffic at ~5 TB/s.
+// 128 rows the matrix unit and the activation slice bound it: the split
+// count minimises whole waves of 256 workgroups times k-steps per workgroup
+// (about 0.107 us of MFMA work per activation tile and NVFP4 k-step, half
+// that per FP8 k-step) plus the partial tiles' write-and-read traffic at
+// ~5 TB/s.  Above 128 rows the wide tile (256 channels x 128 rows) takes the
+// most splits, up to 4, that keep one wave of at most 256 workgroups: the
+// last arriving workgroup of a tile reads all its partial tiles (128 KiB
+// each) alone, so more splits cost more than they bring (5120x17408 at 256
+// rows: 126.0 / 117.5 / 123.9 us with 3 / 4 / 6 splits; 17408x5120: 87.4 us
+// unsplit on 136 workgroups, 137.9 us with 2 splits on 272).
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out) {
+  const bool wide = m > 128;
   const int mt = prefill_tiles(m);
+  const int64_t rb = wide ? (m + 127) / 128 : 1;
   const int64_t P = panels_of(n);
-  const int64_t blocks = (P + kPanelsPerBlock - 1) / kPanelsPerBlock;
+  const int64_t ppb = wide ? kWidePanelsPerBlock : kPanelsPerBlock;
+  const int64_t blocks = (P + ppb - 1) / ppb * rb;  // output tiles
   const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
   const int64_t smax = std::max<int64_t>(1, J / 4);
   auto need = [&](int64_t s) -> size_t {
@@ -418,7 +443,9 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
     return counters + (size_t)s * blocks * (kLanes * kWaves) * (4 * mt) * 16;
   };
   int64_t S = 1;
-  if (blocks > 0 && mt <= 2) {
+  if (blocks > 0 && wide) {
+    S = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, 256 / blocks), smax));
+  } else if (blocks > 0 && mt <= 2) {
     // HBM-bound: the most K splits that keep at most 200 workgroups.  Filling
     // every CU with more splits cost more in split-K fix-ups than the CUs
     // brought: at m = 64, 17408x5120 went from 62 to 43.6 us (one split, 136
@@ -427,9 +454,7 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
     S = std::min<int64_t>(std::max<int64_t>(1, 200 / blocks), smax);
   } else if (blocks > 0) {
     // MFMA time of one activation tile and k-step: an FP8 k-step is 64 K,
-    // half the work of an NVFP4 one (charging it the NVFP4 time chose five
-    // splits where four measured 83.6 against 90.3-91.1 us at FP8 6144x5120
-    // m = 256)
+    // half the work of an NVFP4 one
     const double step_us = fmt == kFmtNvfp4 ? 0.107 : 0.0535;
     double best = 0.0;
     for (int64_t s = 1; s <= std::min<int64_t>(smax, 16); ++s) {
@@ -452,6 +477,8 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   // the partial area is addressed with 32-bit offsets
   if (need(S) >= ((size_t)1 << 31)) return kGemmNoWorkspace;
   out->mt = mt;
+  out->wide = wide;
+  out->row_blocks = (int)rb;
   out->depth = 3;  // as compiled below
   out->blocks = blocks;
   out->splits = (int)S;
@@ -465,14 +492,14 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
 
 namespace {
 
-template <uint32_t FMT, int MT, int D, int NS>
+template <uint32_t FMT, int MT, int D, int NS, bool WIDE>
 hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
-  PrefillSplit sp{l.splits, l.split_steps, nullptr, nullptr};
+  PrefillSplit sp{l.splits, l.split_steps, l.row_blocks, nullptr, nullptr};
   if (l.splits > 1) {
     sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
     sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
   }
-  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS>), dim3((unsigned)l.workgroups),
+  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS, WIDE>), dim3((unsigned)l.workgroups),
                      dim3(kLanes * kWaves), 0, (hipStream_t)a.stream, (const uint8_t*)a.packed,
                      a.x, a.y, a.m, a.n, a.k, sp);
   return hipGetLastError();
@@ -480,13 +507,14 @@ hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
 
 template <uint32_t FMT>
 hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
+  // 3 k-steps of weights ahead; up to 64 rows 4 slice stages measured 3-6%
+  // faster than 5 ahead in 6 stages.  The wide tile's 32 KiB slices also fit
+  // 4 stages.
+  if (l.wide) return launch_pf<FMT, 8, 3, 4, true>(a, l);
   switch (l.mt) {
-    // up to 64 rows: 3 k-steps ahead in 4 slice stages measured 3-6% faster
-    // than 5 ahead in 6 stages at every 17-64-row decoder shape
-    case 1: return launch_pf<FMT, 1, 3, 4>(a, l);
-    case 2: return launch_pf<FMT, 2, 3, 4>(a, l);
-    case 4: return launch_pf<FMT, 4, 3, 4>(a, l);
-    default: return launch_pf<FMT, 8, 3, 2>(a, l);
+    case 1: return launch_pf<FMT, 1, 3, 4, false>(a, l);
+    case 2: return launch_pf<FMT, 2, 3, 4, false>(a, l);
+    default: return launch_pf<FMT, 4, 3, 4, false>(a, l);
   }
 }
 

@@ -127,10 +127,12 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * split_workgroups, the workgroups that work on K ranges (split_workgroups
  * / splits panel groups of the last panels, dispatched first).  The other
  * workgroups - 0 unless the plan balances whole panels per CU - each take
- * panels_per_workgroup whole panels.  For the prefill ops: every workgroup
- * covers 8 panels (two wavefronts per panel, one per half of the activation
- * rows), activation_rows is the 32, 64, 128 or 256 rows a workgroup takes,
- * and split_workgroups equals workgroups.  A pure function of its
+ * panels_per_workgroup whole panels.  For the prefill ops above 16 rows:
+ * up to 128 rows every workgroup covers 8 panels (two wavefronts per panel,
+ * one per half of the activation rows) and activation_rows is the 32, 64 or
+ * 128 rows it takes; above 128 rows it covers 16 panels (one wavefront per
+ * 4 panels) and one block of 128 rows (activation_rows 128; the row blocks
+ * are separate workgroups); split_workgroups equals workgroups.  A pure function of its
  * arguments, independent of any declared maximum.  Any output pointer may
  * be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,

@@ -6,9 +6,10 @@ rows the tiled MFMA kernel.  Both paths are covered below.
 
 The same parity bar as the skinny GEMM: per element |err| <= 1e-2 rms(ref)
 + 1e-3 and relative Frobenius error <= 2e-3 against the FP64 oracle product
-of the canonical codes.  Shapes span several 128-channel blocks, ragged N
-and M tails, K splits, every activation-tile count (32, 64, 128, 256 rows)
-and the full decoder shapes (sampled output channels).
+of the canonical codes.  Shapes span several 128- and 256-channel blocks,
+ragged N and M tails, K splits, every activation-tile count (32, 64, 128
+rows), the wide tile's two 128-row blocks (129 to 256 rows) and the full
+decoder shapes (sampled output channels).
 """
 import numpy as np
 import pytest
