@@ -184,8 +184,8 @@ int plan_query(int op, int plan, int m, int64_t n, int64_t k, PlanInfo* o) {
     o->waves_per_panel = l.wide ? 1 : 2;
     o->panels_per_workgroup = l.wide ? 16 : 8;
     o->depth = l.depth;
-    o->splits = l.splits;
-    o->activation_rows = l.wide ? 128 : 32 * l.mt;  // rows per workgroup
+    o->splits = l.max_pieces;  // the most workgroups one output tile is cut between
+    o->activation_rows = (l.wide ? 16 : 32) * l.mt;  // rows per workgroup
     o->split_wgs = l.workgroups;
     o->valu_dot = 0;
     o->ws_bytes = n == 0 ? 0 : l.ws_needed;

@@ -102,15 +102,18 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 // small for the K splits its LDS budget needs.
 constexpr int kMaxPrefillM = 256;
 constexpr int kPrefillSkinnyRows = 16;
+constexpr int64_t kPrefillWorkgroups = 256;  // one per CU of an MI355X
+constexpr int64_t kPrefillMinK = 512;        // shortest K range of a workgroup
 struct PrefillLaunch {
-  int mt;               // 16-row activation tiles per wavefront (workgroup rows: 32 mt, wide 16 mt)
+  int mt;               // 16-row activation tiles per wavefront (workgroup rows: narrow 32 mt, wide 16 mt)
   bool wide;            // above 128 rows: 256 channels x 128 rows per workgroup
   int row_blocks;       // blocks of 128 rows (wide), else 1
   int depth;            // k-steps of weight loads in flight per wavefront
-  int64_t blocks;       // 128-channel blocks
-  int splits;           // K ranges per block
-  int split_steps;      // k-steps per K range
-  int64_t workgroups;   // blocks * splits
+  int64_t tiles;        // output tiles: channel blocks x row blocks
+  int64_t ksteps;       // k-steps per tile
+  int64_t workgroups;   // equal ranges of the tiles x k-steps units (tiles: whole tiles)
+  int max_pieces;       // the most workgroups one tile is cut between
+  int nodes_per_tile;   // pairwise-tree nodes per tile (max_pieces - 1, at least 1)
   size_t ws_counters_offset;
   size_t ws_partial_offset;
   size_t ws_needed;

@@ -103,12 +103,13 @@ __device__ __forceinline__ uint8_t* slice_stage() {
 
 }  // namespace
 
-struct PrefillSplit {
-  int splits;
-  int split_steps;
+struct PrefillWork {
+  int64_t tiles;       // output tiles: channel blocks x row blocks
   int row_blocks;      // blocks of activation rows (WIDE only; 1 otherwise)
-  float* partial;      // [S][tiles][4 MT fragments][256 threads] float4 partials
-  uint32_t* counters;  // [tiles] arrivals; zero between calls
+  int64_t wgs;         // workgroups; the tiles x k-steps units are cut into wgs equal ranges
+  int nodes_per_tile;  // tree nodes per cut tile
+  float* partial;      // [2 wgs][4 MT fragments][256 threads] float4 partial tiles
+  uint32_t* counters;  // [tiles][nodes_per_tile] node states (slot + 1 of a waiting partial); zero between calls
 };
 
 // D: k-steps of weights in flight (ring R = D + 1); NS: activation slice
@@ -117,7 +118,7 @@ struct PrefillSplit {
 template <uint32_t FMT, int MT, int D, int NS, bool WIDE>
 __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-    int m, int64_t n, int64_t k, PrefillSplit sp) {
+    int m, int64_t n, int64_t k, PrefillWork pw) {
   using F = PFmt<FMT>;
   constexpr int KS = F::kKStep;
   constexpr int GR = F::kGroups;
@@ -154,86 +155,36 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
   const int lane = threadIdx.x & (kLanes - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int wn = wv % WNN, wm = wv / WNN;
-  const int S = sp.splits;
-  const int64_t blk = blockIdx.x / S;  // output tile: (channel block, row block)
-  const int split = blockIdx.x % S;
-  const int64_t cblk = blk / sp.row_blocks;
-  const int row0 = (int)(blk % sp.row_blocks) * 16 * MTW;
   const int64_t P = panels_of(n);
   const int J = (int)((k + KS - 1) / KS);
-  const int j0 = split * sp.split_steps;
-  const int nj = max(0, min(J - j0, sp.split_steps));
-  const int64_t pbase = cblk * PPB + 4 * wn;  // first of this wavefront's 4 panels
+  // Work units: (tile, k-step) pairs, tile-major; a tile with no k-step
+  // (k = 0) still counts one unit, so that its output gets written.
+  // Workgroup w owns units [w U / G, (w + 1) U / G); the owner of unit u is
+  // ceil((u + 1) G / U) - 1.  A tile whose units fall to several workgroups
+  // is summed by the last of them to finish (below).
+  const int64_t Jt = J > 0 ? J : 1;
+  const int64_t U = pw.tiles * Jt;
+  const int64_t G = pw.wgs;
+  auto first_unit = [&](int64_t w) -> int64_t { return w * U / G; };
+  auto owner = [&](int64_t u) -> int64_t { return ((u + 1) * G + U - 1) / U - 1; };
+  const int64_t wg = blockIdx.x;
+  const int64_t u_end = first_unit(wg + 1);
 
-  // ---- header (and FP8 row scales): used in the epilogue ----
+  // ---- header: checked in the epilogue ----
   const __amdgpu_buffer_rsrc_t hres =
       __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, kHeaderBytes, kRsrc);
   const u32x4 hd0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, 0, 0, 0));
   const u32x4 hd1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, 16, 0, 0));
   const uint32_t hd2 = __builtin_amdgcn_raw_buffer_load_b32(hres, 48, 0, 0);
-  float4v row_scale[4] = {};
-  if constexpr (FMT == kFmtFp8) {
-    // the padded scale area holds 16 P floats; panels past P read zeros
-    const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(blob + kHeaderBytes), (short)0, (int)(P * kPanelRows * 4), kRsrc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
-      const int off = pbase + i < P ? (int)(r0 * 4) : 0x7FFFFFF0;
-      row_scale[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0));
-    }
-  }
-  asm volatile("" ::: "memory");
 
-  // ---- weights: chunk (p, j) at codes + (j P + p) * chunk bytes ----
   const uint8_t* codes = blob + (FMT == kFmtNvfp4 ? (uint64_t)kHeaderBytes : f8_codes_offset(n));
   const uint64_t sstride = (uint64_t)P * F::kChunk;
-  auto issue_w = [&](int c, PFrag (&f)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // the address is formed unconditionally (no access happens through a
-      // descriptor of size zero), so the load itself never sits behind a branch
-      const bool ok = c < nj && pbase + i < P;
-      const uint8_t* ch = codes + (uint64_t)(j0 + c) * sstride + (uint64_t)(pbase + i) * F::kChunk;
-      const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc((void*)ch, (short)0, ok ? F::kChunk : 0, kRsrc);
-      f[i].codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 2));
-      if constexpr (FMT == kFmtNvfp4)
-        f[i].scales = __builtin_amdgcn_raw_buffer_load_b16(r, kNvCodeBytes + 2 * lane, 0, 0);
-    }
-  };
-
-  // ---- activation slice of step c -> LDS.  Each direct-to-LDS load reads
-  // eight whole 128-byte lines: 8 rows x 128 bytes of the step's K.  Load q
-  // (1 KiB of LDS) covers rows 8 g .. 8 g + 7 and the h-th 128-byte part of
-  // their k-step (g = q / H, h = q % H).  A lane lands at 16 lane bytes of its
-  // load; lane 16 qq + slot holds piece e = 2 qq + ((slot - g) & 1) (16 bytes
-  // of K) of row 8 g + r, where slot = (2 r + (g & 1) + e) mod 16.  The MFMA
-  // operand of lane (col, kg) then sits at a slot that differs for the 16
-  // lanes of every read group, so the fragment reads are free of bank
-  // conflicts, and each load touches 8 lines instead of 32 (an MFMA fragment
-  // itself spans 16 rows and four 16-byte pieces 64 bytes apart).  Rows >= m
-  // and K >= k read zeros. ----
-  constexpr int H = KS / 64;  // 128-byte parts of a row's k-step
-  static_assert(XQ * kWaves == 2 * MTW * H, "one load per 8 rows and 128 bytes");
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)m * k * 2), kRsrc);
   const int col = lane & 15, kg = lane >> 4;
   const int lq = lane >> 4, lslot = lane & 15;
-  auto issue_x = [&](int c, uint8_t* buf) {
-#pragma unroll
-    for (int i = 0; i < XQ; ++i) {
-      const int q = wv + kWaves * i;
-      const int g = q / H, h = q % H;
-      const int e = 2 * lq + ((lslot - g) & 1);
-      const int row = row0 + 8 * g + (((lslot - (g & 1) - e) & 15) >> 1);
-      const int64_t kpos = (int64_t)(j0 + c) * KS + (h * 8 + e) * 8;
-      const bool ok = c < nj && row < m && kpos < k;
-      const int off = ok ? (int)(((int64_t)row * k + kpos) * 2) : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xres, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16, off, 0, 0, 0);
-    }
-  };
+  constexpr int H = KS / 64;  // 128-byte parts of a row's k-step
+  static_assert(XQ * kWaves == 2 * MTW * H, "one load per 8 rows and 128 bytes");
   // This lane's B operand of MFMA group t in the wave's first activation
   // tile: row 16 (MT wm) + col, piece kg KS / 32 + t of the k-step; the
   // next tile is 2 H loads further (two more row groups, same parity).
@@ -247,163 +198,285 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     xoff[t] = (g * H + h) * 1024 + (16 * (e >> 1) + slot) * 16;
   }
 
-  float4v acc[4][MT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  PFrag ring[R][4];
-  // prologue: what steps -D .. -1 would have sent (slice s + AX when it is
-  // >= 0, weights s + D), in the same order, so that the wait count at the
-  // top of every step is the same.  The scheduler may not move loads across
-  // these points.
-#pragma unroll
-  for (int sidx = -D; sidx < 0; ++sidx) {
-    if (sidx + AX >= 0) issue_x(sidx + AX, stage(sidx + AX));
-    __builtin_amdgcn_sched_barrier(0);
-    issue_w(sidx + D, ring[sidx + D]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  auto step = [&](int c, const uint8_t* xread, uint8_t* xnext, PFrag (&cur)[4], PFrag (&ahead)[4]) {
-    // everything up to this step's slice is in, then everyone's slice is
-    // (and everyone is done reading the stage the next slice goes to)
-    pf_wait_vmcnt<WAITN>();
-    pf_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_x(c + AX, xnext);
-    __builtin_amdgcn_sched_barrier(0);  // all of the slice before any of the weights
-    issue_w(c + D, ahead);
-    __builtin_amdgcn_sched_barrier(0);
-    if (c >= nj) return;  // padding step: loads only (no memory access)
-    half8 a[4][GR];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (FMT == kFmtNvfp4)
-        decode_nvfp4_fragment(cur[i].codes, (uint32_t)cur[i].scales, a[i]);
-      else
-        decode_fp8_fragment(cur[i].codes, a[i]);
+  for (int64_t u = first_unit(wg); u < u_end;) {
+    // ---- this piece: k-steps j0 .. j0 + nj - 1 of one tile ----
+    const int64_t tile = u / Jt;
+    const int64_t piece_end = min((tile + 1) * Jt, u_end);
+    const int j0 = (int)(u - tile * Jt);
+    const int nj = J > 0 ? (int)(piece_end - u) : 0;
+    const bool later_piece = u != first_unit(wg);
+    u = piece_end;
+    const int64_t cblk = tile / pw.row_blocks;
+    const int row0 = (int)(tile % pw.row_blocks) * 16 * MTW;
+    const int64_t pbase = cblk * PPB + 4 * wn;  // first of this wavefront's 4 panels
+    if (later_piece) {
+      // the previous piece's stores are done and every wavefront has
+      // finished reading its LDS stages
+      pf_wait_vmcnt<0>();
+      pf_barrier();
     }
-    // the activation fragments of group t + 1 are read while group t's
-    // MFMAs run
-    half8 b[2][MT];
+
+    float4v row_scale[4] = {};
+    if constexpr (FMT == kFmtFp8) {
+      // the padded scale area holds 16 P floats; panels past P read zeros
+      const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(blob + kHeaderBytes), (short)0, (int)(P * kPanelRows * 4), kRsrc);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      b[0][mt] = *reinterpret_cast<const half8*>(xread + xoff[0] + mt * 2048 * H);
-#pragma unroll
-    for (int t = 0; t < GR; ++t) {
-      if (t + 1 < GR) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          b[(t + 1) & 1][mt] = *reinterpret_cast<const half8*>(xread + xoff[t + 1] + mt * 2048 * H);
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
+        const int off = pbase + i < P ? (int)(r0 * 4) : 0x7FFFFFF0;
+        row_scale[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0));
       }
+    }
+    asm volatile("" ::: "memory");
+
+    // ---- weights: chunk (p, j) at codes + (j P + p) * chunk bytes ----
+    auto issue_w = [&](int c, PFrag (&f)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // the address is formed unconditionally (no access happens through a
+        // descriptor of size zero), so the load itself never sits behind a branch
+        const bool ok = c < nj && pbase + i < P;
+        const uint8_t* ch = codes + (uint64_t)(j0 + c) * sstride + (uint64_t)(pbase + i) * F::kChunk;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)ch, (short)0, ok ? F::kChunk : 0, kRsrc);
+        f[i].codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 2));
+        if constexpr (FMT == kFmtNvfp4)
+          f[i].scales = __builtin_amdgcn_raw_buffer_load_b16(r, kNvCodeBytes + 2 * lane, 0, 0);
+      }
+    };
+
+    // ---- activation slice of step c -> LDS.  Each direct-to-LDS load reads
+    // eight whole 128-byte lines: 8 rows x 128 bytes of the step's K.  Load q
+    // (1 KiB of LDS) covers rows 8 g .. 8 g + 7 and the h-th 128-byte part of
+    // their k-step (g = q / H, h = q % H).  A lane lands at 16 lane bytes of its
+    // load; lane 16 qq + slot holds piece e = 2 qq + ((slot - g) & 1) (16 bytes
+    // of K) of row 8 g + r, where slot = (2 r + (g & 1) + e) mod 16.  The MFMA
+    // operand of lane (col, kg) then sits at a slot that differs for the 16
+    // lanes of every read group, so the fragment reads are free of bank
+    // conflicts, and each load touches 8 lines instead of 32 (an MFMA fragment
+    // itself spans 16 rows and four 16-byte pieces 64 bytes apart).  Rows >= m
+    // and K >= k read zeros. ----
+    auto issue_x = [&](int c, uint8_t* buf) {
+#pragma unroll
+      for (int i = 0; i < XQ; ++i) {
+        const int q = wv + kWaves * i;
+        const int g = q / H, h = q % H;
+        const int e = 2 * lq + ((lslot - g) & 1);
+        const int row = row0 + 8 * g + (((lslot - (g & 1) - e) & 15) >> 1);
+        const int64_t kpos = (int64_t)(j0 + c) * KS + (h * 8 + e) * 8;
+        const bool ok = c < nj && row < m && kpos < k;
+        const int off = ok ? (int)(((int64_t)row * k + kpos) * 2) : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16, off, 0, 0, 0);
+      }
+    };
+
+    float4v acc[4][MT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    PFrag ring[R][4];
+    // prologue: what steps -D .. -1 would have sent (slice s + AX when it is
+    // >= 0, weights s + D), in the same order, so that the wait count at the
+    // top of every step is the same.  The scheduler may not move loads across
+    // these points.
+#pragma unroll
+    for (int sidx = -D; sidx < 0; ++sidx) {
+      if (sidx + AX >= 0) issue_x(sidx + AX, stage(sidx + AX));
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(sidx + D, ring[sidx + D]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    auto step = [&](int c, const uint8_t* xread, uint8_t* xnext, PFrag (&cur)[4], PFrag (&ahead)[4]) {
+      // everything up to this step's slice is in, then everyone's slice is
+      // (and everyone is done reading the stage the next slice goes to)
+      pf_wait_vmcnt<WAITN>();
+      pf_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(c + AX, xnext);
+      __builtin_amdgcn_sched_barrier(0);  // all of the slice before any of the weights
+      issue_w(c + D, ahead);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c >= nj) return;  // padding step: loads only (no memory access)
+      half8 a[4][GR];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FMT == kFmtNvfp4)
+          decode_nvfp4_fragment(cur[i].codes, (uint32_t)cur[i].scales, a[i]);
+        else
+          decode_fp8_fragment(cur[i].codes, a[i]);
+      }
+      // the activation fragments of group t + 1 are read while group t's
+      // MFMAs run
+      half8 b[2][MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
+        b[0][mt] = *reinterpret_cast<const half8*>(xread + xoff[0] + mt * 2048 * H);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i][t], b[t & 1][mt], acc[i][mt], 0, 0, 0);
+      for (int t = 0; t < GR; ++t) {
+        if (t + 1 < GR) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            b[(t + 1) & 1][mt] = *reinterpret_cast<const half8*>(xread + xoff[t + 1] + mt * 2048 * H);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i][t], b[t & 1][mt], acc[i][mt], 0, 0, 0);
+      }
+    };
+
+    // unrolled by the ring length (a multiple of the stage count, so stages
+    // and ring slots are static) over a whole number of ring cycles; steps
+    // past nj only issue size-zero loads, so every wait count is static
+    const int nj_pad = ((nj + R - 1) / R) * R;
+    for (int c0 = 0; c0 < nj_pad; c0 += R) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        step(c0 + i, stage(i), stage(i + AX), ring[i], ring[(i + D) % R]);
     }
-  };
+    pf_wait_vmcnt<0>();  // size-zero surplus loads retired
 
-  // unrolled by the ring length (a multiple of the stage count, so stages
-  // and ring slots are static) over a whole number of ring cycles; steps
-  // past nj only issue size-zero loads, so every wait count is static
-  const int nj_pad = ((nj + R - 1) / R) * R;
-  for (int c0 = 0; c0 < nj_pad; c0 += R) {
+    // ---- a tile cut between workgroups: their partial tiles meet pairwise
+    // up a fixed binary tree over the workgroups in order (contributor c =
+    // w - w_first; at each level subtree pos pairs with pos ^ 1, an odd one
+    // out passes up).  At a node, the first to arrive leaves its partial
+    // tile in its own slot and names the slot in the node's state word; the
+    // second reads it, adds it (FP32 addition is commutative, so the sum
+    // does not depend on who came first) and climbs.  The workgroup that
+    // leaves the root writes the output.  The reader of a slot clears it and
+    // the node's state, so the workspace ends all zeros. ----
+    const int64_t w_first = owner(tile * Jt), w_last = owner(tile * Jt + Jt - 1);
+    if (w_first != w_last) {
+      constexpr int kDevScope = 16;  // sc1: write-through stores, coherent loads
+      constexpr int kTile = kLanes * kWaves * 16;  // bytes of one store instruction of the workgroup
+      constexpr int kSlot = 4 * MT * kTile;        // bytes of one partial tile
+      const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)pw.partial, (short)0, (int)(2 * G * kSlot), kRsrc);
+      const int mine = (int)threadIdx.x * 16;
+      // this workgroup's slot: 2 w for a piece of its first tile, 2 w + 1 for
+      // its last (only a workgroup's first and last piece can be cut)
+      const int my_slot = (int)(2 * wg + (first_unit(wg) / Jt == tile ? 0 : 1));
+      uint32_t* state = pw.counters + tile * pw.nodes_per_tile;
+      __shared__ int partner_slot;  // -1: this workgroup leaves the tree
+      int width = (int)(w_last - w_first + 1), pos = (int)(wg - w_first), node_base = 0;
+      bool leave = false;
+      while (width > 1) {
+        if ((pos ^ 1) < width) {
+          uint32_t* node = state + node_base + (pos >> 1);
+          pf_barrier();  // every wavefront has read the last partner_slot
+          if (threadIdx.x == 0) {
+            const uint32_t seen = __hip_atomic_load(node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            partner_slot = (int)seen - 1;
+          }
+          __syncthreads();
+          int ps = partner_slot;
+          bool wrote = false;
+          if (ps < 0) {
+            // first here as far as this workgroup saw: leave the partial
+            // tile, then name it (a partner that got in meanwhile is found
+            // by the failed exchange)
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-      step(c0 + i, stage(i), stage(i + AX), ring[i], ring[(i + D) % R]);
-  }
-  pf_wait_vmcnt<0>();  // size-zero surplus loads retired
-
-  // ---- header check ----
-  const uint32_t h_magic = __builtin_amdgcn_readfirstlane(hd0[0]);
-  const uint32_t h_format = __builtin_amdgcn_readfirstlane(hd0[1]);
-  const uint32_t h_version = __builtin_amdgcn_readfirstlane(hd0[2]);
-  const int64_t h_n = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
-                                __builtin_amdgcn_readfirstlane(hd1[0]));
-  const int64_t h_k = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[3]) << 32) |
-                                __builtin_amdgcn_readfirstlane(hd1[2]));
-  const float h_scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(hd2));
-  const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
-                     h_n == n && h_k == k;
-
-  // ---- split-K ----
-  if (S > 1) {
-    constexpr int kDevScope = 16;  // sc1: write-through stores, coherent loads
-    const int64_t blocks = gridDim.x / S;
-    const int64_t per_split = blocks * (kLanes * kWaves) * (4 * MT) * 16;
-    const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)sp.partial, (short)0, (int)(S * per_split), kRsrc);
-    // tile u of this thread at blk * 4 MT * 4 KiB + u * 4 KiB + 16 tid (each
-    // store instruction of the workgroup writes 4 KiB contiguously)
-    const int mine = (int)((blk * (4 * MT) * (kLanes * kWaves) + threadIdx.x) * 16);
-    constexpr int kTile = kLanes * kWaves * 16;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+              for (int t = 0; t < MT; ++t)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
+                                                       my_slot * kSlot + mine + (i * MT + t) * kTile, 0,
+                                                       kDevScope);
+            pf_wait_vmcnt<0>();
+            pf_barrier();
+            if (threadIdx.x == 0) {
+              uint32_t expected = 0u;
+              const bool named = __hip_atomic_compare_exchange_strong(
+                  node, &expected, (uint32_t)my_slot + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                  __HIP_MEMORY_SCOPE_AGENT);
+              partner_slot = named ? -1 : (int)expected - 1;
+            }
+            __syncthreads();
+            ps = partner_slot;
+            if (ps < 0) {
+              leave = true;
+              break;
+            }
+            wrote = true;
+          }
+          // second: add the partner's partial tile, clear what was written
+          float4v v[4][MT];
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
-                                               (int)(split * per_split) + mine + (i * MT + t) * kTile,
-                                               0, kDevScope);
-    pf_wait_vmcnt<0>();
-    pf_barrier();
-    __shared__ uint32_t arrived;
-    if (threadIdx.x == 0) {
-      const uint32_t before =
-          __hip_atomic_fetch_add(sp.counters + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (before == (uint32_t)(S - 1))
-        __hip_atomic_store(sp.counters + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      arrived = before;
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+              v[i][t] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        pres, ps * kSlot + mine + (i * MT + t) * kTile, 0,
+                                                        kDevScope));
+          pf_wait_vmcnt<0>();  // read before the slot is cleared
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[i][t] = acc[i][t] + v[i][t];
+#pragma unroll
+          for (int i = 0; i < 4 * MT; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres, ps * kSlot + mine + i * kTile,
+                                                   0, 0);
+          if (wrote) {
+#pragma unroll
+            for (int i = 0; i < 4 * MT; ++i)
+              __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
+                                                     my_slot * kSlot + mine + i * kTile, 0, 0);
+          }
+          if (threadIdx.x == 0) __hip_atomic_store(node, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        node_base += width >> 1;
+        width = (width + 1) >> 1;
+        pos >>= 1;
+      }
+      if (leave) continue;  // uniform over the workgroup
     }
-    __syncthreads();
-    if (arrived != (uint32_t)(S - 1)) return;  // uniform over the workgroup
+
+    // ---- header check ----
+    const uint32_t h_magic = __builtin_amdgcn_readfirstlane(hd0[0]);
+    const uint32_t h_format = __builtin_amdgcn_readfirstlane(hd0[1]);
+    const uint32_t h_version = __builtin_amdgcn_readfirstlane(hd0[2]);
+    const int64_t h_n = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
+                                  __builtin_amdgcn_readfirstlane(hd1[0]));
+    const int64_t h_k = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[3]) << 32) |
+                                  __builtin_amdgcn_readfirstlane(hd1[2]));
+    const float h_scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(hd2));
+    const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
+                       h_n == n && h_k == k;
+
+    // ---- epilogue: lane holds, for panel i and tile t, output channels
+    // 16 p + 4 (lane >> 4) + v (v < 4) of activation row row0 + 16 (MT wm + t) + (lane & 15) ----
+    const bool vec = (n & 3) == 0 && (((uintptr_t)y) & 7) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
+      if (n0 >= n) continue;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        float4v s = {0.f, 0.f, 0.f, 0.f};
-        for (int sx = 0; sx < S; ++sx)
-          s += __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-                                               pres, (int)(sx * per_split) + mine + (i * MT + t) * kTile,
-                                               0, kDevScope));
-        acc[i][t] = s;
-      }
-    // the only reader clears the partials (the workspace ends all zeros)
-    for (int sx = 0; sx < S; ++sx)
+        const int row = row0 + (wm * MT + t) * 16 + col;
+        if (row >= m) continue;
+        uint16_t h[4];
 #pragma unroll
-      for (int i = 0; i < 4 * MT; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
-                                               (int)(sx * per_split) + mine + i * kTile, 0, 0);
-  }
-
-  // ---- epilogue: lane holds, for panel i and tile t, output channels
-  // 16 p + 4 (lane >> 4) + v (v < 4) of activation row row0 + 16 (MT wm + t) + (lane & 15) ----
-  const bool vec = (n & 3) == 0 && (((uintptr_t)y) & 7) == 0;
+        for (int v = 0; v < 4; ++v) {
+          const float sc = FMT == kFmtNvfp4 ? h_scale : row_scale[i][v];
+          const _Float16 o = valid ? (_Float16)(sc * acc[i][t][v]) : (_Float16)__builtin_nanf("");
+          h[v] = __builtin_bit_cast(uint16_t, o);
+        }
+        uint16_t* dst = y + (int64_t)row * n + n0;
+        if (vec && n0 + 3 < n) {
+          *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                 (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t n0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
-    if (n0 >= n) continue;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int row = row0 + (wm * MT + t) * 16 + col;
-      if (row >= m) continue;
-      uint16_t h[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float sc = FMT == kFmtNvfp4 ? h_scale : row_scale[i][v];
-        const _Float16 o = valid ? (_Float16)(sc * acc[i][t][v]) : (_Float16)__builtin_nanf("");
-        h[v] = __builtin_bit_cast(uint16_t, o);
-      }
-      uint16_t* dst = y + (int64_t)row * n + n0;
-      if (vec && n0 + 3 < n) {
-        *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                               (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (n0 + v < n) dst[v] = h[v];
+          for (int v = 0; v < 4; ++v)
+            if (n0 + v < n) dst[v] = h[v];
+        }
       }
     }
   }
@@ -415,18 +488,13 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
 
 int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; }
 
-// K splits.  With 32 or 64 rows the call is HBM-bound: up to 200 workgroups
-// (not one per CU: each split adds a fix-up and partial-tile traffic).  With
-// 128 rows the matrix unit and the activation slice bound it: the split
-// count minimises whole waves of 256 workgroups times k-steps per workgroup
-// (about 0.107 us of MFMA work per activation tile and NVFP4 k-step, half
-// that per FP8 k-step) plus the partial tiles' write-and-read traffic at
-// ~5 TB/s.  Above 128 rows the wide tile (256 channels x 128 rows) takes the
-// most splits, up to 4, that keep one wave of at most 256 workgroups: the
-// last arriving workgroup of a tile reads all its partial tiles (128 KiB
-// each) alone, so more splits cost more than they bring (5120x17408 at 256
-// rows: 126.0 / 117.5 / 123.9 us with 3 / 4 / 6 splits; 17408x5120: 87.4 us
-// unsplit on 136 workgroups, 137.9 us with 2 splits on 272).
+// Work split (stream-K).  The tiles x k-steps units are cut into equal
+// contiguous ranges, one per workgroup, so that every CU streams the same
+// bytes in one wave.  A tile cut between workgroups costs one FP32 partial
+// tile written and read back (16 KiB per 32 activation rows of the narrow
+// tile, 128 KiB for the wide one).  Each range is at least kPrefillMinK of
+// K long, and with kPrefillWorkgroups or more tiles every workgroup takes
+// whole tiles (no partials; the hardware balances the waves).
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out) {
   const bool wide = m > 128;
@@ -434,59 +502,48 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   const int64_t rb = wide ? (m + 127) / 128 : 1;
   const int64_t P = panels_of(n);
   const int64_t ppb = wide ? kWidePanelsPerBlock : kPanelsPerBlock;
-  const int64_t blocks = (P + ppb - 1) / ppb * rb;  // output tiles
+  const int64_t tiles = (P + ppb - 1) / ppb * rb;
+  const int64_t ks = fmt == kFmtNvfp4 ? kNvKStep : kF8KStep;
   const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
-  const int64_t smax = std::max<int64_t>(1, J / 4);
-  auto need = [&](int64_t s) -> size_t {
-    if (s <= 1) return 0;
-    const size_t counters = ((size_t)blocks * 4 + 255) / 256 * 256;
-    return counters + (size_t)s * blocks * (kLanes * kWaves) * (4 * mt) * 16;
+  const int64_t Jt = std::max<int64_t>(J, 1);
+  const int64_t U = tiles * Jt;
+  const size_t slot = (size_t)4 * mt * (kLanes * kWaves) * 16;  // one partial tile (wide: mt = 8)
+  // the most workgroups one tile is cut between, for g workgroups
+  auto max_pieces = [&](int64_t g) -> int64_t {
+    if (g == tiles) return 1;
+    auto owner = [&](int64_t u) { return ((u + 1) * g + U - 1) / U - 1; };
+    int64_t p = 1;
+    for (int64_t t = 0; t < tiles; ++t) p = std::max<int64_t>(p, owner(t * Jt + Jt - 1) - owner(t * Jt) + 1);
+    return p;
   };
-  int64_t S = 1;
-  if (blocks > 0 && wide) {
-    S = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, 256 / blocks), smax));
-  } else if (blocks > 0 && mt <= 2) {
-    // HBM-bound: the most K splits that keep at most 200 workgroups.  Filling
-    // every CU with more splits cost more in split-K fix-ups than the CUs
-    // brought: at m = 64, 17408x5120 went from 62 to 43.6 us (one split, 136
-    // workgroups), 5120x17408 from 65.4 to 47.5 us (five splits, 200) and
-    // FP8 6144x5120 from 41.2 to 30.3 us (four splits, 192).
-    S = std::min<int64_t>(std::max<int64_t>(1, 200 / blocks), smax);
-  } else if (blocks > 0) {
-    // MFMA time of one activation tile and k-step: an FP8 k-step is 64 K,
-    // half the work of an NVFP4 one
-    const double step_us = fmt == kFmtNvfp4 ? 0.107 : 0.0535;
-    double best = 0.0;
-    for (int64_t s = 1; s <= std::min<int64_t>(smax, 16); ++s) {
-      const double waves = (double)((blocks * s + 255) / 256);
-      const double cost = waves * (double)((J + s - 1) / s) * step_us * mt +
-                          2.0 * (double)need(s) / 5e6;  // us
-      if (s == 1 || cost < best) {
-        best = cost;
-        S = s;
-      }
-    }
+  // node states of the pairwise trees (pieces - 1 per tile), then two
+  // partial tiles per workgroup
+  auto states = [&](int64_t g) -> size_t {
+    return ((size_t)tiles * (size_t)(max_pieces(g) - 1) * 4 + 255) / 256 * 256;
+  };
+  auto need = [&](int64_t g) -> size_t { return g == tiles ? 0 : states(g) + 2 * (size_t)g * slot; };
+  int64_t G = tiles;
+  const int64_t target = kPrefillWorkgroups;
+  if (J > 0 && tiles < target) {
+    const int64_t min_units = std::max<int64_t>(1, kPrefillMinK / ks);
+    G = std::max<int64_t>(tiles, std::min<int64_t>(target, U / min_units));
   }
-  int64_t steps = J > 0 ? (J + S - 1) / S : 1;
-  S = J > 0 ? (J + steps - 1) / steps : 1;
-  while (S > 1 && need(S) > ws_bytes) {
-    S -= 1;
-    steps = (J + S - 1) / S;
-    S = (J + steps - 1) / steps;
-  }
+  if (need(G) > ws_bytes) G = tiles;
   // the partial area is addressed with 32-bit offsets
-  if (need(S) >= ((size_t)1 << 31)) return kGemmNoWorkspace;
+  if (need(G) >= ((size_t)1 << 31)) return kGemmNoWorkspace;
+  const int64_t pieces = max_pieces(G);
   out->mt = mt;
   out->wide = wide;
   out->row_blocks = (int)rb;
   out->depth = 3;  // as compiled below
-  out->blocks = blocks;
-  out->splits = (int)S;
-  out->split_steps = (int)steps;
-  out->workgroups = blocks * S;
+  out->tiles = tiles;
+  out->ksteps = J;
+  out->workgroups = G;
+  out->max_pieces = (int)pieces;
+  out->nodes_per_tile = (int)std::max<int64_t>(1, pieces - 1);
   out->ws_counters_offset = 0;
-  out->ws_partial_offset = ((size_t)blocks * 4 + 255) / 256 * 256;
-  out->ws_needed = need(S);
+  out->ws_partial_offset = states(G);
+  out->ws_needed = need(G);
   return kGemmLaunchOk;
 }
 
@@ -494,14 +551,14 @@ namespace {
 
 template <uint32_t FMT, int MT, int D, int NS, bool WIDE>
 hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
-  PrefillSplit sp{l.splits, l.split_steps, l.row_blocks, nullptr, nullptr};
-  if (l.splits > 1) {
-    sp.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
-    sp.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
+  PrefillWork pw{l.tiles, l.row_blocks, l.workgroups, l.nodes_per_tile, nullptr, nullptr};
+  if (l.ws_needed > 0) {
+    pw.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
+    pw.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
   }
   hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS, WIDE>), dim3((unsigned)l.workgroups),
                      dim3(kLanes * kWaves), 0, (hipStream_t)a.stream, (const uint8_t*)a.packed,
-                     a.x, a.y, a.m, a.n, a.k, sp);
+                     a.x, a.y, a.m, a.n, a.k, pw);
   return hipGetLastError();
 }
 

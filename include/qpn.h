@@ -113,8 +113,10 @@ QPN_API size_t qpn_fp8_packed_bytes(int64_t n, int64_t k);
  * the fewest splits whose activation slice (m * K / splits FP16 values) fits
  * in LDS still fit the workspace; otherwise it returns QPN_ERR_BUFFER (only
  * for large m * k, e.g. m > 4 with k = 17408).  The prefill ops take
- * 0 <= m <= 256 and run with fewer splits (down to none) on any smaller
- * workspace.  Returns (size_t)-1 for an unknown op or invalid shape.  Pure
+ * 0 <= m <= 256; above 16 rows, when output tiles are cut between
+ * workgroups, they need one arrival counter per tile and room for two FP32
+ * partial tiles per workgroup, and on any smaller workspace every workgroup
+ * takes whole tiles.  Returns (size_t)-1 for an unknown op or invalid shape.  Pure
  * host. */
 QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
 
@@ -132,7 +134,10 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * one per half of the activation rows) and activation_rows is the 32, 64 or
  * 128 rows it takes; above 128 rows it covers 16 panels (one wavefront per
  * 4 panels) and one block of 128 rows (activation_rows 128; the row blocks
- * are separate workgroups); split_workgroups equals workgroups.  A pure function of its
+ * are separate workgroups).  The workgroups cut the (tile, k-step) pairs
+ * into equal contiguous ranges; splits is the most workgroups that one
+ * output tile is cut between (1: whole tiles), and split_workgroups equals
+ * workgroups.  A pure function of its
  * arguments, independent of any declared maximum.  Any output pointer may
  * be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
 QPN_API int qpn_gemm_plan(int op, int m, int64_t n, int64_t k, int64_t *workgroups,
@@ -227,9 +232,11 @@ QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int
  * splits the skinny kernel needs, a tiled MFMA kernel.  Both reach the same
  * parity bar.  x: [m, k] FP16, 16-byte aligned; y: [m, n] FP16.
  * workspace: zero-filled device memory, 16-byte aligned, of
- * qpn_workspace_bytes(QPN_OP_PREFILL_*, m, n, k) bytes for the preferred K
- * split (NULL with 0 bytes is valid and runs without splitting K); every
- * call leaves it zero-filled.  m > 256 gives QPN_ERR_SHAPE.  A blob whose
+ * qpn_workspace_bytes(QPN_OP_PREFILL_*, m, n, k) bytes for the preferred
+ * plan (NULL with 0 bytes is valid and runs whole tiles per workgroup);
+ * every call leaves it zero-filled.  Output tiles cut between workgroups are
+ * summed by the last of them to finish, in workgroup order, so results are
+ * deterministic.  m > 256 gives QPN_ERR_SHAPE.  A blob whose
  * header does not match gives FP16 NaN outputs.  One kernel on `stream`. */
 QPN_API int qpn_gemm_prefill_nvfp4(const void *packed, const uint16_t *x, uint16_t *y,
                                    int m, int64_t n, int64_t k, void *workspace,

@@ -298,31 +298,34 @@ def test_prefill_queries(qpn):
             ks = 128 if op == qpn.OP_PREFILL_NVFP4 else 64
             J = -(-k // ks)
             if m <= 128:   # narrow tile: 128 channels x all rows
-                blocks = -(-n // 128)
+                tiles, chans = -(-n // 128), 128
                 assert (pl.waves_per_panel, pl.panels_per_workgroup) == (2, 8)
                 assert pl.activation_rows in (32, 64, 128) and pl.activation_rows >= m
                 assert pl.activation_rows < 2 * m or pl.activation_rows == 32
             else:          # wide tile: 256 channels x 128-row blocks
-                blocks = -(-n // 256) * -(-m // 128)
+                tiles, chans = -(-n // 256) * -(-m // 128), 256
                 assert (pl.waves_per_panel, pl.panels_per_workgroup) == (1, 16)
                 assert pl.activation_rows == 128
-                assert 1 <= pl.splits <= 4 and blocks * pl.splits <= max(256, blocks)
-            assert pl.workgroups == blocks * pl.splits == pl.split_workgroups
-            assert 1 <= pl.splits <= max(1, J // 4)
-            # every split has at least one k-step and together they cover K
-            steps = -(-J // pl.splits)
-            assert (pl.splits - 1) * steps < J <= pl.splits * steps
-            assert (ws == 0) == (pl.splits == 1)
-            if pl.splits > 1:   # counters, then S partial tiles of channels x rows FP32 per tile
-                cnt = -(-blocks * 4 // 256) * 256
-                chans = 128 if m <= 128 else 256
-                assert ws == cnt + pl.splits * blocks * chans * pl.activation_rows * 4
+            # stream-K: the (tile, k-step) units cut into equal contiguous
+            # ranges, one per workgroup, at least 512 of K each, up to 256
+            # workgroups; from 256 tiles on, whole tiles
+            U = tiles * max(J, 1)
+            G = tiles if (J == 0 or tiles >= 256) else max(tiles, min(256, U // (512 // ks)))
+            assert pl.workgroups == G == pl.split_workgroups
+            owner = lambda u: ((u + 1) * G + U - 1) // U - 1
+            pieces = max(owner(t * J + J - 1) - owner(t * J) + 1 for t in range(tiles)) if G != tiles else 1
+            assert pl.splits == pieces
+            if G == tiles:
+                assert ws == 0
+            else:          # tree node states, then two FP32 partial tiles per workgroup
+                cnt = -(-tiles * (pieces - 1) * 4 // 256) * 256
+                assert ws == cnt + 2 * G * chans * pl.activation_rows * 4
         assert qpn.workspace_bytes(op, 0, 64, 64) == 0
         assert qpn.workspace_bytes(op, 257, 64, 64) == 2 ** 64 - 1
         with pytest.raises(qpn.QpnError):
             qpn.gemm_plan(op, 257, 64, 64)
-    # a long-K call is split so that most CUs get one workgroup (one wave of them)
-    assert 128 <= qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 5120, 17408).workgroups <= 256
+    # a long-K call fills every CU with one workgroup (one wave of them)
+    assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 5120, 17408).workgroups == 256
 
 
 def test_prefill_argument_errors(qpn):

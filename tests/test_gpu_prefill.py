@@ -96,25 +96,27 @@ def test_prefill_full_size_sampled(fmt, n, k):
 
 
 def test_prefill_is_deterministic_and_row_independent():
-    """Two identical calls give identical bits (split-K partials are summed
-    in split order), and a row's result does not depend on the rows around
-    it: the first 20 rows of a 200-row block equal a 20-row call bit for bit
-    (the K summation order of a row is the same in every tile)."""
+    """Two identical calls give identical bits (the workgroups that share a
+    tile are summed in workgroup order, whichever finishes last), and a
+    row's result does not depend on the rows around it: the first 150 rows
+    of a 200-row block equal a 150-row call bit for bit (same plan, so the
+    same K ranges for every tile).  A 20-row call takes the narrow tile,
+    whose K ranges differ, so it is held to parity."""
     qpn = need_gpu()
     n, k = 3000, 2048
     w = synth.weights(n, k, seed=9)
     x = synth.activations(200, k, seed=9, m_max=200)
     pw, ref = _pack(qpn, "nvfp4", w)
+    p200 = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 200, n, k)
+    assert p200.splits > 1  # tiles are cut between workgroups
     y1 = host(qpn.prefill(pw, dev(x)))
     y2 = host(qpn.prefill(pw, dev(x)))
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
     parity(y1, ref(x), "prefill 200 rows")
-    y20 = host(qpn.prefill(pw, dev(x[:20])))
-    splits = [qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, n, k).splits for m in (20, 200)]
-    if splits[0] == splits[1]:
-        assert np.array_equal(y20.view(np.uint16), y1[:20].view(np.uint16))
-    else:  # a different K split regroups the FP32 sums: parity only
-        parity(y20, ref(x[:20]), "prefill 20 rows")
+    assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 150, n, k) == p200
+    y150 = host(qpn.prefill(pw, dev(x[:150])))
+    assert np.array_equal(y150.view(np.uint16), y1[:150].view(np.uint16))
+    parity(host(qpn.prefill(pw, dev(x[:20]))), ref(x[:20]), "prefill 20 rows")
 
 
 def test_prefill_leaves_workspace_zeroed_and_runs_without_one():
