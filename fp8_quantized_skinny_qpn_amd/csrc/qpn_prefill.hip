@@ -42,10 +42,12 @@
 // by two, so the compiler sees that the reads of one never alias the
 // direct-to-LDS writes of the other and keeps the waits exact.
 //
-// Split-K (S > 1) combines FP32 partial tiles exactly as the skinny kernel
-// does: device-scope write-through partial stores, an arrival counter per
-// panel block, and the last arriver summing the S partials in split order
-// (deterministic) and clearing them.
+// Work split (stream-K).  The (tile, k-step) pairs are cut into equal
+// contiguous ranges, one per workgroup (256, one per CU, when the tiles are
+// fewer), so every CU streams the same bytes in a single wave.  A workgroup
+// runs its range as pieces, one per tile it touches.  The partial tiles of
+// a tile cut between workgroups meet pairwise up a fixed binary tree (see
+// the kernel), deterministically.
 #include <algorithm>
 
 #include "qpn_common.h"
@@ -490,11 +492,18 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 
 // Work split (stream-K).  The tiles x k-steps units are cut into equal
 // contiguous ranges, one per workgroup, so that every CU streams the same
-// bytes in one wave.  A tile cut between workgroups costs one FP32 partial
-// tile written and read back (16 KiB per 32 activation rows of the narrow
-// tile, 128 KiB for the wide one).  Each range is at least kPrefillMinK of
-// K long, and with kPrefillWorkgroups or more tiles every workgroup takes
-// whole tiles (no partials; the hardware balances the waves).
+// bytes in one wave.  A tile cut between workgroups costs FP32 partial tiles
+// written and read back (16 KiB per 32 activation rows of the narrow tile,
+// 128 KiB for the wide one) at the nodes of its pairwise tree.  Each range is
+// at least kPrefillMinK of K long, and with kPrefillWorkgroups or more tiles
+// every workgroup takes whole tiles (no partials; the hardware balances the
+// waves).  Measured on MI355X against the earlier equal K splits (at most
+// 200 workgroups up to 64 rows, a last arriver reading every partial tile):
+// 17408x5120 m = 256 85 -> 74 us, 5120x17408 m = 256 118 -> 90 us, m = 128
+// 73 -> 64 us.  512 workgroups (two per CU) lost at 32 and 64 rows (28 ->
+// 34 us), and the 256-channel tile lost below 129 rows (m = 128: 53 -> 67
+// us), its partial tiles being twice as large and its tiles cut twice as
+// often.
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out) {
   const bool wide = m > 128;
