@@ -320,7 +320,8 @@ int qpn_gemm_nvfp4_noalloc(const void* packed, const uint16_t* x, uint16_t* y, i
 namespace {
 
 int prefill_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t* y, int m,
-                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream,
+                  int spin_limit = kPrefillSpinLimit) {
   if (m < 0 || m > kMaxPrefillM) return QPN_ERR_SHAPE;
   if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
   if (m == 0 || n == 0) return QPN_OK;
@@ -340,6 +341,7 @@ int prefill_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t*
   PrefillLaunch l;
   if (prefill_launch_for(fmt, m, n, k, workspace ? workspace_bytes : 0, &l) != kGemmLaunchOk)
     return QPN_ERR_BUFFER;
+  l.spin_limit = spin_limit;
   return launch_status(launch_prefill(fmt, a, l));
 }
 
@@ -476,6 +478,14 @@ int qpn_debug_run_plan(int op, int plan, const void* packed, const uint16_t* x, 
                            workspace_bytes, stream);
     default: return QPN_ERR_SHAPE;
   }
+}
+
+int qpn_debug_prefill_no_wait(int op, const void* packed, const uint16_t* x, uint16_t* y, int m,
+                              int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (op != QPN_OP_PREFILL_NVFP4 && op != QPN_OP_PREFILL_FP8) return QPN_ERR_SHAPE;
+  return prefill_entry(op == QPN_OP_PREFILL_NVFP4 ? kFmtNvfp4 : kFmtFp8, packed, x, y, m, n, k,
+                       workspace, workspace_bytes, stream, 0);
 }
 
 int qpn_debug_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

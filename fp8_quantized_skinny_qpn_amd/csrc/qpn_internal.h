@@ -104,6 +104,7 @@ constexpr int kMaxPrefillM = 256;
 constexpr int kPrefillSkinnyRows = 16;
 constexpr int64_t kPrefillWorkgroups = 256;  // one per CU of an MI355X
 constexpr int64_t kPrefillMinK = 512;        // shortest K range of a workgroup
+constexpr int kPrefillSpinLimit = 1 << 16;   // polls (~1 us each) a contributor waits for a cut tile's others
 struct PrefillLaunch {
   int mt;               // 16-row activation tiles per wavefront (workgroup rows: narrow 32 mt, wide 16 mt)
   bool wide;            // above 128 rows: 256 channels x 128 rows per workgroup
@@ -113,7 +114,9 @@ struct PrefillLaunch {
   int64_t ksteps;       // k-steps per tile
   int64_t workgroups;   // equal ranges of the tiles x k-steps units (tiles: whole tiles)
   int max_pieces;       // the most workgroups one tile is cut between
-  int nodes_per_tile;   // pairwise-tree nodes per tile (max_pieces - 1, at least 1)
+  int state_words;      // per cut tile: arrivals, departures, a claim per contributor
+  int spin_limit;       // polls of the arrival count before a contributor stops waiting
+  bool shares;          // cut tiles summed in shares (else up the pairwise tree)
   size_t ws_counters_offset;
   size_t ws_partial_offset;
   size_t ws_needed;

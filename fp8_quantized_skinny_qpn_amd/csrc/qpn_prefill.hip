@@ -73,6 +73,7 @@ struct PFmt<kFmtFp8> {
 };
 
 constexpr int kRsrc = 0x00020000;  // raw dword access
+constexpr int kTreePieces = 3;     // cut tiles of up to this many pieces use the pairwise tree
 constexpr int kPanelsPerBlock = 8;       // narrow tile: 128 output channels per workgroup
 constexpr int kWidePanelsPerBlock = 16;  // wide tile: 256 output channels per workgroup
 constexpr int kWaves = 4;
@@ -109,15 +110,17 @@ struct PrefillWork {
   int64_t tiles;       // output tiles: channel blocks x row blocks
   int row_blocks;      // blocks of activation rows (WIDE only; 1 otherwise)
   int64_t wgs;         // workgroups; the tiles x k-steps units are cut into wgs equal ranges
-  int nodes_per_tile;  // tree nodes per cut tile
+  int state_words;     // per cut tile: arrivals, departures, one claim per contributor
+  int spin_limit;      // polls of the arrival count before a contributor stops waiting
   float* partial;      // [2 wgs][4 MT fragments][256 threads] float4 partial tiles
-  uint32_t* counters;  // [tiles][nodes_per_tile] node states (slot + 1 of a waiting partial); zero between calls
+  uint32_t* counters;  // [tiles][state_words]; zero between calls
 };
 
 // D: k-steps of weights in flight (ring R = D + 1); NS: activation slice
 // stages in LDS (2, or R when they fit), the slice being sent NS - 1 steps
 // ahead; WIDE: 16 panels x 16 MT rows per workgroup instead of 8 x 32 MT.
-template <uint32_t FMT, int MT, int D, int NS, bool WIDE>
+// SHARES: cut tiles are summed in shares (else up the pairwise tree).
+template <uint32_t FMT, int MT, int D, int NS, bool WIDE, bool SHARES>
 __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     int m, int64_t n, int64_t k, PrefillWork pw) {
@@ -207,6 +210,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     const int j0 = (int)(u - tile * Jt);
     const int nj = J > 0 ? (int)(piece_end - u) : 0;
     const bool later_piece = u != first_unit(wg);
+    const bool final_piece = piece_end == u_end;
     u = piece_end;
     const int64_t cblk = tile / pw.row_blocks;
     const int row0 = (int)(tile % pw.row_blocks) * 16 * MTW;
@@ -344,143 +348,249 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     }
     pf_wait_vmcnt<0>();  // size-zero surplus loads retired
 
-    // ---- a tile cut between workgroups: their partial tiles meet pairwise
-    // up a fixed binary tree over the workgroups in order (contributor c =
-    // w - w_first; at each level subtree pos pairs with pos ^ 1, an odd one
-    // out passes up).  At a node, the first to arrive leaves its partial
-    // tile in its own slot and names the slot in the node's state word; the
-    // second reads it, adds it (FP32 addition is commutative, so the sum
-    // does not depend on who came first) and climbs.  The workgroup that
-    // leaves the root writes the output.  The reader of a slot clears it and
-    // the node's state, so the workspace ends all zeros. ----
+    // ---- output of fragment (i, t): this lane holds output channels 16 p +
+    // 4 (lane >> 4) + v (v < 4) of activation row row0 + 16 (MT wm + t) +
+    // (lane & 15).  A blob whose header does not match gives NaN. ----
+    auto emit = [&](int i, int t, float4v sum) {
+      const int64_t n0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
+      const int row = row0 + (wm * MT + t) * 16 + col;
+      if (n0 >= n || row >= m) return;
+      const uint32_t h_magic = __builtin_amdgcn_readfirstlane(hd0[0]);
+      const uint32_t h_format = __builtin_amdgcn_readfirstlane(hd0[1]);
+      const uint32_t h_version = __builtin_amdgcn_readfirstlane(hd0[2]);
+      const int64_t h_n = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
+                                    __builtin_amdgcn_readfirstlane(hd1[0]));
+      const int64_t h_k = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[3]) << 32) |
+                                    __builtin_amdgcn_readfirstlane(hd1[2]));
+      const float h_scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(hd2));
+      const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
+                         h_n == n && h_k == k;
+      float4v rs = {h_scale, h_scale, h_scale, h_scale};
+      if constexpr (FMT == kFmtFp8)
+        rs = i == 0 ? row_scale[0] : i == 1 ? row_scale[1] : i == 2 ? row_scale[2] : row_scale[3];
+      uint16_t h[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const _Float16 o = valid ? (_Float16)(rs[v] * sum[v]) : (_Float16)__builtin_nanf("");
+        h[v] = __builtin_bit_cast(uint16_t, o);
+      }
+      uint16_t* dst = y + (int64_t)row * n + n0;
+      if ((n & 3) == 0 && (((uintptr_t)y) & 7) == 0 && n0 + 3 < n) {
+        *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                               (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n0 + v < n) dst[v] = h[v];
+      }
+    };
+
     const int64_t w_first = owner(tile * Jt), w_last = owner(tile * Jt + Jt - 1);
     if (w_first != w_last) {
-      constexpr int kDevScope = 16;  // sc1: write-through stores, coherent loads
-      constexpr int kTile = kLanes * kWaves * 16;  // bytes of one store instruction of the workgroup
-      constexpr int kSlot = 4 * MT * kTile;        // bytes of one partial tile
-      const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)pw.partial, (short)0, (int)(2 * G * kSlot), kRsrc);
-      const int mine = (int)threadIdx.x * 16;
-      // this workgroup's slot: 2 w for a piece of its first tile, 2 w + 1 for
-      // its last (only a workgroup's first and last piece can be cut)
-      const int my_slot = (int)(2 * wg + (first_unit(wg) / Jt == tile ? 0 : 1));
-      uint32_t* state = pw.counters + tile * pw.nodes_per_tile;
-      __shared__ int partner_slot;  // -1: this workgroup leaves the tree
-      int width = (int)(w_last - w_first + 1), pos = (int)(wg - w_first), node_base = 0;
-      bool leave = false;
-      while (width > 1) {
-        if ((pos ^ 1) < width) {
-          uint32_t* node = state + node_base + (pos >> 1);
-          pf_barrier();  // every wavefront has read the last partner_slot
-          if (threadIdx.x == 0) {
-            const uint32_t seen = __hip_atomic_load(node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            partner_slot = (int)seen - 1;
-          }
-          __syncthreads();
-          int ps = partner_slot;
-          bool wrote = false;
-          if (ps < 0) {
-            // first here as far as this workgroup saw: leave the partial
-            // tile, then name it (a partner that got in meanwhile is found
-            // by the failed exchange)
+    // ---- a tile cut between P workgroups (contributors c = w - w_first).
+    // Their FP32 partial tiles live in per-workgroup slots: a workgroup's
+    // piece of its first tile in slot 2 w, of its last (another tile) in
+    // slot 2 w + 1; only a workgroup's first and last piece can be cut.
+    // Up to kTreePieces contributors meet pairwise up a fixed binary tree
+    // (at each level subtree pos pairs with pos ^ 1, an odd one out passes
+    // up): the first to arrive at a node leaves its partial tile in its slot
+    // and names the slot in the node's state word; the second adds it (FP32
+    // addition is commutative, so the sum does not depend on who came first)
+    // and climbs, and the one that leaves the root writes the output.  The
+    // contributors of such tiles mostly finish at different times, so a
+    // partner is usually there already.  With more contributors, which
+    // mostly finish together, each sums a share of the fragments instead (see
+    // below).  Readers clear what they read, so the workspace ends all
+    // zeros. ----
+    constexpr int kDevScope = 16;  // sc1: write-through stores, coherent loads
+    constexpr int kTile = kLanes * kWaves * 16;  // bytes of one fragment of the workgroup
+    constexpr int kSlot = 4 * MT * kTile;        // bytes of one partial tile
+    constexpr int NF = 4 * MT;                   // fragments
+    const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)pw.partial, (short)0, (int)(2 * G * kSlot), kRsrc);
+    const int mine = (int)threadIdx.x * 16;
+    const int P = (int)(w_last - w_first + 1), c = (int)(wg - w_first);
+    static_assert(NS >= kWaves, "one LDS stage per wavefront");
+    if constexpr (!SHARES) {
+        const int my_slot = (int)(2 * wg + (first_unit(wg) / Jt == tile ? 0 : 1));
+        uint32_t* state = pw.counters + tile * pw.state_words;
+        __shared__ int partner_slot;  // -1: this workgroup leaves the tree
+        int width = (int)(w_last - w_first + 1), pos = (int)(wg - w_first), node_base = 0;
+        bool leave = false;
+        while (width > 1) {
+          if ((pos ^ 1) < width) {
+            uint32_t* node = state + node_base + (pos >> 1);
+            pf_barrier();  // every wavefront has read the last partner_slot
+            if (threadIdx.x == 0) {
+              const uint32_t seen = __hip_atomic_load(node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              partner_slot = (int)seen - 1;
+            }
+            __syncthreads();
+            int ps = partner_slot;
+            bool wrote = false;
+            if (ps < 0) {
+              // first here as far as this workgroup saw: leave the partial
+              // tile, then name it (a partner that got in meanwhile is found
+              // by the failed exchange)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
+                                                         my_slot * kSlot + mine + (i * MT + t) * kTile, 0,
+                                                         kDevScope);
+              pf_wait_vmcnt<0>();
+              pf_barrier();
+              if (threadIdx.x == 0) {
+                uint32_t expected = 0u;
+                const bool named = __hip_atomic_compare_exchange_strong(
+                    node, &expected, (uint32_t)my_slot + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                    __HIP_MEMORY_SCOPE_AGENT);
+                partner_slot = named ? -1 : (int)expected - 1;
+              }
+              __syncthreads();
+              ps = partner_slot;
+              if (ps < 0) {
+                leave = true;
+                break;
+              }
+              wrote = true;
+            }
+            // second: add the partner's partial tile, clear what was written
+            float4v v[4][MT];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int t = 0; t < MT; ++t)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
-                                                       my_slot * kSlot + mine + (i * MT + t) * kTile, 0,
-                                                       kDevScope);
-            pf_wait_vmcnt<0>();
-            pf_barrier();
-            if (threadIdx.x == 0) {
-              uint32_t expected = 0u;
-              const bool named = __hip_atomic_compare_exchange_strong(
-                  node, &expected, (uint32_t)my_slot + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                  __HIP_MEMORY_SCOPE_AGENT);
-              partner_slot = named ? -1 : (int)expected - 1;
-            }
-            __syncthreads();
-            ps = partner_slot;
-            if (ps < 0) {
-              leave = true;
-              break;
-            }
-            wrote = true;
-          }
-          // second: add the partner's partial tile, clear what was written
-          float4v v[4][MT];
+                v[i][t] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          pres, ps * kSlot + mine + (i * MT + t) * kTile, 0,
+                                                          kDevScope));
+            pf_wait_vmcnt<0>();  // read before the slot is cleared
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-              v[i][t] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        pres, ps * kSlot + mine + (i * MT + t) * kTile, 0,
-                                                        kDevScope));
-          pf_wait_vmcnt<0>();  // read before the slot is cleared
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int t = 0; t < MT; ++t) acc[i][t] = acc[i][t] + v[i][t];
-#pragma unroll
-          for (int i = 0; i < 4 * MT; ++i)
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres, ps * kSlot + mine + i * kTile,
-                                                   0, 0);
-          if (wrote) {
+              for (int t = 0; t < MT; ++t) acc[i][t] = acc[i][t] + v[i][t];
 #pragma unroll
             for (int i = 0; i < 4 * MT; ++i)
-              __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
-                                                     my_slot * kSlot + mine + i * kTile, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres, ps * kSlot + mine + i * kTile,
+                                                     0, 0);
+            if (wrote) {
+#pragma unroll
+              for (int i = 0; i < 4 * MT; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
+                                                       my_slot * kSlot + mine + i * kTile, 0, 0);
+            }
+            if (threadIdx.x == 0) __hip_atomic_store(node, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          if (threadIdx.x == 0) __hip_atomic_store(node, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          node_base += width >> 1;
+          width = (width + 1) >> 1;
+          pos >>= 1;
         }
-        node_base += width >> 1;
-        width = (width + 1) >> 1;
-        pos >>= 1;
+        if (leave) continue;  // uniform over the workgroup
+    } else {
+
+    // ---- shares (the other kind of launch): every contributor leaves its partial tile in its slot
+    // and counts itself in; then each sums its share of the tile's fragments
+    // (f = c, c + P, c + 2 P, ...) over all P partial tiles, in contributor
+    // order (deterministic whoever sums it), writes those outputs and clears
+    // them in every slot.  Only a contributor on its last piece waits for the
+    // others, and only for a bounded time: one that does not wait (or stops
+    // waiting) leaves its share unclaimed, and the last one to arrive, which
+    // never waits, takes every share still unclaimed.  The last contributor
+    // to leave resets the tile's counters. ----
+    {
+      const int b_first = first_unit(w_first) < tile * Jt ? 1 : 0;  // w_first's side
+      auto slot_of = [&](int64_t w) -> int { return (int)(2 * w + (w == w_first ? b_first : 0)) * kSlot; };
+      uint32_t* const st = pw.counters + tile * pw.state_words;  // arrivals, departures, claims[P]
+      __shared__ uint32_t sh_arrival, sh_claim;
+
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
+                                                 slot_of(wg) + mine + (i * MT + t) * kTile, 0, kDevScope);
+      pf_wait_vmcnt<0>();
+      pf_barrier();  // (also: every wavefront is done reading the LDS stages)
+      if (threadIdx.x == 0)
+        sh_arrival = __hip_atomic_fetch_add(st, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const bool last = sh_arrival == (uint32_t)(P - 1);
+      if (threadIdx.x == 0) {
+        // only a workgroup's final piece waits: an earlier one has more work
+        // to do, and the others of its tile may be waiting for that work
+        bool ready = last;
+        for (int s = 0; final_piece && !ready && s < pw.spin_limit; ++s) {
+          __builtin_amdgcn_s_sleep(2);
+          ready = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)P;
+        }
+        uint32_t expected = 0u;
+        sh_claim = ready && __hip_atomic_compare_exchange_strong(st + 2 + c, &expected, 1u, __ATOMIC_RELAXED,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (leave) continue;  // uniform over the workgroup
+      __syncthreads();
+
+      // The share of contributor cc, through this wavefront's LDS stage: per
+      // round up to `cf` fragments of all P partial tiles, one 1 KiB load per
+      // fragment, wavefront and partial tile (each lane reads back only its
+      // own 16 bytes).
+      uint8_t* const lds = stage(wv);
+      auto sum_share = [&](int cc) {
+        const int nfs = cc < NF ? (NF - 1 - cc) / P + 1 : 0;
+        const int cf = STAGE / (P * 1024);  // >= 1: the launch keeps P within the stage
+        for (int f0 = 0; f0 < nfs; f0 += cf > 0 ? cf : nfs) {
+          const int nj = min(cf, nfs - f0);
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of the stage are done
+          for (int wi = 0; wi < P; ++wi) {
+            const int so = slot_of(w_first + wi) + mine;
+            for (int j = 0; j < nj; ++j)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  pres, (__attribute__((address_space(3))) void*)(lds + (wi * cf + j) * 1024), 16,
+                  so + (cc + (f0 + j) * P) * kTile, 0, 0, kDevScope);
+          }
+          pf_wait_vmcnt<0>();
+          for (int j = 0; j < nj; ++j) {
+            const int f = cc + (f0 + j) * P;
+            float4v sum = *reinterpret_cast<const float4v*>(lds + j * 1024 + lane * 16);
+            for (int wi = 1; wi < P; ++wi)
+              sum += *reinterpret_cast<const float4v*>(lds + (wi * cf + j) * 1024 + lane * 16);
+            emit(f / MT, f % MT, sum);
+            for (int wi = 0; wi < P; ++wi)
+              __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
+                                                     slot_of(w_first + wi) + mine + f * kTile, 0, 0);
+          }
+        }
+      };
+      if (sh_claim) sum_share(c);
+      if (last) {
+        for (int cc = 0; cc < P; ++cc) {
+          if (cc == c) continue;
+          __syncthreads();  // sh_claim of the previous share has been read
+          if (threadIdx.x == 0) {
+            uint32_t expected = 0u;
+            sh_claim = __hip_atomic_compare_exchange_strong(st + 2 + cc, &expected, 1u, __ATOMIC_RELAXED,
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          __syncthreads();
+          if (sh_claim) sum_share(cc);
+        }
+      }
+      pf_wait_vmcnt<0>();  // this workgroup's outputs and clears are done
+      pf_barrier();
+      if (threadIdx.x == 0 &&
+          __hip_atomic_fetch_add(st + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1)) {
+        for (int q = 0; q < 2 + P; ++q) __hip_atomic_store(st + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    continue;
+    }
     }
 
-    // ---- header check ----
-    const uint32_t h_magic = __builtin_amdgcn_readfirstlane(hd0[0]);
-    const uint32_t h_format = __builtin_amdgcn_readfirstlane(hd0[1]);
-    const uint32_t h_version = __builtin_amdgcn_readfirstlane(hd0[2]);
-    const int64_t h_n = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
-                                  __builtin_amdgcn_readfirstlane(hd1[0]));
-    const int64_t h_k = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hd1[3]) << 32) |
-                                  __builtin_amdgcn_readfirstlane(hd1[2]));
-    const float h_scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(hd2));
-    const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
-                       h_n == n && h_k == k;
-
-    // ---- epilogue: lane holds, for panel i and tile t, output channels
-    // 16 p + 4 (lane >> 4) + v (v < 4) of activation row row0 + 16 (MT wm + t) + (lane & 15) ----
-    const bool vec = (n & 3) == 0 && (((uintptr_t)y) & 7) == 0;
+    // ---- a whole tile, or the root of a tree: the outputs ----
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t n0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
-      if (n0 >= n) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int row = row0 + (wm * MT + t) * 16 + col;
-        if (row >= m) continue;
-        uint16_t h[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float sc = FMT == kFmtNvfp4 ? h_scale : row_scale[i][v];
-          const _Float16 o = valid ? (_Float16)(sc * acc[i][t][v]) : (_Float16)__builtin_nanf("");
-          h[v] = __builtin_bit_cast(uint16_t, o);
-        }
-        uint16_t* dst = y + (int64_t)row * n + n0;
-        if (vec && n0 + 3 < n) {
-          *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                                 (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n0 + v < n) dst[v] = h[v];
-        }
-      }
-    }
+      for (int t = 0; t < MT; ++t) emit(i, t, acc[i][t]);
   }
 }
 
@@ -494,16 +604,28 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 // contiguous ranges, one per workgroup, so that every CU streams the same
 // bytes in one wave.  A tile cut between workgroups costs FP32 partial tiles
 // written and read back (16 KiB per 32 activation rows of the narrow tile,
-// 128 KiB for the wide one) at the nodes of its pairwise tree.  Each range is
-// at least kPrefillMinK of K long, and with kPrefillWorkgroups or more tiles
-// every workgroup takes whole tiles (no partials; the hardware balances the
-// waves).  Measured on MI355X against the earlier equal K splits (at most
-// 200 workgroups up to 64 rows, a last arriver reading every partial tile):
-// 17408x5120 m = 256 85 -> 74 us, 5120x17408 m = 256 118 -> 90 us, m = 128
-// 73 -> 64 us.  512 workgroups (two per CU) lost at 32 and 64 rows (28 ->
-// 34 us), and the 256-channel tile lost below 129 rows (m = 128: 53 -> 67
-// us), its partial tiles being twice as large and its tiles cut twice as
-// often.
+// 128 KiB for the wide one).  Each range is at least kPrefillMinK of K long,
+// and with kPrefillWorkgroups or more tiles every workgroup takes whole tiles
+// (no partials; the hardware balances the waves).  Measured on MI355X
+// against the earlier equal K splits (at most 200 workgroups up to 64 rows,
+// a last arriver reading every partial tile): 17408x5120 m = 256 85 -> 74
+// us, m = 128 59 -> 52 us.  512 workgroups (two per CU) lost at 32 and 64
+// rows (28 -> 34 us), and the 256-channel tile lost below 129 rows (m = 128:
+// 53 -> 67 us), its partial tiles being twice as large and its tiles cut
+// twice as often.
+//
+// Summing a cut tile: up the pairwise tree, or in shares where the partial
+// tiles are 64 KiB or more and a tile is cut more than kTreePieces ways
+// (5120x17408 at 128 and 256 rows, FP8 6144x5120 at 256 rows).  There all
+// but one contributor finish together, and the tree's levels, each a store,
+// a compare-exchange and a load of 64-128 KiB in series, made up a third of
+// the time: in shares 5120x17408 m = 128 went from 63 to 57.6 us, m = 256
+// from 90 to 80 us, and FP8 6144x5120 m = 256 from 71 to 55.5 us.  With
+// small partial tiles, or two or three contributors that finish at
+// different times, the tree measured as fast or faster.  Per-lane atomic
+// exchanges of the partial tiles (as the skinny kernel's split-K does) were
+// 1.3-1.5x slower on every shape: the atomics' throughput, not latency,
+// bounds tiles this large.
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out) {
   const bool wide = m > 128;
@@ -525,17 +647,21 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
     for (int64_t t = 0; t < tiles; ++t) p = std::max<int64_t>(p, owner(t * Jt + Jt - 1) - owner(t * Jt) + 1);
     return p;
   };
-  // node states of the pairwise trees (pieces - 1 per tile), then two
-  // partial tiles per workgroup
-  auto states = [&](int64_t g) -> size_t {
-    return ((size_t)tiles * (size_t)(max_pieces(g) - 1) * 4 + 255) / 256 * 256;
-  };
+  // per cut tile: arrival and departure counts and one claim per
+  // contributor; then two partial tiles per workgroup
+  auto state_words = [&](int64_t g) -> int64_t { return 2 + max_pieces(g); };
+  auto states = [&](int64_t g) -> size_t { return ((size_t)tiles * state_words(g) * 4 + 255) / 256 * 256; };
   auto need = [&](int64_t g) -> size_t { return g == tiles ? 0 : states(g) + 2 * (size_t)g * slot; };
   int64_t G = tiles;
   const int64_t target = kPrefillWorkgroups;
   if (J > 0 && tiles < target) {
     const int64_t min_units = std::max<int64_t>(1, kPrefillMinK / ks);
     G = std::max<int64_t>(tiles, std::min<int64_t>(target, U / min_units));
+    // a contributor sums its share of a cut tile through its wavefronts' 1
+    // KiB-per-partial LDS stages: at most (stage bytes / 1 KiB) contributors
+    // where tiles are summed in shares
+    const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? 8 : 2 * mt);
+    if ((wide || mt >= 4) && max_pieces(G) > stage_kib) G = std::max<int64_t>(tiles, tiles * (stage_kib - 1));
   }
   if (need(G) > ws_bytes) G = tiles;
   // the partial area is addressed with 32-bit offsets
@@ -549,7 +675,12 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   out->ksteps = J;
   out->workgroups = G;
   out->max_pieces = (int)pieces;
-  out->nodes_per_tile = (int)std::max<int64_t>(1, pieces - 1);
+  out->state_words = (int)(2 + pieces);
+  // Summing in shares pays when the partial tiles are large (64 KiB and up)
+  // and cut between more than kTreePieces workgroups, which then mostly
+  // finish together; otherwise the pairwise tree is cheaper.
+  out->shares = pieces > kTreePieces && (wide || mt >= 4);
+  out->spin_limit = kPrefillSpinLimit;
   out->ws_counters_offset = 0;
   out->ws_partial_offset = states(G);
   out->ws_needed = need(G);
@@ -558,14 +689,14 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
 
 namespace {
 
-template <uint32_t FMT, int MT, int D, int NS, bool WIDE>
+template <uint32_t FMT, int MT, int D, int NS, bool WIDE, bool SHARES>
 hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
-  PrefillWork pw{l.tiles, l.row_blocks, l.workgroups, l.nodes_per_tile, nullptr, nullptr};
+  PrefillWork pw{l.tiles, l.row_blocks, l.workgroups, l.state_words, l.spin_limit, nullptr, nullptr};
   if (l.ws_needed > 0) {
     pw.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
     pw.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
   }
-  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS, WIDE>), dim3((unsigned)l.workgroups),
+  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS, WIDE, SHARES>), dim3((unsigned)l.workgroups),
                      dim3(kLanes * kWaves), 0, (hipStream_t)a.stream, (const uint8_t*)a.packed,
                      a.x, a.y, a.m, a.n, a.k, pw);
   return hipGetLastError();
@@ -576,11 +707,12 @@ hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
   // 3 k-steps of weights ahead; up to 64 rows 4 slice stages measured 3-6%
   // faster than 5 ahead in 6 stages.  The wide tile's 32 KiB slices also fit
   // 4 stages.
-  if (l.wide) return launch_pf<FMT, 8, 3, 4, true>(a, l);
+  if (l.wide) return l.shares ? launch_pf<FMT, 8, 3, 4, true, true>(a, l) : launch_pf<FMT, 8, 3, 4, true, false>(a, l);
   switch (l.mt) {
-    case 1: return launch_pf<FMT, 1, 3, 4, false>(a, l);
-    case 2: return launch_pf<FMT, 2, 3, 4, false>(a, l);
-    default: return launch_pf<FMT, 4, 3, 4, false>(a, l);
+    case 1: return launch_pf<FMT, 1, 3, 4, false, false>(a, l);
+    case 2: return launch_pf<FMT, 2, 3, 4, false, false>(a, l);
+    default:
+      return l.shares ? launch_pf<FMT, 4, 3, 4, false, true>(a, l) : launch_pf<FMT, 4, 3, 4, false, false>(a, l);
   }
 }
 

@@ -66,6 +66,7 @@ def _load():
         "qpn_debug_read_ceiling": ([vp, sz, vp, vp], i32),
         "qpn_debug_plan": ([i32, i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "qpn_debug_run_plan": ([i32, i32, vp, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
+        "qpn_debug_prefill_no_wait": ([i32, vp, vp, vp, i32, i64, i64, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -84,7 +85,8 @@ EXPORTED = ("qpn_status_string", "qpn_layout_version", "qpn_nvfp4_packed_bytes",
             "qpn_lmhead_nvfp4", "qpn_lmhead_verify_nvfp4",
             "qpn_debug_unpack_nvfp4",
             "qpn_debug_unpack_fp8", "qpn_debug_decode_nvfp4", "qpn_debug_decode_fp8",
-            "qpn_debug_read_ceiling", "qpn_debug_plan", "qpn_debug_run_plan")
+            "qpn_debug_read_ceiling", "qpn_debug_plan", "qpn_debug_run_plan",
+            "qpn_debug_prefill_no_wait")
 
 
 def status_string(rc: int) -> str:
@@ -290,10 +292,11 @@ def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=Non
 
 
 def prefill(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=None,
-            ws: torch.Tensor = None) -> torch.Tensor:
+            ws: torch.Tensor = None, no_wait: bool = False) -> torch.Tensor:
     """Y = X * What^T for 0 <= m <= 256 activation rows through
-    qpn_gemm_prefill_nvfp4 / qpn_gemm_prefill_fp8.  `ws` (zero-filled before
-    its first use) defaults to a cached per-stream workspace."""
+    qpn_gemm_prefill_nvfp4 / qpn_gemm_prefill_fp8 (qpn_debug_prefill_no_wait
+    when `no_wait`).  `ws` (zero-filled before its first use) defaults to a
+    cached per-stream workspace."""
     _x_check(x, pw.k)
     m = x.shape[0]
     if out is None:
@@ -305,8 +308,12 @@ def prefill(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=
     need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
     if ws is None and need > 0:
         ws = workspace(need, x.device, ts)
-    check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k,
-             _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, st))
+    wsp, wsn = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
+    if no_wait:
+        check(lib.qpn_debug_prefill_no_wait(op, _ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k,
+                                            wsp, wsn, st))
+    else:
+        check(fn(_ptr(pw.blob), _ptr(x), _ptr(out), m, pw.n, pw.k, wsp, wsn, st))
     return out
 
 

@@ -338,6 +338,17 @@ QPN_API int qpn_debug_run_plan(int op, int plan, const void *packed, const uint1
                                uint16_t *y, int32_t *argmax, int m, int64_t n, int64_t k,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Diagnostic: qpn_gemm_prefill_nvfp4 (op QPN_OP_PREFILL_NVFP4) or
+ * qpn_gemm_prefill_fp8 (QPN_OP_PREFILL_FP8) with no waiting: where a tile
+ * is cut between workgroups that sum it in shares, none waits for the
+ * others, so the last one to arrive sums every share (the path taken when a
+ * wait runs out).  The results are bit-identical to the entry point's.
+ * Arguments, workspace rules and failure behaviour as that entry point;
+ * QPN_ERR_SHAPE for another op.  Touches no state outside its arguments. */
+QPN_API int qpn_debug_prefill_no_wait(int op, const void *packed, const uint16_t *x, uint16_t *y,
+                                      int m, int64_t n, int64_t k, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* Diagnostic: reads `bytes` (a multiple of 16, at most 2^40) of device
  * memory at `buf` once with the same nontemporal 16-byte loads the GEMM
  * kernels use; *sink is written only if a fold of the data equals a fixed

@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(qpn):
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 24
     lib = ctypes.CDLL(qpn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -310,15 +310,23 @@ def test_prefill_queries(qpn):
             # ranges, one per workgroup, at least 512 of K each, up to 256
             # workgroups; from 256 tiles on, whole tiles
             U = tiles * max(J, 1)
+
+            def pieces_of(g):
+                owner = lambda u: ((u + 1) * g + U - 1) // U - 1
+                return max(owner(t * J + J - 1) - owner(t * J) + 1 for t in range(tiles)) if g != tiles else 1
             G = tiles if (J == 0 or tiles >= 256) else max(tiles, min(256, U // (512 // ks)))
+            # tiles summed in shares (64 KiB partial tiles and up) go through
+            # 1 KiB-per-contributor LDS stages of a wavefront: at most that many
+            stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * pl.activation_rows // 16
+            if (m > 128 or pl.activation_rows == 128) and pieces_of(G) > stage_kib:
+                G = max(tiles, tiles * (stage_kib - 1))
             assert pl.workgroups == G == pl.split_workgroups
-            owner = lambda u: ((u + 1) * G + U - 1) // U - 1
-            pieces = max(owner(t * J + J - 1) - owner(t * J) + 1 for t in range(tiles)) if G != tiles else 1
+            pieces = pieces_of(G)
             assert pl.splits == pieces
             if G == tiles:
                 assert ws == 0
-            else:          # tree node states, then two FP32 partial tiles per workgroup
-                cnt = -(-tiles * (pieces - 1) * 4 // 256) * 256
+            else:          # per cut tile 2 + pieces state words, then two FP32 partial tiles per workgroup
+                cnt = -(-tiles * (2 + pieces) * 4 // 256) * 256
                 assert ws == cnt + 2 * G * chans * pl.activation_rows * 4
         assert qpn.workspace_bytes(op, 0, 64, 64) == 0
         assert qpn.workspace_bytes(op, 257, 64, 64) == 2 ** 64 - 1

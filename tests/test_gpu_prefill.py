@@ -119,6 +119,36 @@ def test_prefill_is_deterministic_and_row_independent():
     parity(host(qpn.prefill(pw, dev(x[:20]))), ref(x[:20]), "prefill 20 rows")
 
 
+# (m, n, k): tiles cut between many workgroups and summed in shares (narrow
+# 128-row and wide tiles), and one summed up the pairwise tree
+SHARE_CASES = [(96, 640, 8192), (200, 3000, 2048), (128, 1000, 6144), (200, 1500, 4096), (40, 300, 9008)]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_prefill_shares_without_waiting(fmt):
+    """No contributor waits (the path a wait that runs out takes): the last
+    to arrive sums every share.  The result must be bit-identical to the
+    normal call, the workspace must end all zeros, and both must meet the
+    oracle."""
+    qpn = need_gpu()
+    op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+    for m, n, k in SHARE_CASES:
+        pl = qpn.gemm_plan(op, m, n, k)
+        assert pl.splits > 1, (m, n, k, pl)
+        w = synth.weights(n, k, seed=m + n)
+        x = synth.activations(m, k, seed=m + n, m_max=m)
+        pw, ref = _pack(qpn, fmt, w)
+        ws = torch.zeros(qpn.workspace_bytes(op, m, n, k), dtype=torch.uint8, device="cuda")
+        log(f"prefill {fmt} {m}x{n}x{k}: {pl.workgroups} workgroups, up to {pl.splits} per tile")
+        y = host(qpn.prefill(pw, dev(x), ws=ws))
+        assert not host(ws).any()
+        y_nw = host(qpn.prefill(pw, dev(x), ws=ws, no_wait=True))
+        assert not host(ws).any()
+        assert np.array_equal(y.view(np.uint16), y_nw.view(np.uint16)), (fmt, m, n, k)
+        rows = np.unique(np.linspace(0, n - 1, 96).astype(np.int64))
+        parity(y[:, rows], ref(x, rows), f"prefill {fmt} {m}x{n}x{k} shares")
+
+
 def test_prefill_leaves_workspace_zeroed_and_runs_without_one():
     qpn = need_gpu()
     n, k = 640, 8192
