@@ -98,8 +98,8 @@ TP4 = [("tp4_qkv_fp8_K5120_N1792", 1792, 5120, "fp8"), ("tp4_o_fp8_K1280_N5120",
        ("tp4_down_nvfp4_K4352_N5120", 5120, 4352, "nvfp4")]
 TP4_LMHEAD = ("tp4_lmhead_nvfp4_K5120_N37984", 37984, 5120, "nvfp4")
 # Prefill-sized activation blocks through the tiled MFMA kernel.
-PREFILL = [("prefill_gate_up_nvfp4_K5120_N17408", 17408, 5120, "nvfp4", (16, 64, 128, 256)),
-           ("prefill_down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4", (16, 64, 128, 256)),
+PREFILL = [("prefill_gate_up_nvfp4_K5120_N17408", 17408, 5120, "nvfp4", (16, 32, 64, 128, 256)),
+           ("prefill_down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4", (16, 32, 64, 128, 256)),
            ("prefill_fp8_K5120_N6144", 6144, 5120, "fp8", (64, 256))]
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix peak
 
@@ -454,6 +454,57 @@ def summarize_pmc(counter_csv, match=""):
     return out
 
 
+def prefill_calls():
+    """The (call, m) pairs of --prefill-workload, in launch order; each is
+    launched six times in a row."""
+    return [(name, n, k, m) for name, n, k, fmt, ms in PREFILL for m in ms]
+
+
+def summarize_prefill(trace_csv, counter_csvs):
+    """The --prefill-workload runs: one row per (call, m) with its kernel,
+    median launch time and TFLOP/s from the kernel trace, and the average of
+    each counter of the given PMC passes of the same workload.  The GEMM
+    dispatches of each run are taken in dispatch order, six per call."""
+    import csv
+
+    def gemm_dispatches(path, kind):
+        rows = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = (r["Kernel_Name"].replace("(anonymous namespace)", "{anon}")
+                        .split("(")[0].replace("void ", ""))
+                if "gemm_kernel" not in name:
+                    continue
+                d = rows.setdefault(int(r["Dispatch_Id"]), {"kernel": name})
+                if kind == "trace":
+                    d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                else:
+                    d[r["Counter_Name"]] = float(r["Counter_Value"])
+        return [rows[i] for i in sorted(rows)]
+
+    calls = prefill_calls()
+    trace = gemm_dispatches(trace_csv, "trace")
+    if len(trace) != 6 * len(calls):
+        raise SystemExit(f"{trace_csv}: {len(trace)} GEMM dispatches, expected {6 * len(calls)}")
+    passes = [gemm_dispatches(c, "pmc") for c in counter_csvs]
+    for c, rows in zip(counter_csvs, passes):
+        if len(rows) != len(trace):
+            raise SystemExit(f"{c}: {len(rows)} GEMM dispatches, expected {len(trace)}")
+    counters = [sorted(k for k in rows[0] if k != "kernel") for rows in passes]
+    head = ["call", "m", "kernel", "median us", "TFLOP/s"] + [c for cs in counters for c in cs]
+    out = ["| " + " | ".join(head) + " |", "|---|---:|---|" + "---:|" * (len(head) - 3)]
+    for i, (name, n, k, m) in enumerate(calls):
+        block = trace[6 * i: 6 * i + 6]
+        us = float(np.median([d["us"] for d in block]))
+        vals = []
+        for rows, cs in zip(passes, counters):
+            b = rows[6 * i: 6 * i + 6]
+            vals += [f"{np.mean([d.get(c, 0.0) for d in b]):,.0f}" for c in cs]
+        out.append(f"| {name} | {m} | `{block[0]['kernel']}` | {us:.1f} | {2.0 * m * n * k / us / 1e6:.0f} | "
+                   + " | ".join(vals) + " |")
+    return out
+
+
 SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES")
 
 
@@ -563,6 +614,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar=("COUNTER_CSV", "MATCH"),
                     help="per-kernel counter averages from a rocprofv3 PMC pass (optionally only "
                          "kernels whose name contains MATCH)")
+    ap.add_argument("--summarize-prefill", nargs="+", metavar=("KERNEL_TRACE_CSV", "COUNTER_CSV"),
+                    help="per-call table of the --prefill-workload runs: trace times and the "
+                         "counters of any PMC passes of the same workload")
     ap.add_argument("--traffic-workload", action="store_true",
                     help="only run the workload of the PMC traffic passes (no JSON line)")
     ap.add_argument("--prefill-workload", action="store_true",
@@ -576,6 +630,9 @@ def main():
         return
     if args.summarize_pmc:  # host only: post-processes rocprofv3 output
         print("\n".join(summarize_pmc(*args.summarize_pmc[:2])))
+        return
+    if args.summarize_prefill:  # host only: post-processes rocprofv3 output
+        print("\n".join(summarize_prefill(args.summarize_prefill[0], args.summarize_prefill[1:])))
         return
     if args.summarize_trace:  # host only: post-processes rocprofv3 output
         print("\n".join(summarize_trace(args.summarize_trace)))
