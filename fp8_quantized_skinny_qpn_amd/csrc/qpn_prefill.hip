@@ -77,6 +77,19 @@ constexpr int kTreePieces = 3;     // cut tiles of up to this many pieces use th
 constexpr int kPanelsPerBlock = 8;       // narrow tile: 128 output channels per workgroup
 constexpr int kWidePanelsPerBlock = 16;  // wide tile: 256 output channels per workgroup
 constexpr int kWaves = 4;
+// Wavefronts per workgroup.  With four, the accumulators of a 128- or
+// 256-row tile fill a SIMD's registers, one wavefront per SIMD, and a wait
+// for a load left the SIMD idle: in a per-k-step ablation the MFMA time
+// (0.85 us of ~2.5 us per step at 256 rows) added to everything else.  Eight
+// wavefronts, each decoding half as many panels, put two on every SIMD:
+// 17408x5120 at 256 rows went from 75.4 to 67.3 us, at 128 rows from 52.6
+// to 47.4, at 64 rows from 36 to 33.8, at 32 rows from 27.6 to 25.8;
+// 5120x17408 at 128 rows from 57.3 to 52.5, FP8 6144x5120 at 256 rows from
+// 56.5 to 47.6 us.
+constexpr int kWideWaves = 8;  // wavefronts of a 256-channel workgroup (two panels each)
+// wavefronts of a 128-channel workgroup of 32 mt rows (8 needs a whole slice
+// load per wavefront: 2 mt 16-row tiles x the k-step's 128-byte line pairs)
+constexpr int narrow_waves(uint32_t fmt, int mt) { return mt * (fmt == kFmtNvfp4 ? 2 : 1) >= 2 ? 8 : 4; }
 
 template <int N>
 __device__ __forceinline__ void pf_wait_vmcnt() {
@@ -119,21 +132,25 @@ struct PrefillWork {
 // D: k-steps of weights in flight (ring R = D + 1); NS: activation slice
 // stages in LDS (2, or R when they fit), the slice being sent NS - 1 steps
 // ahead; WIDE: 16 panels x 16 MT rows per workgroup instead of 8 x 32 MT.
-// SHARES: cut tiles are summed in shares (else up the pairwise tree).
-template <uint32_t FMT, int MT, int D, int NS, bool WIDE, bool SHARES>
-__global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
+// SHARES: cut tiles are summed in shares (else up the pairwise tree).  WV:
+// wavefronts per workgroup, 4 or 8 (with 8, each decodes half as many
+// panels, so that two wavefronts fit a SIMD).
+template <uint32_t FMT, int MT, int D, int NS, bool WIDE, bool SHARES, int WV>
+__global__ __launch_bounds__(kLanes * WV) void prefill_gemm_kernel(
     const uint8_t* __restrict__ blob, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     int m, int64_t n, int64_t k, PrefillWork pw) {
   using F = PFmt<FMT>;
   constexpr int KS = F::kKStep;
   constexpr int GR = F::kGroups;
-  constexpr int WNN = WIDE ? 4 : 2;                  // wavefronts across panels
-  constexpr int PPB = 4 * WNN;                       // panels per workgroup
-  constexpr int MTW = (kWaves / WNN) * MT;           // 16-row activation tiles per workgroup
+  constexpr int WNN = WIDE ? WV : WV / 2;            // wavefronts across panels
+  constexpr int PPB = WIDE ? kWidePanelsPerBlock : kPanelsPerBlock;  // panels per workgroup
+  constexpr int PW = PPB / WNN;                      // panels per wavefront
+  constexpr int MTW = (WV / WNN) * MT;               // 16-row activation tiles per workgroup
+  static_assert(PW * WNN == PPB && (WV == 4 || WV == 8), "tile shape");
   constexpr int STAGE = GR * MTW * 1024;             // LDS bytes of one step's slice
-  constexpr int XQ = GR * MTW / kWaves;              // slice loads per wavefront per step
+  constexpr int XQ = GR * MTW / WV;                  // slice loads per wavefront per step
   constexpr int LPS = FMT == kFmtNvfp4 ? 2 : 1;      // weight loads per chunk
-  constexpr int WL = 4 * LPS;                        // weight loads per wavefront per step
+  constexpr int WL = PW * LPS;                       // weight loads per wavefront per step
   constexpr int R = D + 1;
   constexpr int AX = NS - 1;  // slice distance
   // Step c needs slice c and weights c.  Both went out in step c - AX when
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
   static_assert(AX >= 1 && AX <= D, "weights go at least as far ahead as slices");
   static_assert(R % NS == 0, "stages repeat within one ring cycle");
   static_assert(WAITN < 64, "vmcnt range");
-  static_assert(XQ * kWaves == GR * MTW, "slice loads split evenly");
+  static_assert(XQ * WV == GR * MTW, "slice loads split evenly");
   auto stage = [](int c) -> uint8_t* {
     switch (c % NS) {
       case 0: return slice_stage<0, STAGE>();
@@ -189,7 +206,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
   const int col = lane & 15, kg = lane >> 4;
   const int lq = lane >> 4, lslot = lane & 15;
   constexpr int H = KS / 64;  // 128-byte parts of a row's k-step
-  static_assert(XQ * kWaves == 2 * MTW * H, "one load per 8 rows and 128 bytes");
+  static_assert(XQ * WV == 2 * MTW * H, "one load per 8 rows and 128 bytes");
   // This lane's B operand of MFMA group t in the wave's first activation
   // tile: row 16 (MT wm) + col, piece kg KS / 32 + t of the k-step; the
   // next tile is 2 H loads further (two more row groups, same parity).
@@ -214,7 +231,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     u = piece_end;
     const int64_t cblk = tile / pw.row_blocks;
     const int row0 = (int)(tile % pw.row_blocks) * 16 * MTW;
-    const int64_t pbase = cblk * PPB + 4 * wn;  // first of this wavefront's 4 panels
+    const int64_t pbase = cblk * PPB + PW * wn;  // first of this wavefront's PW panels
     if (later_piece) {
       // the previous piece's stores are done and every wavefront has
       // finished reading its LDS stages
@@ -222,13 +239,13 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       pf_barrier();
     }
 
-    float4v row_scale[4] = {};
+    float4v row_scale[PW] = {};
     if constexpr (FMT == kFmtFp8) {
       // the padded scale area holds 16 P floats; panels past P read zeros
       const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(blob + kHeaderBytes), (short)0, (int)(P * kPanelRows * 4), kRsrc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PW; ++i) {
         const int64_t r0 = (pbase + i) * kPanelRows + 4 * (lane >> 4);
         const int off = pbase + i < P ? (int)(r0 * 4) : 0x7FFFFFF0;
         row_scale[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0));
@@ -237,9 +254,9 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     asm volatile("" ::: "memory");
 
     // ---- weights: chunk (p, j) at codes + (j P + p) * chunk bytes ----
-    auto issue_w = [&](int c, PFrag (&f)[4]) {
+    auto issue_w = [&](int c, PFrag (&f)[PW]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PW; ++i) {
         // the address is formed unconditionally (no access happens through a
         // descriptor of size zero), so the load itself never sits behind a branch
         const bool ok = c < nj && pbase + i < P;
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     auto issue_x = [&](int c, uint8_t* buf) {
 #pragma unroll
       for (int i = 0; i < XQ; ++i) {
-        const int q = wv + kWaves * i;
+        const int q = wv + WV * i;
         const int g = q / H, h = q % H;
         const int e = 2 * lq + ((lslot - g) & 1);
         const int row = row0 + 8 * g + (((lslot - (g & 1) - e) & 15) >> 1);
@@ -278,13 +295,13 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       }
     };
 
-    float4v acc[4][MT];
+    float4v acc[PW][MT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < PW; ++i)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    PFrag ring[R][4];
+    PFrag ring[R][PW];
     // prologue: what steps -D .. -1 would have sent (slice s + AX when it is
     // >= 0, weights s + D), in the same order, so that the wait count at the
     // top of every step is the same.  The scheduler may not move loads across
@@ -297,7 +314,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    auto step = [&](int c, const uint8_t* xread, uint8_t* xnext, PFrag (&cur)[4], PFrag (&ahead)[4]) {
+    auto step = [&](int c, const uint8_t* xread, uint8_t* xnext, PFrag (&cur)[PW], PFrag (&ahead)[PW]) {
       // everything up to this step's slice is in, then everyone's slice is
       // (and everyone is done reading the stage the next slice goes to)
       pf_wait_vmcnt<WAITN>();
@@ -308,9 +325,9 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       issue_w(c + D, ahead);
       __builtin_amdgcn_sched_barrier(0);
       if (c >= nj) return;  // padding step: loads only (no memory access)
-      half8 a[4][GR];
+      half8 a[PW][GR];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PW; ++i) {
         if constexpr (FMT == kFmtNvfp4)
           decode_nvfp4_fragment(cur[i].codes, (uint32_t)cur[i].scales, a[i]);
         else
@@ -332,7 +349,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < PW; ++i)
             acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i][t], b[t & 1][mt], acc[i][mt], 0, 0, 0);
       }
     };
@@ -366,8 +383,12 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       const bool valid = h_magic == kMagic && h_format == FMT && h_version == kLayoutVersion &&
                          h_n == n && h_k == k;
       float4v rs = {h_scale, h_scale, h_scale, h_scale};
-      if constexpr (FMT == kFmtFp8)
-        rs = i == 0 ? row_scale[0] : i == 1 ? row_scale[1] : i == 2 ? row_scale[2] : row_scale[3];
+      if constexpr (FMT == kFmtFp8) {
+        rs = row_scale[0];
+#pragma unroll
+        for (int q = 1; q < PW; ++q)
+          if (i == q) rs = row_scale[q];
+      }
       uint16_t h[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -403,14 +424,18 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
     // below).  Readers clear what they read, so the workspace ends all
     // zeros. ----
     constexpr int kDevScope = 16;  // sc1: write-through stores, coherent loads
-    constexpr int kTile = kLanes * kWaves * 16;  // bytes of one fragment of the workgroup
-    constexpr int kSlot = 4 * MT * kTile;        // bytes of one partial tile
-    constexpr int NF = 4 * MT;                   // fragments
+    constexpr int kTile = kLanes * WV * 16;      // bytes of one fragment of the workgroup
+    constexpr int kSlot = PW * MT * kTile;       // bytes of one partial tile
+    constexpr int NF = PW * MT;                  // fragments
     const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)pw.partial, (short)0, (int)(2 * G * kSlot), kRsrc);
     const int mine = (int)threadIdx.x * 16;
     const int P = (int)(w_last - w_first + 1), c = (int)(wg - w_first);
-    static_assert(NS >= kWaves, "one LDS stage per wavefront");
+    // a wavefront's own LDS region for staging partial tiles: a stage, or
+    // half of one when two wavefronts share it
+    constexpr int WPS = (WV + NS - 1) / NS;
+    constexpr int WSTAGE = STAGE / WPS;
+    static_assert(NS * WPS >= WV, "an LDS region per wavefront");
     if constexpr (!SHARES) {
         const int my_slot = (int)(2 * wg + (first_unit(wg) / Jt == tile ? 0 : 1));
         uint32_t* state = pw.counters + tile * pw.state_words;
@@ -433,7 +458,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
               // tile, then name it (a partner that got in meanwhile is found
               // by the failed exchange)
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
+              for (int i = 0; i < PW; ++i)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
                   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
@@ -457,9 +482,9 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
               wrote = true;
             }
             // second: add the partner's partial tile, clear what was written
-            float4v v[4][MT];
+            float4v v[PW][MT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < PW; ++i)
 #pragma unroll
               for (int t = 0; t < MT; ++t)
                 v[i][t] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
@@ -467,16 +492,16 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
                                                           kDevScope));
             pf_wait_vmcnt<0>();  // read before the slot is cleared
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < PW; ++i)
 #pragma unroll
               for (int t = 0; t < MT; ++t) acc[i][t] = acc[i][t] + v[i][t];
 #pragma unroll
-            for (int i = 0; i < 4 * MT; ++i)
+            for (int i = 0; i < PW * MT; ++i)
               __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres, ps * kSlot + mine + i * kTile,
                                                      0, 0);
             if (wrote) {
 #pragma unroll
-              for (int i = 0; i < 4 * MT; ++i)
+              for (int i = 0; i < PW * MT; ++i)
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pres,
                                                        my_slot * kSlot + mine + i * kTile, 0, 0);
             }
@@ -505,7 +530,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       __shared__ uint32_t sh_arrival, sh_claim;
 
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PW; ++i)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), pres,
@@ -534,10 +559,10 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
       // round up to `cf` fragments of all P partial tiles, one 1 KiB load per
       // fragment, wavefront and partial tile (each lane reads back only its
       // own 16 bytes).
-      uint8_t* const lds = stage(wv);
+      uint8_t* const lds = stage(wv / WPS) + (wv % WPS) * WSTAGE;
       auto sum_share = [&](int cc) {
         const int nfs = cc < NF ? (NF - 1 - cc) / P + 1 : 0;
-        const int cf = STAGE / (P * 1024);  // >= 1: the launch keeps P within the stage
+        const int cf = WSTAGE / (P * 1024);  // >= 1: the launch keeps P within the stage
         for (int f0 = 0; f0 < nfs; f0 += cf > 0 ? cf : nfs) {
           const int nj = min(cf, nfs - f0);
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of the stage are done
@@ -588,7 +613,7 @@ __global__ __launch_bounds__(kLanes * kWaves) void prefill_gemm_kernel(
 
     // ---- a whole tile, or the root of a tree: the outputs ----
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < PW; ++i)
 #pragma unroll
       for (int t = 0; t < MT; ++t) emit(i, t, acc[i][t]);
   }
@@ -660,7 +685,8 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
     // a contributor sums its share of a cut tile through its wavefronts' 1
     // KiB-per-partial LDS stages: at most (stage bytes / 1 KiB) contributors
     // where tiles are summed in shares
-    const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? 8 : 2 * mt);
+    const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? 8 : 2 * mt) /
+                              (((wide ? kWideWaves : narrow_waves(fmt, mt)) + 3) / 4);
     if ((wide || mt >= 4) && max_pieces(G) > stage_kib) G = std::max<int64_t>(tiles, tiles * (stage_kib - 1));
   }
   if (need(G) > ws_bytes) G = tiles;
@@ -689,15 +715,15 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
 
 namespace {
 
-template <uint32_t FMT, int MT, int D, int NS, bool WIDE, bool SHARES>
+template <uint32_t FMT, int MT, int D, int NS, bool WIDE, bool SHARES, int WV = kWaves>
 hipError_t launch_pf(const GemmArgs& a, const PrefillLaunch& l) {
   PrefillWork pw{l.tiles, l.row_blocks, l.workgroups, l.state_words, l.spin_limit, nullptr, nullptr};
   if (l.ws_needed > 0) {
     pw.counters = reinterpret_cast<uint32_t*>((uint8_t*)a.ws + l.ws_counters_offset);
     pw.partial = reinterpret_cast<float*>((uint8_t*)a.ws + l.ws_partial_offset);
   }
-  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS, WIDE, SHARES>), dim3((unsigned)l.workgroups),
-                     dim3(kLanes * kWaves), 0, (hipStream_t)a.stream, (const uint8_t*)a.packed,
+  hipLaunchKernelGGL((prefill_gemm_kernel<FMT, MT, D, NS, WIDE, SHARES, WV>), dim3((unsigned)l.workgroups),
+                     dim3(kLanes * WV), 0, (hipStream_t)a.stream, (const uint8_t*)a.packed,
                      a.x, a.y, a.m, a.n, a.k, pw);
   return hipGetLastError();
 }
@@ -707,12 +733,15 @@ hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
   // 3 k-steps of weights ahead; up to 64 rows 4 slice stages measured 3-6%
   // faster than 5 ahead in 6 stages.  The wide tile's 32 KiB slices also fit
   // 4 stages.
-  if (l.wide) return l.shares ? launch_pf<FMT, 8, 3, 4, true, true>(a, l) : launch_pf<FMT, 8, 3, 4, true, false>(a, l);
+  if (l.wide)
+    return l.shares ? launch_pf<FMT, 8, 3, 4, true, true, kWideWaves>(a, l)
+                    : launch_pf<FMT, 8, 3, 4, true, false, kWideWaves>(a, l);
   switch (l.mt) {
-    case 1: return launch_pf<FMT, 1, 3, 4, false, false>(a, l);
-    case 2: return launch_pf<FMT, 2, 3, 4, false, false>(a, l);
+    case 1: return launch_pf<FMT, 1, 3, 4, false, false, narrow_waves(FMT, 1)>(a, l);
+    case 2: return launch_pf<FMT, 2, 3, 4, false, false, narrow_waves(FMT, 2)>(a, l);
     default:
-      return l.shares ? launch_pf<FMT, 4, 3, 4, false, true>(a, l) : launch_pf<FMT, 4, 3, 4, false, false>(a, l);
+      return l.shares ? launch_pf<FMT, 4, 3, 4, false, true, narrow_waves(FMT, 4)>(a, l)
+                      : launch_pf<FMT, 4, 3, 4, false, false, narrow_waves(FMT, 4)>(a, l);
   }
 }
 

@@ -318,6 +318,8 @@ def test_prefill_queries(qpn):
             # tiles summed in shares (64 KiB partial tiles and up) go through
             # 1 KiB-per-contributor LDS stages of a wavefront: at most that many
             stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * pl.activation_rows // 16
+            if m > 64:  # eight wavefronts share the tile's four stages (128 rows and up)
+                stage_kib //= 2
             if (m > 128 or pl.activation_rows == 128) and pieces_of(G) > stage_kib:
                 G = max(tiles, tiles * (stage_kib - 1))
             assert pl.workgroups == G == pl.split_workgroups
