@@ -110,6 +110,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
 
 
+def _empty(ts, shape, dtype, device):
+    # allocated on the stream the kernel runs on, so the caching allocator
+    # never hands out a block that work queued on another stream still uses
+    with torch.cuda.stream(ts):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def nvfp4_packed_bytes(n: int, k: int) -> int:
     return int(lib.qpn_nvfp4_packed_bytes(n, k))
 
@@ -230,7 +237,7 @@ def pack_nvfp4(w: torch.Tensor, stream=None) -> PackedWeight:
     nb = nvfp4_packed_bytes(n, k)
     if nb == 0:
         raise QpnError(2, status_string(2))
-    blob = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    blob = _empty(_torch_stream(stream), (nb,), torch.uint8, w.device)
     check(lib.qpn_pack_nvfp4(_ptr(w), n, k, _ptr(blob), nb, _stream(stream)))
     return PackedWeight(blob, n, k, FMT_NVFP4)
 
@@ -241,7 +248,7 @@ def pack_fp8(w: torch.Tensor, stream=None) -> PackedWeight:
     nb = fp8_packed_bytes(n, k)
     if nb == 0:
         raise QpnError(2, status_string(2))
-    blob = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    blob = _empty(_torch_stream(stream), (nb,), torch.uint8, w.device)
     check(lib.qpn_pack_fp8(_ptr(w), n, k, _ptr(blob), nb, _stream(stream)))
     return PackedWeight(blob, n, k, FMT_FP8)
 
@@ -253,7 +260,7 @@ def requant_fp8_to_nvfp4(pw: PackedWeight, stream=None) -> PackedWeight:
     nb = nvfp4_packed_bytes(pw.n, pw.k)
     if nb == 0:
         raise QpnError(2, status_string(2))
-    blob = torch.empty(nb, dtype=torch.uint8, device=pw.blob.device)
+    blob = _empty(_torch_stream(stream), (nb,), torch.uint8, pw.blob.device)
     check(lib.qpn_requant_fp8_to_nvfp4(_ptr(pw.blob), pw.nbytes, pw.n, pw.k, _ptr(blob), nb,
                                        _stream(stream)))
     return PackedWeight(blob, pw.n, pw.k, FMT_NVFP4)
@@ -273,11 +280,11 @@ def gemm(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=Non
     before its first use) defaults to a cached per-stream workspace."""
     _x_check(x, pw.k)
     m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
-    op = OP_GEMM_NVFP4 if pw.fmt == FMT_NVFP4 else OP_GEMM_FP8
     ts = _torch_stream(stream)
     st = _stream(ts)
+    if out is None:
+        out = _empty(ts, (m, pw.n), torch.float16, x.device)
+    op = OP_GEMM_NVFP4 if pw.fmt == FMT_NVFP4 else OP_GEMM_FP8
     need = workspace_bytes(op, m, pw.n, pw.k, plan) if m > 0 else 0
     if ws is None and need > 0:
         ws = workspace(need, x.device, ts)
@@ -299,12 +306,12 @@ def prefill(pw: PackedWeight, x: torch.Tensor, out: torch.Tensor = None, stream=
     cached per-stream workspace."""
     _x_check(x, pw.k)
     m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
-    op = OP_PREFILL_NVFP4 if pw.fmt == FMT_NVFP4 else OP_PREFILL_FP8
-    fn = lib.qpn_gemm_prefill_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_prefill_fp8
     ts = _torch_stream(stream)
     st = _stream(ts)
+    if out is None:
+        out = _empty(ts, (m, pw.n), torch.float16, x.device)
+    op = OP_PREFILL_NVFP4 if pw.fmt == FMT_NVFP4 else OP_PREFILL_FP8
+    fn = lib.qpn_gemm_prefill_nvfp4 if pw.fmt == FMT_NVFP4 else lib.qpn_gemm_prefill_fp8
     need = workspace_bytes(op, m, pw.n, pw.k) if m > 0 else 0
     if ws is None and need > 0:
         ws = workspace(need, x.device, ts)
@@ -325,12 +332,12 @@ def lmhead_nvfp4(pw: PackedWeight, x: torch.Tensor, logits=None, argmax=None, wo
         raise ValueError("lm_head needs an NVFP4 blob")
     _x_check(x, pw.k)
     m = x.shape[0]
-    if logits is None:
-        logits = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
-    if argmax is None:
-        argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
     ts = _torch_stream(stream)
     st = _stream(ts)
+    if logits is None:
+        logits = _empty(ts, (m, pw.n), torch.float16, x.device)
+    if argmax is None:
+        argmax = _empty(ts, (m,), torch.int32, x.device)
     need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k, plan)
     ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, ts)
     if plan == 0:
@@ -354,14 +361,14 @@ def lmhead_verify_nvfp4(pw: PackedWeight, x: torch.Tensor, draft: torch.Tensor, 
         raise ValueError("draft must be int32 [m - 1]")
     if draft.numel() and (draft.device != x.device or not draft.is_contiguous()):
         raise ValueError("draft must be contiguous on the activation's device")
-    if logits is None:
-        logits = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
-    if argmax is None:
-        argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
-    if result is None:
-        result = torch.empty((2,), dtype=torch.int32, device=x.device)
     ts = _torch_stream(stream)
     st = _stream(ts)
+    if logits is None:
+        logits = _empty(ts, (m, pw.n), torch.float16, x.device)
+    if argmax is None:
+        argmax = _empty(ts, (m,), torch.int32, x.device)
+    if result is None:
+        result = _empty(ts, (2,), torch.int32, x.device)
     need = workspace_bytes(OP_LMHEAD_NVFP4, m, pw.n, pw.k)
     ws = workspace_ if workspace_ is not None else workspace(max(need, 8), x.device, ts)
     check(lib.qpn_lmhead_verify_nvfp4(_ptr(pw.blob), _ptr(x), _ptr(logits), _ptr(argmax),
@@ -372,10 +379,10 @@ def lmhead_verify_nvfp4(pw: PackedWeight, x: torch.Tensor, draft: torch.Tensor, 
 
 def debug_unpack_nvfp4(pw: PackedWeight, stream=None):
     """Canonical (codes [n, k/2], scales [n, k/16], g) read back from the blob."""
-    dev = pw.blob.device
-    codes = torch.empty((pw.n, pw.k // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((pw.n, pw.k // 16), dtype=torch.uint8, device=dev)
-    g = torch.empty((1,), dtype=torch.float32, device=dev)
+    dev, ts = pw.blob.device, _torch_stream(stream)
+    codes = _empty(ts, (pw.n, pw.k // 2), torch.uint8, dev)
+    scales = _empty(ts, (pw.n, pw.k // 16), torch.uint8, dev)
+    g = _empty(ts, (1,), torch.float32, dev)
     check(lib.qpn_debug_unpack_nvfp4(_ptr(pw.blob), pw.n, pw.k, _ptr(codes), _ptr(scales), _ptr(g),
                                      _stream(stream)))
     return codes, scales, g
@@ -383,9 +390,9 @@ def debug_unpack_nvfp4(pw: PackedWeight, stream=None):
 
 def debug_unpack_fp8(pw: PackedWeight, stream=None):
     """Canonical (codes [n, k], row_scale [n]) read back from the blob."""
-    dev = pw.blob.device
-    codes = torch.empty((pw.n, pw.k), dtype=torch.uint8, device=dev)
-    rs = torch.empty((pw.n,), dtype=torch.float32, device=dev)
+    dev, ts = pw.blob.device, _torch_stream(stream)
+    codes = _empty(ts, (pw.n, pw.k), torch.uint8, dev)
+    rs = _empty(ts, (pw.n,), torch.float32, dev)
     check(lib.qpn_debug_unpack_fp8(_ptr(pw.blob), pw.n, pw.k, _ptr(codes), _ptr(rs),
                                    _stream(stream)))
     return codes, rs
@@ -393,14 +400,14 @@ def debug_unpack_fp8(pw: PackedWeight, stream=None):
 
 def debug_decode_nvfp4(codes16: torch.Tensor, scales2: torch.Tensor, stream=None) -> torch.Tensor:
     f = codes16.shape[0]
-    out = torch.empty((f, 32), dtype=torch.float16, device=codes16.device)
+    out = _empty(_torch_stream(stream), (f, 32), torch.float16, codes16.device)
     check(lib.qpn_debug_decode_nvfp4(_ptr(codes16), _ptr(scales2), f, _ptr(out), _stream(stream)))
     return out
 
 
 def debug_decode_fp8(codes16: torch.Tensor, stream=None) -> torch.Tensor:
     f = codes16.shape[0]
-    out = torch.empty((f, 16), dtype=torch.float16, device=codes16.device)
+    out = _empty(_torch_stream(stream), (f, 16), torch.float16, codes16.device)
     check(lib.qpn_debug_decode_fp8(_ptr(codes16), f, _ptr(out), _stream(stream)))
     return out
 
