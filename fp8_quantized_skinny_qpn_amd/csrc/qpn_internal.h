@@ -95,7 +95,8 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 
 // Prefill-sized activation blocks (9 <= m <= 256): one launch of the tiled
 // MFMA kernel, 128 output channels by 32 mt activation rows per workgroup up
-// to 128 rows, 256 channels by 128 rows above.
+// to 128 rows, 256 channels by 128-row blocks above (and by 32 or 64 rows
+// for NVFP4 blocks of 17-64 rows when that fills half the CUs).
 // Calls of up to kPrefillSkinnyRows rows run the skinny kernel instead, with
 // a 16-row activation tile that fills the MFMA's B operand exactly (the
 // weights stream once, as at m <= 8), unless the workspace given is too
@@ -104,11 +105,12 @@ constexpr int kMaxPrefillM = 256;
 constexpr int kPrefillSkinnyRows = 16;
 constexpr int64_t kPrefillWorkgroups = 256;  // one per CU of an MI355X
 constexpr int64_t kPrefillMinK = 512;        // shortest K range of a workgroup
+constexpr int64_t kPrefillPieceK = 1024;     // shortest piece of a tile summed in shares
 constexpr int kPrefillSpinLimit = 1 << 16;   // polls (~1 us each) a contributor waits for a cut tile's others
 struct PrefillLaunch {
   int mt;               // 16-row activation tiles per wavefront (workgroup rows: narrow 32 mt, wide 16 mt)
-  bool wide;            // above 128 rows: 256 channels x 128 rows per workgroup
-  int row_blocks;       // blocks of 128 rows (wide), else 1
+  bool wide;            // 256 channels per workgroup (else 128)
+  int row_blocks;       // blocks of 16 mt rows (wide), else 1
   int depth;            // k-steps of weight loads in flight per wavefront
   int64_t tiles;        // output tiles: channel blocks x row blocks
   int64_t ksteps;       // k-steps per tile

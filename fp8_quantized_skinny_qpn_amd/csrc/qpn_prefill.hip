@@ -10,44 +10,39 @@
 // At 2M flops per weight the work turns from HBM-bound (M below ~90 on
 // MI355X) to matrix-unit-bound.
 //
-// Work split.  Up to 128 rows, a workgroup of four wavefronts owns 8
-// consecutive 16-row panels (128 output channels) and all BM = 32 MT
-// activation rows, over one K range ("split"); wavefront (wn, wm) decodes
-// panels 4 wn .. 4 wn + 3 and multiplies them against activation tiles MT wm
-// .. MT wm + MT - 1, so each decoded weight fragment feeds MT MFMAs and each
-// activation fragment read from LDS feeds 4.  Above 128 rows (WIDE) a
-// workgroup owns 16 panels (256 channels) and one block of 128 rows, the
-// four wavefronts side by side (wavefront w: panels 4 w .. 4 w + 3, all 8
-// tiles of the block), so that every wavefront loads only its own weights
-// and the 32 KiB activation slice of a k-step serves twice the channels.  A
-// CU pulls only ~25-30 GB/s from L2 and beyond on MI355X, so the bytes a
-// workgroup fetches per k-step set the pace: 32 KiB of activations and 18
-// KiB of weights per 256 x 128 x 128 x 2 flops here, against 64 KiB and 18
-// KiB (every panel loaded by two wavefronts) per 128 x 256 x 128 x 2 for the
-// narrow tile at 256 rows: 17408x5120 at 256 rows went from 108.5 to 87 us.
-// The activation slice of a k-step reaches LDS through loads of whole
-// 128-byte lines, swizzled so that the MFMA operand reads are free of bank
-// conflicts (see issue_x).
+// Tiles.  A workgroup of eight wavefronts owns one tile: 8 consecutive
+// 16-row panels (128 output channels, "narrow") or 16 panels (256 channels,
+// "wide"), by a block of 32, 64 or 128 activation rows.  In the narrow tile
+// the wavefronts are 4 across the panels by 2 across the rows (each decodes
+// 2 panels against half the rows); in the wide tile they stand side by side
+// (each decodes 2 panels against all the rows), so a k-step's activation
+// slice serves twice the channels.  Each decoded weight fragment feeds one
+// MFMA per 16-row activation tile, each activation fragment read from LDS
+// feeds 2.  A CU pulls only ~25-30 GB/s from L2 and beyond on MI355X, so the
+// bytes a workgroup fetches per k-step set the pace, and the wide tile
+// fetches half the activation bytes per channel: it runs above 128 rows
+// (two row blocks from 129 rows) and, for NVFP4, from 17 to 64 rows when it
+// still gives half the CUs a workgroup (launch choice below).  The
+// activation slice of a k-step reaches LDS through loads of whole 128-byte
+// lines, swizzled so that the MFMA operand reads are free of bank conflicts
+// (see issue_x).
 //
 // Pipeline per k-step c (static wait counts; loads of a wavefront complete
-// in order):
-//   wait until this wavefront's loads for step c are in; barrier (everyone's
-//   activation slice for c is in LDS, and everyone is done reading the
-//   buffer the next slice goes to);
-//   send the activation slice of step c + 1 to the other LDS buffer
-//   (direct-to-LDS loads) and the weights of step c + D to the register
-//   ring;
-//   decode step c's weights, MFMAs against the slice in LDS.
-// The two slices live in two separate LDS arrays and the loop is unrolled
-// by two, so the compiler sees that the reads of one never alias the
-// direct-to-LDS writes of the other and keeps the waits exact.
+// in order): wait until this wavefront's loads for step c are in; barrier
+// (everyone's slice for c is in LDS, and everyone is done reading the stage
+// the next slice goes to); send the slice of step c + NS - 1 to its LDS
+// stage (direct-to-LDS loads) and the weights of step c + D to the register
+// ring; decode step c's weights, MFMAs against the slice in LDS.  The NS
+// stages are separate LDS objects and the loop is unrolled by the ring
+// length, so the compiler sees that the reads of one stage never alias the
+// direct-to-LDS writes of another and keeps the waits exact.
 //
-// Work split (stream-K).  The (tile, k-step) pairs are cut into equal
-// contiguous ranges, one per workgroup (256, one per CU, when the tiles are
-// fewer), so every CU streams the same bytes in a single wave.  A workgroup
-// runs its range as pieces, one per tile it touches.  The partial tiles of
-// a tile cut between workgroups meet pairwise up a fixed binary tree (see
-// the kernel), deterministically.
+// Work split (stream-K).  The (tile, k-step) pairs are cut into contiguous
+// ranges, one per workgroup (up to 256, one per CU, when the tiles are
+// fewer), so every CU streams about the same bytes in a single wave.  A
+// workgroup runs its range as pieces, one per tile it touches.  The partial
+// tiles of a tile cut between workgroups are summed deterministically, up
+// a fixed pairwise tree or in shares (see the kernel).
 #include <algorithm>
 
 #include "qpn_common.h"
@@ -628,16 +623,38 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 // Work split (stream-K).  The tiles x k-steps units are cut into equal
 // contiguous ranges, one per workgroup, so that every CU streams the same
 // bytes in one wave.  A tile cut between workgroups costs FP32 partial tiles
-// written and read back (16 KiB per 32 activation rows of the narrow tile,
-// 128 KiB for the wide one).  Each range is at least kPrefillMinK of K long,
-// and with kPrefillWorkgroups or more tiles every workgroup takes whole tiles
-// (no partials; the hardware balances the waves).  Measured on MI355X
-// against the earlier equal K splits (at most 200 workgroups up to 64 rows,
-// a last arriver reading every partial tile): 17408x5120 m = 256 85 -> 74
-// us, m = 128 59 -> 52 us.  512 workgroups (two per CU) lost at 32 and 64
-// rows (28 -> 34 us), and the 256-channel tile lost below 129 rows (m = 128:
-// 53 -> 67 us), its partial tiles being twice as large and its tiles cut
-// twice as often.
+// written and read back (16 KiB per 32 activation rows and 128 channels).
+// Each range is at least kPrefillMinK of K long, and with kPrefillWorkgroups
+// or more tiles every workgroup takes whole tiles (no partials; the hardware
+// balances the waves).  Measured on MI355X against the earlier equal K
+// splits (at most 200 workgroups up to 64 rows, a last arriver reading every
+// partial tile): 17408x5120 m = 256 85 -> 74 us, m = 128 59 -> 52 us.  512
+// workgroups (two per CU) lost at 32 and 64 rows (28 -> 34 us).
+//
+// Whole pieces.  Where tiles are summed in shares (128-row and wide tiles),
+// a range that straddles two tiles leaves its workgroup two partial tiles
+// of up to 128 KiB to write and two shares to sum, and restarts its
+// pipeline.  There the workgroup count is instead a multiple c of the
+// tiles, so every workgroup runs exactly one piece of one tile: c as large
+// as 256 workgroups and the shares' LDS staging allow, each piece at least
+// kPrefillPieceK of K.  Same-box A/B against the equal ranges of 256
+// workgroups: 5120x17408 at 128 / 256 rows 52.4 -> 45.4 / 72.1 -> 65.7 us;
+// FP8 6144x5120 36.1 -> 30.0 / 47.4 -> 39.8; FP8 5120x5120 35.6 -> 28.3 /
+// 46.1 -> 36.9; NVFP4 5120x4096 33.4 -> 25.4 / 42.9 -> 37.3; FP8 7168x5120
+// at 256 rows 51.0 -> 44.5.  With at least 512 of K per piece (more pieces)
+// the FP8 5120x5120 and NVFP4 5120x4096 calls were 4-12% slower again.  With
+// 136 or more tiles (17408x5120) only c = 1 fits, whole tiles on 136 CUs,
+// which lost to 256 equal ranges (45.4 against 50.9 us at 128 rows).  Tiles
+// summed up the tree keep the equal ranges, whose contributors finish at
+// different times (aligned pieces: 5120x17408 at 32 rows 26.3 -> 27.7 us).
+//
+// The wide tile at 17-64 NVFP4 rows.  Fewer, larger tiles: taken when that
+// launch still has at least 128 workgroups.  A/B: 17408x5120 at 32 / 64 rows
+// 25.9 -> 22.2 / 34.8 -> 32.4 us; 5120x17408 at 64 rows 37.4 -> 37.0.  At
+// 5120x17408 and 32 rows it would have 60 workgroups (three pieces of each
+// of 20 tiles, the most its 32-row shares stage holds) and took 37 against
+// 28 us; at 128 rows it lost on every shape tried (5120x17408: 45.7 against
+// 43.5 us with whole pieces both).
 //
 // Summing a cut tile: up the pairwise tree, or in shares where the partial
 // tiles are 64 KiB or more and a tile is cut more than kTreePieces ways
@@ -651,19 +668,34 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 // exchanges of the partial tiles (as the skinny kernel's split-K does) were
 // 1.3-1.5x slower on every shape: the atomics' throughput, not latency,
 // bounds tiles this large.
-int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
-                       PrefillLaunch* out) {
-  const bool wide = m > 128;
-  const int mt = prefill_tiles(m);
-  const int64_t rb = wide ? (m + 127) / 128 : 1;
+namespace {
+
+// One tile shape's launch: the workgroup count and the most pieces a tile
+// is cut into.
+struct PfShape {
+  bool wide;
+  int mt;
+  int64_t rb, tiles, J, G, pieces;
+  size_t states, need;
+};
+
+PfShape prefill_shape(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes, bool wide) {
+  PfShape sh{};
+  sh.wide = wide;
+  const int mt = wide ? (m <= 32 ? 2 : m <= 64 ? 4 : 8) : prefill_tiles(m);
+  sh.mt = mt;
+  sh.rb = (m + 16 * (wide ? mt : 2 * mt) - 1) / (16 * (wide ? mt : 2 * mt));
   const int64_t P = panels_of(n);
   const int64_t ppb = wide ? kWidePanelsPerBlock : kPanelsPerBlock;
-  const int64_t tiles = (P + ppb - 1) / ppb * rb;
+  const int64_t tiles = (P + ppb - 1) / ppb * sh.rb;
+  sh.tiles = tiles;
   const int64_t ks = fmt == kFmtNvfp4 ? kNvKStep : kF8KStep;
   const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
+  sh.J = J;
   const int64_t Jt = std::max<int64_t>(J, 1);
   const int64_t U = tiles * Jt;
-  const size_t slot = (size_t)4 * mt * (kLanes * kWaves) * 16;  // one partial tile (wide: mt = 8)
+  // one partial tile: 128 or 256 channels x the tile's rows, FP32
+  const size_t slot = (size_t)ppb * kPanelRows * 16 * (wide ? mt : 2 * mt) * 4;
   // the most workgroups one tile is cut between, for g workgroups
   auto max_pieces = [&](int64_t g) -> int64_t {
     if (g == tiles) return 1;
@@ -674,25 +706,58 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   };
   // per cut tile: arrival and departure counts and one claim per
   // contributor; then two partial tiles per workgroup
-  auto state_words = [&](int64_t g) -> int64_t { return 2 + max_pieces(g); };
-  auto states = [&](int64_t g) -> size_t { return ((size_t)tiles * state_words(g) * 4 + 255) / 256 * 256; };
+  auto states = [&](int64_t g) -> size_t { return ((size_t)tiles * (2 + max_pieces(g)) * 4 + 255) / 256 * 256; };
   auto need = [&](int64_t g) -> size_t { return g == tiles ? 0 : states(g) + 2 * (size_t)g * slot; };
   int64_t G = tiles;
   const int64_t target = kPrefillWorkgroups;
   if (J > 0 && tiles < target) {
     const int64_t min_units = std::max<int64_t>(1, kPrefillMinK / ks);
     G = std::max<int64_t>(tiles, std::min<int64_t>(target, U / min_units));
-    // a contributor sums its share of a cut tile through its wavefronts' 1
-    // KiB-per-partial LDS stages: at most (stage bytes / 1 KiB) contributors
-    // where tiles are summed in shares
-    const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? 8 : 2 * mt) /
-                              (((wide ? kWideWaves : narrow_waves(fmt, mt)) + 3) / 4);
-    if ((wide || mt >= 4) && max_pieces(G) > stage_kib) G = std::max<int64_t>(tiles, tiles * (stage_kib - 1));
+    // Tile shapes whose cut tiles are summed in shares (large partial
+    // tiles).  A contributor sums its share through its wavefronts' 1
+    // KiB-per-partial LDS stages, so at most (stage bytes / 1 KiB)
+    // contributors.  And every workgroup takes one whole piece of one tile
+    // (G a multiple of the tiles): a range that straddles two tiles leaves
+    // two partial tiles to write and sum and restarts the pipeline.  Each
+    // piece keeps at least kPrefillPieceK of K.
+    if (wide || mt >= 4) {
+      const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? mt : 2 * mt) /
+                                (((wide ? kWideWaves : narrow_waves(fmt, mt)) + 3) / 4);
+      if (target / tiles >= 2) {
+        const int64_t c = std::min<int64_t>(std::min<int64_t>(target / tiles, stage_kib),
+                                            std::max<int64_t>(1, J * ks / kPrefillPieceK));
+        G = tiles * c;
+      } else if (max_pieces(G) > stage_kib) {
+        G = std::max<int64_t>(tiles, tiles * (stage_kib - 1));
+      }
+    }
   }
   if (need(G) > ws_bytes) G = tiles;
+  sh.G = G;
+  sh.pieces = max_pieces(G);
+  sh.states = states(G);
+  sh.need = need(G);
+  return sh;
+}
+
+}  // namespace
+
+int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
+                       PrefillLaunch* out) {
+  PfShape sh = prefill_shape(fmt, m, n, k, ws_bytes, m > 128);
+  // NVFP4 blocks of 17 to 64 rows: the 256-channel tile when it still fills
+  // half the CUs or more
+  if (fmt == kFmtNvfp4 && m > kPrefillSkinnyRows && m <= 64) {
+    const PfShape w = prefill_shape(fmt, m, n, k, ws_bytes, true);
+    if (w.G >= kPrefillWorkgroups / 2) sh = w;
+  }
   // the partial area is addressed with 32-bit offsets
-  if (need(G) >= ((size_t)1 << 31)) return kGemmNoWorkspace;
-  const int64_t pieces = max_pieces(G);
+  if (sh.need >= ((size_t)1 << 31)) return kGemmNoWorkspace;
+  const int64_t G = sh.G, tiles = sh.tiles, J = sh.J;
+  const int mt = sh.mt;
+  const bool wide = sh.wide;
+  const int64_t rb = sh.rb;
+  const int64_t pieces = sh.pieces;
   out->mt = mt;
   out->wide = wide;
   out->row_blocks = (int)rb;
@@ -708,8 +773,8 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   out->shares = pieces > kTreePieces && (wide || mt >= 4);
   out->spin_limit = kPrefillSpinLimit;
   out->ws_counters_offset = 0;
-  out->ws_partial_offset = states(G);
-  out->ws_needed = need(G);
+  out->ws_partial_offset = sh.states;
+  out->ws_needed = sh.need;
   return kGemmLaunchOk;
 }
 
@@ -733,9 +798,18 @@ hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
   // 3 k-steps of weights ahead; up to 64 rows 4 slice stages measured 3-6%
   // faster than 5 ahead in 6 stages.  The wide tile's 32 KiB slices also fit
   // 4 stages.
-  if (l.wide)
+  if (l.wide) {
+    if constexpr (FMT == kFmtNvfp4) {
+      if (l.mt == 2)
+        return l.shares ? launch_pf<FMT, 2, 3, 4, true, true, kWideWaves>(a, l)
+                        : launch_pf<FMT, 2, 3, 4, true, false, kWideWaves>(a, l);
+      if (l.mt == 4)
+        return l.shares ? launch_pf<FMT, 4, 3, 4, true, true, kWideWaves>(a, l)
+                        : launch_pf<FMT, 4, 3, 4, true, false, kWideWaves>(a, l);
+    }
     return l.shares ? launch_pf<FMT, 8, 3, 4, true, true, kWideWaves>(a, l)
                     : launch_pf<FMT, 8, 3, 4, true, false, kWideWaves>(a, l);
+  }
   switch (l.mt) {
     case 1: return launch_pf<FMT, 1, 3, 4, false, false, narrow_waves(FMT, 1)>(a, l);
     case 2: return launch_pf<FMT, 2, 3, 4, false, false, narrow_waves(FMT, 2)>(a, l);

@@ -129,14 +129,17 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * split_workgroups, the workgroups that work on K ranges (split_workgroups
  * / splits panel groups of the last panels, dispatched first).  The other
  * workgroups - 0 unless the plan balances whole panels per CU - each take
- * panels_per_workgroup whole panels.  For the prefill ops above 16 rows:
- * up to 128 rows every workgroup covers 8 panels (two wavefronts per panel,
- * one per half of the activation rows) and activation_rows is the 32, 64 or
- * 128 rows it takes; above 128 rows it covers 16 panels (one wavefront per
- * 4 panels) and one block of 128 rows (activation_rows 128; the row blocks
- * are separate workgroups).  The workgroups cut the (tile, k-step) pairs
- * into equal contiguous ranges; splits is the most workgroups that one
- * output tile is cut between (1: whole tiles), and split_workgroups equals
+ * panels_per_workgroup whole panels.  For the prefill ops above 16 rows a
+ * workgroup covers either 8 panels (waves_per_panel 2: a wavefront per half
+ * of the activation rows) or 16 panels (waves_per_panel 1; above 128 rows,
+ * and for NVFP4 at 17-64 rows when that launch still has 128 workgroups or
+ * more) by activation_rows = 32, 64 or 128 rows (the fewest that hold m, at
+ * most 128; more rows are further row blocks, as separate workgroups).  The
+ * workgroups cut the (tile, k-step) pairs into contiguous ranges: equal
+ * ones, or, where the partial tiles are summed in shares (128 rows or 16
+ * panels), a whole piece of one tile each, the workgroup count a multiple
+ * of the tile count.  splits is the most workgroups that one output tile
+ * is cut between (1: whole tiles), and split_workgroups equals
  * workgroups.  A pure function of its
  * arguments, independent of any declared maximum.  Any output pointer may
  * be NULL.  Returns QPN_OK or QPN_ERR_SHAPE.  Pure host. */
@@ -235,8 +238,8 @@ QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int
  * qpn_workspace_bytes(QPN_OP_PREFILL_*, m, n, k) bytes for the preferred
  * plan (NULL with 0 bytes is valid and runs whole tiles per workgroup);
  * every call leaves it zero-filled.  Output tiles cut between workgroups are
- * summed by the last of them to finish, in workgroup order, so results are
- * deterministic.  m > 256 gives QPN_ERR_SHAPE.  A blob whose
+ * summed in an order fixed by the launch (a pairwise tree over the pieces,
+ * or each output in piece order), so results are deterministic.  m > 256 gives QPN_ERR_SHAPE.  A blob whose
  * header does not match gives FP16 NaN outputs.  One kernel on `stream`. */
 QPN_API int qpn_gemm_prefill_nvfp4(const void *packed, const uint16_t *x, uint16_t *y,
                                    int m, int64_t n, int64_t k, void *workspace,

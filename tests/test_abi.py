@@ -284,8 +284,9 @@ def test_requant_argument_errors(qpn):
 def test_prefill_queries(qpn):
     for op in (qpn.OP_PREFILL_NVFP4, qpn.OP_PREFILL_FP8):
         for m, n, k in [(9, 17408, 5120), (16, 5120, 17408), (17, 17408, 5120), (64, 5120, 17408),
-                        (256, 17408, 5120), (256, 5120, 17408), (130, 200, 1024), (1, 16, 64),
-                        (256, 6144, 5120)]:
+                        (32, 5120, 17408), (64, 17408, 5120), (128, 5120, 17408), (128, 6144, 5120),
+                        (128, 5120, 4096), (256, 17408, 5120), (256, 5120, 17408), (130, 200, 1024),
+                        (1, 16, 64), (256, 6144, 5120), (256, 5120, 5120), (100, 40000, 1024)]:
             pl = qpn.gemm_plan(op, m, n, k)
             ws = qpn.workspace_bytes(op, m, n, k)
             if m <= 16:
@@ -297,33 +298,39 @@ def test_prefill_queries(qpn):
                 continue
             ks = 128 if op == qpn.OP_PREFILL_NVFP4 else 64
             J = -(-k // ks)
-            if m <= 128:   # narrow tile: 128 channels x all rows
-                tiles, chans = -(-n // 128), 128
-                assert (pl.waves_per_panel, pl.panels_per_workgroup) == (2, 8)
-                assert pl.activation_rows in (32, 64, 128) and pl.activation_rows >= m
-                assert pl.activation_rows < 2 * m or pl.activation_rows == 32
-            else:          # wide tile: 256 channels x 128-row blocks
-                tiles, chans = -(-n // 256) * -(-m // 128), 256
-                assert (pl.waves_per_panel, pl.panels_per_workgroup) == (1, 16)
-                assert pl.activation_rows == 128
-            # stream-K: the (tile, k-step) units cut into equal contiguous
-            # ranges, one per workgroup, at least 512 of K each, up to 256
-            # workgroups; from 256 tiles on, whole tiles
-            U = tiles * max(J, 1)
+            # a workgroup's rows: 32, 64 or 128 (the fewest that hold m), at
+            # most 128 per row block; 128 channels (narrow) or 256 (wide)
+            rows = 32 if m <= 32 else 64 if m <= 64 else 128
 
-            def pieces_of(g):
-                owner = lambda u: ((u + 1) * g + U - 1) // U - 1
-                return max(owner(t * J + J - 1) - owner(t * J) + 1 for t in range(tiles)) if g != tiles else 1
-            G = tiles if (J == 0 or tiles >= 256) else max(tiles, min(256, U // (512 // ks)))
-            # tiles summed in shares (64 KiB partial tiles and up) go through
-            # 1 KiB-per-contributor LDS stages of a wavefront: at most that many
-            stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * pl.activation_rows // 16
-            if m > 64:  # eight wavefronts share the tile's four stages (128 rows and up)
-                stage_kib //= 2
-            if (m > 128 or pl.activation_rows == 128) and pieces_of(G) > stage_kib:
-                G = max(tiles, tiles * (stage_kib - 1))
+            def launch(wide):
+                chans = 256 if wide else 128
+                tiles = -(-n // chans) * -(-m // rows)
+                U = tiles * max(J, 1)
+
+                def pieces_of(g):
+                    owner = lambda u: ((u + 1) * g + U - 1) // U - 1
+                    return max(owner(t * J + J - 1) - owner(t * J) + 1 for t in range(tiles)) if g != tiles else 1
+                # stream-K: the (tile, k-step) units cut into equal contiguous
+                # ranges, one per workgroup, at least 512 of K each, up to 256
+                # workgroups; from 256 tiles on, whole tiles
+                G = tiles if (J == 0 or tiles >= 256) else max(tiles, min(256, U // (512 // ks)))
+                # tiles of 128 rows or 256 channels are summed in shares through
+                # 1 KiB-per-contributor LDS stages (eight wavefronts, two per stage)
+                if (wide or rows == 128) and J > 0 and tiles < 256:
+                    stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * rows // 16 // 2
+                    if 256 // tiles >= 2:
+                        # whole pieces: a multiple of the tiles, each piece >= 1024 of K
+                        G = tiles * min(256 // tiles, stage_kib, max(1, J * ks // 1024))
+                    elif pieces_of(G) > stage_kib:
+                        G = max(tiles, tiles * (stage_kib - 1))
+                return chans, tiles, G, pieces_of(G)
+            wide = m > 128
+            if op == qpn.OP_PREFILL_NVFP4 and m <= 64 and launch(True)[2] >= 128:
+                wide = True   # 17-64 NVFP4 rows: 256 channels when that still fills half the CUs
+            chans, tiles, G, pieces = launch(wide)
+            assert (pl.waves_per_panel, pl.panels_per_workgroup) == ((1, 16) if wide else (2, 8))
+            assert pl.activation_rows == rows
             assert pl.workgroups == G == pl.split_workgroups
-            pieces = pieces_of(G)
             assert pl.splits == pieces
             if G == tiles:
                 assert ws == 0
@@ -334,8 +341,15 @@ def test_prefill_queries(qpn):
         assert qpn.workspace_bytes(op, 257, 64, 64) == 2 ** 64 - 1
         with pytest.raises(qpn.QpnError):
             qpn.gemm_plan(op, 257, 64, 64)
-    # a long-K call fills every CU with one workgroup (one wave of them)
-    assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 5120, 17408).workgroups == 256
+    # 5120x17408 at 256 rows: 40 tiles, each cut into six whole pieces (one per workgroup)
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 5120, 17408)
+    assert (pl.workgroups, pl.splits) == (240, 6)
+    # 17408x5120 at 32 rows: 68 tiles of 256 channels, three pieces each
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 32, 17408, 5120)
+    assert (pl.workgroups, pl.splits, pl.panels_per_workgroup) == (204, 3, 16)
+    # 5120x17408 at 32 rows: the wide tile would leave 60 workgroups; 128 channels, 256 workgroups
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 32, 5120, 17408)
+    assert (pl.workgroups, pl.panels_per_workgroup) == (256, 8)
 
 
 def test_prefill_argument_errors(qpn):

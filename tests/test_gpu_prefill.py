@@ -8,8 +8,8 @@ The same parity bar as the skinny GEMM: per element |err| <= 1e-2 rms(ref)
 + 1e-3 and relative Frobenius error <= 2e-3 against the FP64 oracle product
 of the canonical codes.  Shapes span several 128- and 256-channel blocks,
 ragged N and M tails, K splits, every activation-tile count (32, 64, 128
-rows), the wide tile's two 128-row blocks (129 to 256 rows) and the full
-decoder shapes (sampled output channels).
+rows), the wide tile at 17 to 64 rows and its two 128-row blocks (129 to 256
+rows), and the full decoder shapes (sampled output channels).
 """
 import numpy as np
 import pytest
@@ -87,12 +87,31 @@ def test_prefill_full_size_sampled(fmt, n, k):
     x = synth.activations(256, k, seed=7, m_max=256)
     pw, ref = _pack(qpn, fmt, w)
     rows = np.sort(np.concatenate([np.random.default_rng(n).choice(n - 1, 191, replace=False), [n - 1]]))
-    for m in (16, 64, 128, 256):
+    for m in (16, 32, 64, 128, 256):
         log(f"prefill full {fmt} {n}x{k} m={m}")
         y = host(qpn.prefill(pw, dev(x[:m])))
         parity(y[:, rows], ref(x[:m], rows), f"prefill full {fmt} {n}x{k} m={m}")
     y = host(_prefill_one_range(qpn, pw, dev(x[:128])))
     parity(y[:, rows], ref(x[:128], rows), f"prefill full {fmt} {n}x{k} m=128 one K range")
+
+
+def test_prefill_wide_tile_small_blocks():
+    """17-64 NVFP4 rows on the 256-channel tile (32- and 64-row tiles, taken
+    when the call still fills half the CUs): ragged N (33 blocks, the last
+    one 8 channels) and M, with and without a workspace, every output."""
+    qpn = need_gpu()
+    n, k = 8200, 4096
+    w = synth.weights(n, k, seed=8200)
+    x = synth.activations(64, k, seed=8200, m_max=64)
+    pw, ref = _pack(qpn, "nvfp4", w)
+    for m in (17, 31, 32, 33, 50, 64):
+        pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, n, k)
+        assert pl.panels_per_workgroup == 16 and pl.splits > 1, (m, pl)
+        log(f"prefill wide {n}x{k} m={m}: {pl.workgroups} workgroups, {pl.splits} per tile")
+        xd = dev(x[:m])
+        y_ref = ref(x[:m])
+        parity(host(qpn.prefill(pw, xd)), y_ref, f"prefill wide {n}x{k} m={m}")
+        parity(host(_prefill_one_range(qpn, pw, xd)), y_ref, f"prefill wide {n}x{k} m={m} one K range")
 
 
 def test_prefill_is_deterministic_and_row_independent():
