@@ -105,7 +105,8 @@ constexpr int kMaxPrefillM = 256;
 constexpr int kPrefillSkinnyRows = 16;
 constexpr int64_t kPrefillWorkgroups = 256;  // one per CU of an MI355X
 constexpr int64_t kPrefillMinK = 512;        // shortest K range of a workgroup
-constexpr int64_t kPrefillPieceK = 1024;     // shortest piece of a tile summed in shares
+constexpr int64_t kPrefillPieceK = 1024;     // shortest piece of a tile cut into whole pieces
+constexpr int64_t kPrefillMaxPieceK = 4096;  // longest such piece (else equal ranges)
 constexpr int kPrefillSpinLimit = 1 << 16;   // polls (~1 us each) a contributor waits for a cut tile's others
 struct PrefillLaunch {
   int mt;               // 16-row activation tiles per wavefront (workgroup rows: narrow 32 mt, wide 16 mt)

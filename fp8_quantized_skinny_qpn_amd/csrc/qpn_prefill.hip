@@ -631,22 +631,26 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 // partial tile): 17408x5120 m = 256 85 -> 74 us, m = 128 59 -> 52 us.  512
 // workgroups (two per CU) lost at 32 and 64 rows (28 -> 34 us).
 //
-// Whole pieces.  Where tiles are summed in shares (128-row and wide tiles),
-// a range that straddles two tiles leaves its workgroup two partial tiles
-// of up to 128 KiB to write and two shares to sum, and restarts its
-// pipeline.  There the workgroup count is instead a multiple c of the
-// tiles, so every workgroup runs exactly one piece of one tile: c as large
-// as 256 workgroups and the shares' LDS staging allow, each piece at least
-// kPrefillPieceK of K.  Same-box A/B against the equal ranges of 256
-// workgroups: 5120x17408 at 128 / 256 rows 52.4 -> 45.4 / 72.1 -> 65.7 us;
-// FP8 6144x5120 36.1 -> 30.0 / 47.4 -> 39.8; FP8 5120x5120 35.6 -> 28.3 /
-// 46.1 -> 36.9; NVFP4 5120x4096 33.4 -> 25.4 / 42.9 -> 37.3; FP8 7168x5120
-// at 256 rows 51.0 -> 44.5.  With at least 512 of K per piece (more pieces)
-// the FP8 5120x5120 and NVFP4 5120x4096 calls were 4-12% slower again.  With
-// 136 or more tiles (17408x5120) only c = 1 fits, whole tiles on 136 CUs,
-// which lost to 256 equal ranges (45.4 against 50.9 us at 128 rows).  Tiles
-// summed up the tree keep the equal ranges, whose contributors finish at
-// different times (aligned pieces: 5120x17408 at 32 rows 26.3 -> 27.7 us).
+// Whole pieces.  A range that straddles two tiles leaves its workgroup two
+// partial tiles to write and two shares to sum, and restarts its pipeline.
+// So the workgroup count is a multiple c of the tiles wherever that keeps
+// the pieces between kPrefillPieceK and kPrefillMaxPieceK of K, and every
+// workgroup runs exactly one piece of one tile; c is as large as 256
+// workgroups and the shares' LDS staging allow.  The pieces of a tile then
+// finish together, so they are summed in shares (above kTreePieces).
+// Same-box A/B against equal ranges over 256 workgroups: 5120x17408 at 128
+// / 256 rows 52.4 -> 45.4 / 72.1 -> 65.7 us; FP8 6144x5120 at 64 / 128 /
+// 256 rows 26.3 -> 21.5 / 36.1 -> 30.0 / 47.4 -> 39.8; FP8 5120x5120 at 32 /
+// 64 / 128 / 256 rows 19.7 -> 18.6 / 27.7 -> 20.6 / 35.6 -> 28.3 / 46.1 ->
+// 36.9; NVFP4 5120x4096 at 32 / 64 / 128 / 256 rows 18.9 -> 15.6 / 26.1 ->
+// 18.5 / 33.4 -> 25.4 / 42.9 -> 37.3; FP8 7168x5120 at 32 / 64 / 256 rows
+// 20.8 -> 19.7 / 27.1 -> 22.2 / 51.0 -> 44.5.  With pieces of 512 K (more of
+// them) the FP8 5120x5120 and NVFP4 5120x4096 calls were 4-12% slower
+// again.  5120x17408 at 32 rows would get four pieces of 4352 K (its 32-row
+// shares stage holds four): 160 workgroups, 27.7 -> 29.3 us, hence the
+// longest piece.  With 136 or more tiles (17408x5120) only c = 1 fits,
+// whole tiles on 136 CUs, which lost to 256 equal ranges (45.4 against 50.9
+// us at 128 rows).
 //
 // The wide tile at 17-64 NVFP4 rows.  Fewer, larger tiles: taken when that
 // launch still has at least 128 workgroups.  A/B: 17408x5120 at 32 / 64 rows
@@ -673,7 +677,7 @@ namespace {
 // One tile shape's launch: the workgroup count and the most pieces a tile
 // is cut into.
 struct PfShape {
-  bool wide;
+  bool wide, shares;
   int mt;
   int64_t rb, tiles, J, G, pieces;
   size_t states, need;
@@ -709,32 +713,41 @@ PfShape prefill_shape(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes
   auto states = [&](int64_t g) -> size_t { return ((size_t)tiles * (2 + max_pieces(g)) * 4 + 255) / 256 * 256; };
   auto need = [&](int64_t g) -> size_t { return g == tiles ? 0 : states(g) + 2 * (size_t)g * slot; };
   int64_t G = tiles;
+  bool whole = false;
   const int64_t target = kPrefillWorkgroups;
   if (J > 0 && tiles < target) {
     const int64_t min_units = std::max<int64_t>(1, kPrefillMinK / ks);
     G = std::max<int64_t>(tiles, std::min<int64_t>(target, U / min_units));
-    // Tile shapes whose cut tiles are summed in shares (large partial
-    // tiles).  A contributor sums its share through its wavefronts' 1
+    // A contributor sums its share of a cut tile through its wavefronts' 1
     // KiB-per-partial LDS stages, so at most (stage bytes / 1 KiB)
-    // contributors.  And every workgroup takes one whole piece of one tile
-    // (G a multiple of the tiles): a range that straddles two tiles leaves
-    // two partial tiles to write and sum and restarts the pipeline.  Each
-    // piece keeps at least kPrefillPieceK of K.
-    if (wide || mt >= 4) {
-      const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? mt : 2 * mt) /
-                                (((wide ? kWideWaves : narrow_waves(fmt, mt)) + 3) / 4);
-      if (target / tiles >= 2) {
-        const int64_t c = std::min<int64_t>(std::min<int64_t>(target / tiles, stage_kib),
-                                            std::max<int64_t>(1, J * ks / kPrefillPieceK));
-        G = tiles * c;
-      } else if (max_pieces(G) > stage_kib) {
-        G = std::max<int64_t>(tiles, tiles * (stage_kib - 1));
-      }
+    // contributors where tiles are summed in shares.
+    const int64_t stage_kib = (fmt == kFmtNvfp4 ? 4 : 2) * (wide ? mt : 2 * mt) /
+                              (((wide ? kWideWaves : narrow_waves(fmt, mt)) + 3) / 4);
+    // Whole pieces: every workgroup takes one piece of one tile (G a
+    // multiple of the tiles), as many pieces per tile as 256 workgroups and
+    // the staging allow, each at least kPrefillPieceK of K; a range that
+    // straddles two tiles leaves two partial tiles to write and sum and
+    // restarts the pipeline.  Unless that leaves pieces longer than
+    // kPrefillMaxPieceK of K: then equal ranges over all the CUs.
+    const int64_t c = std::min<int64_t>(std::min<int64_t>(target / tiles, stage_kib),
+                                        std::max<int64_t>(1, J * ks / kPrefillPieceK));
+    if (c >= 2 && J * ks <= c * kPrefillMaxPieceK) {
+      G = tiles * c;
+      whole = true;
+    } else if ((wide || mt >= 4) && max_pieces(G) > stage_kib) {
+      G = std::max<int64_t>(tiles, tiles * (stage_kib - 1));
     }
   }
-  if (need(G) > ws_bytes) G = tiles;
+  if (need(G) > ws_bytes) {
+    G = tiles;
+    whole = false;
+  }
   sh.G = G;
   sh.pieces = max_pieces(G);
+  // Summing in shares pays where the contributors mostly finish together:
+  // whole pieces, or large partial tiles (128 rows, 256 channels) cut more
+  // than kTreePieces ways; otherwise the pairwise tree is cheaper.
+  sh.shares = sh.pieces > kTreePieces && (whole || wide || mt >= 4);
   sh.states = states(G);
   sh.need = need(G);
   return sh;
@@ -767,10 +780,7 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
   out->workgroups = G;
   out->max_pieces = (int)pieces;
   out->state_words = (int)(2 + pieces);
-  // Summing in shares pays when the partial tiles are large (64 KiB and up)
-  // and cut between more than kTreePieces workgroups, which then mostly
-  // finish together; otherwise the pairwise tree is cheaper.
-  out->shares = pieces > kTreePieces && (wide || mt >= 4);
+  out->shares = sh.shares;
   out->spin_limit = kPrefillSpinLimit;
   out->ws_counters_offset = 0;
   out->ws_partial_offset = sh.states;
@@ -811,8 +821,12 @@ hipError_t launch_pf_fmt(const GemmArgs& a, const PrefillLaunch& l) {
                     : launch_pf<FMT, 8, 3, 4, true, false, kWideWaves>(a, l);
   }
   switch (l.mt) {
-    case 1: return launch_pf<FMT, 1, 3, 4, false, false, narrow_waves(FMT, 1)>(a, l);
-    case 2: return launch_pf<FMT, 2, 3, 4, false, false, narrow_waves(FMT, 2)>(a, l);
+    case 1:
+      return l.shares ? launch_pf<FMT, 1, 3, 4, false, true, narrow_waves(FMT, 1)>(a, l)
+                      : launch_pf<FMT, 1, 3, 4, false, false, narrow_waves(FMT, 1)>(a, l);
+    case 2:
+      return l.shares ? launch_pf<FMT, 2, 3, 4, false, true, narrow_waves(FMT, 2)>(a, l)
+                      : launch_pf<FMT, 2, 3, 4, false, false, narrow_waves(FMT, 2)>(a, l);
     default:
       return l.shares ? launch_pf<FMT, 4, 3, 4, false, true, narrow_waves(FMT, 4)>(a, l)
                       : launch_pf<FMT, 4, 3, 4, false, false, narrow_waves(FMT, 4)>(a, l);

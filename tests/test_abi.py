@@ -286,7 +286,8 @@ def test_prefill_queries(qpn):
         for m, n, k in [(9, 17408, 5120), (16, 5120, 17408), (17, 17408, 5120), (64, 5120, 17408),
                         (32, 5120, 17408), (64, 17408, 5120), (128, 5120, 17408), (128, 6144, 5120),
                         (128, 5120, 4096), (256, 17408, 5120), (256, 5120, 17408), (130, 200, 1024),
-                        (1, 16, 64), (256, 6144, 5120), (256, 5120, 5120), (100, 40000, 1024)]:
+                        (1, 16, 64), (256, 6144, 5120), (256, 5120, 5120), (100, 40000, 1024),
+                        (32, 6144, 5120), (40, 300, 9008), (40, 300, 20000), (64, 5120, 4096)]:
             pl = qpn.gemm_plan(op, m, n, k)
             ws = qpn.workspace_bytes(op, m, n, k)
             if m <= 16:
@@ -314,14 +315,18 @@ def test_prefill_queries(qpn):
                 # ranges, one per workgroup, at least 512 of K each, up to 256
                 # workgroups; from 256 tiles on, whole tiles
                 G = tiles if (J == 0 or tiles >= 256) else max(tiles, min(256, U // (512 // ks)))
-                # tiles of 128 rows or 256 channels are summed in shares through
-                # 1 KiB-per-contributor LDS stages (eight wavefronts, two per stage)
-                if (wide or rows == 128) and J > 0 and tiles < 256:
-                    stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * rows // 16 // 2
-                    if 256 // tiles >= 2:
-                        # whole pieces: a multiple of the tiles, each piece >= 1024 of K
-                        G = tiles * min(256 // tiles, stage_kib, max(1, J * ks // 1024))
-                    elif pieces_of(G) > stage_kib:
+                shares = False
+                if J > 0 and tiles < 256:
+                    # tiles summed in shares go through 1 KiB-per-contributor LDS
+                    # stages: four per workgroup, shared by two of its eight
+                    # wavefronts (four wavefronts for FP8 32-row tiles: one each)
+                    waves = 4 if (op == qpn.OP_PREFILL_FP8 and not wide and rows == 32) else 8
+                    stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * rows // 16 // (waves // 4)
+                    # whole pieces: a multiple of the tiles, each piece 1024 to 4096 of K
+                    c = min(256 // tiles, stage_kib, max(1, J * ks // 1024))
+                    if c >= 2 and J * ks <= c * 4096:
+                        G, shares = tiles * c, True
+                    elif (wide or rows == 128) and pieces_of(G) > stage_kib:
                         G = max(tiles, tiles * (stage_kib - 1))
                 return chans, tiles, G, pieces_of(G)
             wide = m > 128
@@ -347,9 +352,13 @@ def test_prefill_queries(qpn):
     # 17408x5120 at 32 rows: 68 tiles of 256 channels, three pieces each
     pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 32, 17408, 5120)
     assert (pl.workgroups, pl.splits, pl.panels_per_workgroup) == (204, 3, 16)
-    # 5120x17408 at 32 rows: the wide tile would leave 60 workgroups; 128 channels, 256 workgroups
+    # 5120x17408 at 32 rows: the wide tile would leave 80 workgroups, and four
+    # whole pieces of 4352 K each are too long: equal ranges over 256 workgroups
     pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 32, 5120, 17408)
     assert (pl.workgroups, pl.panels_per_workgroup) == (256, 8)
+    # FP8 5120x5120 at 64 rows: 40 tiles in four whole pieces of 1280 K
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, 64, 5120, 5120)
+    assert (pl.workgroups, pl.splits) == (160, 4)
 
 
 def test_prefill_argument_errors(qpn):

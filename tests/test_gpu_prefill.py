@@ -139,7 +139,7 @@ def test_prefill_is_deterministic_and_row_independent():
 
 
 # (m, n, k): tiles cut between many workgroups and summed in shares (narrow
-# 128-row and wide tiles), and one summed up the pairwise tree
+# 64- and 128-row tiles, wide tiles)
 SHARE_CASES = [(96, 640, 8192), (200, 3000, 2048), (128, 1000, 6144), (200, 1500, 4096), (40, 300, 9008)]
 
 

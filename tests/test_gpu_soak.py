@@ -37,8 +37,8 @@ CASES = [
     ("gemm", "nvfp4", 1, 5120, 17408, 4), ("gemm", "nvfp4", 1, 4805, 16000, 6),
     ("lmhead", "nvfp4", 2, 300, 2048, 2), ("lmhead", "nvfp4", 8, 1000, 4096, 3),
     ("prefill", "nvfp4", 16, 300, 9008, 7), ("prefill", "fp8", 9, 300, 4096, 7),
-    ("prefill", "nvfp4", 40, 300, 9008, 19), ("prefill", "nvfp4", 200, 1500, 4096, 4),
-    ("prefill", "fp8", 128, 1000, 6144, 6),
+    ("prefill", "nvfp4", 40, 300, 9008, 8), ("prefill", "nvfp4", 200, 1500, 4096, 4),
+    ("prefill", "fp8", 128, 1000, 6144, 6), ("prefill", "fp8", 40, 300, 20000, 39),
     ("noalloc", "nvfp4", 8, 300, 8192, 7),
 ]
 
