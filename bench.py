@@ -100,7 +100,8 @@ TP4_LMHEAD = ("tp4_lmhead_nvfp4_K5120_N37984", 37984, 5120, "nvfp4")
 # Prefill-sized activation blocks through the tiled MFMA kernel.
 PREFILL = [("prefill_gate_up_nvfp4_K5120_N17408", 17408, 5120, "nvfp4", (16, 32, 64, 128, 256)),
            ("prefill_down_nvfp4_K17408_N5120", 5120, 17408, "nvfp4", (16, 32, 64, 128, 256)),
-           ("prefill_fp8_K5120_N6144", 6144, 5120, "fp8", (64, 256))]
+           ("prefill_fp8_K5120_N6144", 6144, 5120, "fp8", (32, 64, 128, 256)),
+           ("prefill_fp8_K5120_N5120", 5120, 5120, "fp8", (32, 64, 128, 256))]
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix peak
 
 
