@@ -69,7 +69,9 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
     tmp = lib + ".tmp"
-    link_extra = ["-shared-libsan", *HOST_SANITIZE] if sanitize else []
+    # every symbol resolved at link time: a kernel whose host-side launch
+    # stub the compiler did not emit fails here, not when the library loads
+    link_extra = ["-shared-libsan", *HOST_SANITIZE] if sanitize else ["-Wl,--no-undefined"]
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
