@@ -784,7 +784,17 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   // placement 0 spreads the panels thinner (down to one per workgroup)
   // before splitting K further; placement 1 keeps every workgroup's G panel
   // slots filled and splits K instead.
-  if (pl.placement == 0 && groups * S < want) groups = std::min<int64_t>(P, (want + S - 1) / S);
+  // Shared-slice plans whose K the LDS budget already splits: when twice
+  // the splits of G-panel groups still fit in one workgroup per CU (256),
+  // take them instead of spreading panels thinner.  Each workgroup then
+  // stages half the activation slice for the same weight bytes, and the
+  // per-CU fetch is what sets the pace: 5120x17408 at M = 4 (S = 2 -> 4, 192
+  // -> 256 workgroups of five panels) went from 14.95 to 13.77 us.
+  if (pl.placement == 0 && pl.panels_per_workgroup > 2 && S > 1 && groups * S < want &&
+      groups * 2 * S <= 256 && (J + 2 * S - 1) / (2 * S) >= 2 * pl.waves_per_panel)
+    S *= 2;
+  else if (pl.placement == 0 && groups * S < want)
+    groups = std::min<int64_t>(P, (want + S - 1) / S);
   if (groups < 1) groups = 1;
   while (groups * S < want && (J + S) / (S + 1) >= 2 * pl.waves_per_panel) ++S;
   auto need = [&](int64_t s) -> size_t { return need_for(s, groups); };

@@ -6,7 +6,8 @@ remainder split (256 to 767 panels with a remainder of 16 or more) over a
 long K (64 or more k-steps; eight wavefronts per panel for NVFP4, four for
 FP8) and over a short K with 512 or more panels (four wavefronts); whole
 panels for a short K below 512 panels; five NVFP4 panels or two FP8 panels
-per workgroup above 2 (NVFP4) or 4 (FP8) rows; eight NVFP4 panels per
+per workgroup above 2 (NVFP4) or 4 (FP8) rows (with twice the K splits the
+LDS budget forces when those still fit 256 workgroups); eight NVFP4 panels per
 workgroup for 2048 or more panels when they fill whole rounds of 256 CUs.
 The plan fields reported through the C ABI are asserted first, so each case
 covers the branch it names.
@@ -31,6 +32,7 @@ CASES = [
     ("nvfp4", 8704, 2048, 1, 4, 1, True, "remainder split, short K, >= 512 panels"),
     ("nvfp4", 5120, 2048, 1, 4, 1, False, "whole panels, short K, < 512 panels"),
     ("nvfp4", 4100, 2048, 5, 3, 5, False, "five panels per workgroup"),
+    ("nvfp4", 4100, 10368, 4, 3, 5, False, "five panels per workgroup, LDS-forced K splits doubled"),
     ("fp8", 4100, 2048, 6, 4, 2, False, "two FP8 panels per workgroup"),
     ("nvfp4", 32768, 512, 2, 2, 8, False, "eight panels per workgroup, 2 rows"),
     ("nvfp4", 32768, 512, 8, 2, 8, False, "eight panels per workgroup, 8 rows"),
@@ -55,6 +57,8 @@ def test_automatic_plan_branch(fmt, n, k, m, wpp, ppw, whole, branch):
     w = synth.weights(n, k, seed=n + k + m)
     x = synth.activations(m, k, seed=n + k + m)
     pw, ref = _pack(qpn, fmt, w)
+    if "doubled" in branch:
+        assert (pl.workgroups, pl.splits) == (208, 4), pl   # 52 groups of five panels
     log(f"plan branch '{branch}': {fmt} {n}x{k} m={m}, {pl.workgroups} workgroups, {pl.splits} splits")
     parity(host(qpn.gemm(pw, dev(x))), ref(x), f"{branch}: {fmt} {n}x{k} m={m}")
 
