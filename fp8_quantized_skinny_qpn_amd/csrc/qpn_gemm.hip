@@ -605,6 +605,7 @@ constexpr GemmPlan kPlans[] = {
     {3, 5, 3, 0, 192, 1},     // 11: plan 2, VALU dot
     {4, 1, 4, 0, 128, 1},     // 12: plan 1, VALU dot
     {2, 8, 4, 0, 256},        // 13
+    {1, 16, 4, 0, 256},       // 14
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -624,6 +625,7 @@ hipError_t launch_plan(const GemmArgs& a, const GemmLaunch& l) {
     case 11: return launch_mb<FMT, 3, 5, 3, ARGMAX, true>(a, l);
     case 12: return launch_mb<FMT, 4, 1, 4, ARGMAX, true>(a, l);
     case 13: return launch_mb<FMT, 2, 8, 4, ARGMAX>(a, l);
+    case 14: return launch_mb<FMT, 1, 16, 4, ARGMAX>(a, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -671,6 +673,17 @@ int gemm_activation_rows(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 
 //     M=8 went from 88.6 to 75.8 us, M=4 from 78.4 to 69.0 us, 65536x5120
 //     M=8 from 42.3 to 34.3 us, and at M=2 151936x5120 from 72.0 to 67.1 us;
 //     with 297 workgroups (37984x5120) it lost, and at M=1 it ties plan 1.
+//   NVFP4 m >= 2 with 8-16 panels per CU where neither the eight- nor the
+//     five-panel workgroups fill their rounds of 256 CUs to 82%: one
+//     workgroup per CU holding all of its panels, one wavefront each, so
+//     each CU stages the slice once.  49152x5120 (3072 panels; 615
+//     five-panel workgroups fill 80%) at M = 2 / 4 / 8 went from 25.4 / 27.5
+//     / 30.6 to 24.3 / 24.8 / 26.1 us.  At 34816x5120 (2176 panels, 85%) it
+//     won at M = 8 on one box (23.7 -> 22.0 us) and lost at M = 2 and 4 on
+//     another (19.0 -> 20.1, 19.9 -> 21.4), so it is not used there.  Where a
+//     plan fills its rounds (2048, 2560, 3968 panels) it lost by 2-7%, and
+//     with 4.25 panels per CU (17408x5120 M=8) by 13%: a workgroup of four
+//     or five wavefronts hides less latency than fifteen.
 namespace {
 double round_fill(int64_t workgroups) {  // average / largest workgroups per CU
   const int64_t rounds = (workgroups + 255) / 256;
@@ -697,6 +710,9 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
   // NVFP4 1792x5120 M=4 6.6 against 8.2 us, FP8 1792x5120 M=8 7.4 against 8.4
   if (P < 256) return 1;
   if (fmt == kFmtNvfp4) {
+    if (m >= 2 && P >= 8 * 256 && P <= 16 * 256 &&
+        std::max(round_fill((P + 7) / 8), round_fill((P + 4) / 5)) < 0.82)
+      return 14;
     if (m >= 2 && P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02)
       return 13;
     if (m <= 2) return uneven ? 4 : uneven_short ? 5 : 1;

@@ -121,8 +121,8 @@ def test_gemm_plan(qpn):
 
 def test_forced_plans_reject_unknown_ids(qpn):
     v = ctypes.c_void_p
-    assert qpn.plan_ids() == list(range(1, 14))
-    for bad in (10 ** 6, -1, 14):
+    assert qpn.plan_ids() == list(range(1, 15))
+    for bad in (10 ** 6, -1, 15):
         with pytest.raises(qpn.QpnError):
             qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 16, 16, plan=bad)
         # the run entry point checks the plan before anything else

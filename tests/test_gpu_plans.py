@@ -8,7 +8,9 @@ FP8) and over a short K with 512 or more panels (four wavefronts); whole
 panels for a short K below 512 panels; five NVFP4 panels or two FP8 panels
 per workgroup above 2 (NVFP4) or 4 (FP8) rows (with twice the K splits the
 LDS budget forces when those still fit 256 workgroups); eight NVFP4 panels per
-workgroup for 2048 or more panels when they fill whole rounds of 256 CUs.
+workgroup for 2048 or more panels when they fill whole rounds of 256 CUs;
+one workgroup per CU with all its 8-16 panels (one wavefront each) when
+neither the eight- nor the five-panel workgroups fill 82% of their rounds.
 The plan fields reported through the C ABI are asserted first, so each case
 covers the branch it names.
 """
@@ -36,6 +38,8 @@ CASES = [
     ("fp8", 4100, 2048, 6, 4, 2, False, "two FP8 panels per workgroup"),
     ("nvfp4", 32768, 512, 2, 2, 8, False, "eight panels per workgroup, 2 rows"),
     ("nvfp4", 32768, 512, 8, 2, 8, False, "eight panels per workgroup, 8 rows"),
+    ("nvfp4", 49152, 256, 2, 1, 16, False, "sixteen panels per workgroup, 2 rows"),
+    ("nvfp4", 49152, 256, 8, 1, 16, False, "sixteen panels per workgroup, 8 rows"),
 ]
 
 
