@@ -810,7 +810,8 @@ int gemm_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, int plan, size_t 
   // take them instead of spreading panels thinner.  Each workgroup then
   // stages half the activation slice for the same weight bytes, and the
   // per-CU fetch is what sets the pace: 5120x17408 at M = 4 (S = 2 -> 4, 192
-  // -> 256 workgroups of five panels) went from 14.95 to 13.77 us.
+  // -> 256 workgroups of five panels) went from 14.95 to 13.77 us on one box
+  // and measured the same either way (14.7-15.1 us) on another.
   if (pl.placement == 0 && pl.panels_per_workgroup > 2 && S > 1 && groups * S < want &&
       groups * 2 * S <= 256 && (J + 2 * S - 1) / (2 * S) >= 2 * pl.waves_per_panel)
     S *= 2;
