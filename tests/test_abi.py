@@ -99,6 +99,24 @@ def test_gemm_plan(qpn):
     # 320 panels on 256 CUs: 256 whole panels plus the last 64 split four ways
     pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 5120, 17408)
     assert (pl.workgroups, pl.split_workgroups, pl.splits) == (512, 256, 4)
+    # the LDS budget splits 5120x17408 at M = 4 in two; twice that over
+    # 64 groups of five panels still fits one workgroup per CU: 4 splits, 256
+    pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 4, 5120, 17408)
+    assert (pl.workgroups, pl.panels_per_workgroup, pl.splits) == (256, 5, 4)
+    # 3072 panels: 615 five-panel (80% of 3 rounds) or 384 eight-panel
+    # workgroups (75% of 2) fill their rounds poorly; 256 of 12 panels each
+    for m in (2, 4, 8):
+        pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, 49152, 5120)
+        assert (pl.workgroups, pl.waves_per_panel, pl.panels_per_workgroup) == (256, 1, 16)
+    # 2176 panels (436 five-panel workgroups, 85%) keep the five-panel plan
+    pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 34816, 5120)
+    assert (pl.workgroups, pl.panels_per_workgroup) == (436, 5)
+    # FP8 at 3-4 rows over 384 panels and 80 k-steps: two panels per workgroup;
+    # at 1-2 rows, or with 1088 panels, one panel per workgroup
+    for m in (3, 4):
+        assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 6144, 5120).panels_per_workgroup == 2
+    assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 2, 6144, 5120).panels_per_workgroup == 1
+    assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 4, 17408, 5120).panels_per_workgroup == 1
     # the VALU-dot diagnostic plans repeat plans 2 and 1 with the other contraction
     auto = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
     for vd, base in ((11, 2), (12, 1)):
