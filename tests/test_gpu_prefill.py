@@ -58,7 +58,7 @@ def test_prefill_small(fmt, n, k):
         parity(host(_prefill_one_range(qpn, pw, xd)), y_ref, f"prefill {fmt} {n}x{k} m={m} one K range")
 
 
-@pytest.mark.parametrize("fmt,n,k,ppw,splits", [("nvfp4", 4100, 1280, 5, 1), ("nvfp4", 4100, 3328, 5, 2),
+@pytest.mark.parametrize("fmt,n,k,ppw,splits", [("nvfp4", 4100, 1280, 5, 1), ("nvfp4", 4100, 3328, 5, 4),
                                                ("fp8", 4100, 3328, 2, 2), ("nvfp4", 65536, 256, 8, 1)])
 def test_prefill_16_rows_multi_panel(fmt, n, k, ppw, splits):
     """9-16 rows through the skinny kernel's shared-slice plans (five and
