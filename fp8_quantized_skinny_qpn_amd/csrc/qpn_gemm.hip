@@ -703,7 +703,10 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
   const int64_t J = fmt == kFmtNvfp4 ? nv_ksteps_of(k) : f8_ksteps_of(k);
   const bool remainder = P >= 256 && P < 3 * 256 && P % 256 >= 16;
   const bool uneven = remainder && J >= 64;
-  const bool uneven_short = remainder && J < 64 && P >= 2 * 256;
+  // (and a remainder of a quarter round or more: 8704x5120 M=1, 544 panels,
+  // ran 8.2 us whole against 8.7-10.0 split; 9216x5120, 576 panels, 8.15
+  // split against 8.3 whole)
+  const bool uneven_short = remainder && J < 64 && P >= 2 * 256 && P % 256 >= 64;
   // fewer panels than CUs: one panel per workgroup at any m (the slice of a
   // few panels is cheap to stage, and sharing it costs parallelism):
   // 2048x2048 M=8 4.8 us against 7.7 us with five-panel workgroups,
@@ -716,6 +719,15 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
     if (m >= 2 && P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02)
       return 13;
     if (m <= 2) return uneven ? 4 : uneven_short ? 5 : 1;
+    // Up to 8 rows over 1-2 panels per CU whose whole activation slice fits
+    // the LDS budget: two panels per workgroup, four wavefronts each, six
+    // k-steps in flight
+    // (more workgroups and deeper prefetch than five-panel workgroups spread
+    // this thin): M=8 5120x4352 / 5120x5120 / 6144x5120 / 7168x5120 went from
+    // 8.41 / 9.13 / 9.16 / 10.18 to 8.08 / 8.45 / 8.51 / 8.55 us, M=4
+    // 6144x5120 from 8.22 to 7.60.  A slice that must be split (4352x8192
+    // M=8) took 13.2 against 10.2 us.
+    if (m <= 8 && P < 2 * 256 && J * x_step_bytes(fmt, m) <= kSliceBudget) return 3;
     return 2;
   }
   // FP8 at 3-4 rows over 1-3 panels per CU and a long K: two panels share

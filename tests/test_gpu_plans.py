@@ -4,9 +4,11 @@ it, against the oracle (every output element).
 The branches: one panel per workgroup below 256 panels at any m; the
 remainder split (256 to 767 panels with a remainder of 16 or more) over a
 long K (64 or more k-steps; eight wavefronts per panel for NVFP4, four for
-FP8) and over a short K with 512 or more panels (four wavefronts); whole
-panels for a short K below 512 panels; five NVFP4 panels or two FP8 panels
-per workgroup above 2 (NVFP4) or 4 (FP8) rows, and for FP8 at 3-4 rows
+FP8) and over a short K with 512 or more panels and a remainder of 64 or
+more (four wavefronts); whole panels for a short K otherwise; five NVFP4
+panels or two FP8 panels per workgroup above 2 (NVFP4) or 4 (FP8) rows,
+two NVFP4 panels up to 8 rows over fewer than 512 panels when the whole
+activation slice fits the LDS budget, and for FP8 at 3-4 rows
 with fewer than 768 panels and 64 or more k-steps (with twice the K splits the
 LDS budget forces when those still fit 256 workgroups); eight NVFP4 panels per
 workgroup for 2048 or more panels when they fill whole rounds of 256 CUs;
@@ -32,9 +34,11 @@ CASES = [
     ("nvfp4", 5120, 8192, 1, 8, 1, True, "remainder split, long K, NVFP4"),
     ("nvfp4", 5120, 8192, 2, 8, 1, True, "remainder split, long K, NVFP4, 2 rows"),
     ("fp8", 5120, 4096, 2, 4, 1, True, "remainder split, long K, FP8"),
-    ("nvfp4", 8704, 2048, 1, 4, 1, True, "remainder split, short K, >= 512 panels"),
+    ("nvfp4", 10240, 2048, 1, 4, 1, True, "remainder split, short K, >= 512 panels"),
+    ("nvfp4", 8704, 2048, 1, 4, 1, False, "whole panels, short K, remainder under a quarter round"),
     ("nvfp4", 5120, 2048, 1, 4, 1, False, "whole panels, short K, < 512 panels"),
-    ("nvfp4", 4100, 2048, 5, 3, 5, False, "five panels per workgroup"),
+    ("nvfp4", 8200, 2048, 5, 3, 5, False, "five panels per workgroup"),
+    ("nvfp4", 4100, 2048, 5, 4, 2, False, "two NVFP4 panels per workgroup, 1-2 panels per CU"),
     ("nvfp4", 4100, 10368, 4, 3, 5, False, "five panels per workgroup, LDS-forced K splits doubled"),
     ("fp8", 4100, 2048, 6, 4, 2, False, "two FP8 panels per workgroup"),
     ("fp8", 4100, 4096, 4, 4, 2, False, "two FP8 panels per workgroup, 4 rows, long K"),
