@@ -117,6 +117,18 @@ def test_gemm_plan(qpn):
         assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 6144, 5120).panels_per_workgroup == 2
     assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 2, 6144, 5120).panels_per_workgroup == 1
     assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 4, 17408, 5120).panels_per_workgroup == 1
+    # NVFP4 at 3-8 rows over fewer than 512 panels whose whole slice fits the
+    # LDS budget: two panels per workgroup; 4352x8192 at 8 rows would need a
+    # split slice and keeps five
+    for n, k in ((5120, 5120), (7168, 5120), (5120, 4352)):
+        for m in (4, 8):
+            assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, n, k).panels_per_workgroup == 2
+    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 4352, 8192).panels_per_workgroup == 5
+    # a short K splits the remainder panels only from a quarter round (64) on
+    pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 8704, 5120)          # 544 panels
+    assert pl.workgroups == pl.split_workgroups == 544
+    pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 9216, 5120)          # 576 panels
+    assert pl.workgroups > pl.split_workgroups
     # the VALU-dot diagnostic plans repeat plans 2 and 1 with the other contraction
     auto = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 17408, 5120)
     for vd, base in ((11, 2), (12, 1)):
