@@ -730,13 +730,24 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
     if (m <= 8 && P < 2 * 256 && J * x_step_bytes(fmt, m) <= kSliceBudget) return 3;
     return 2;
   }
-  // FP8 at 3-4 rows over 1-3 panels per CU and a long K: two panels share
-  // the staged slice (6144 / 5120 / 7168 x 5120 M=4: 9.05 / 8.72 / 9.66 us
-  // -> 8.77 / 8.51 / 9.22; 5120x17408 M=4: 25.2 -> 23.5); with 4.25 panels
-  // per CU (17408x5120) one panel per workgroup stays 5% faster
-  if (m > 2 && m <= 4 && P < 3 * 256 && J >= 64) return 3;
-  if (m <= 4) return uneven || uneven_short ? 5 : 1;
-  return 3;
+  // FP8 above 2 rows: two panels per workgroup over 1-2 panels per CU when
+  // the whole slice fits the LDS budget (6144 / 5120 / 7168 x 5120 M=4:
+  // 9.05 / 8.72 / 9.66 us with one panel per workgroup -> 8.77 / 8.51 /
+  // 9.22); otherwise the five-panel plan, or all of a CU's panels in one
+  // workgroup where those fill their rounds poorly, as for NVFP4.  Against
+  // one or two panels per workgroup at M = 4 / 8: 8704x5120 13.4 / 15.4 ->
+  // 11.2 / 12.3 us, 17408x5120 19.3 / 23.1 -> 17.6 / 18.6, 5120x17408 23.3 /
+  // 25.5 -> 20.2 / 20.9, 37984x5120 38.1 / 40.6 -> 32.4 / 34.0, 49152x5120
+  // 43.3 / 47.5 -> 39.9 / 41.1 (sixteen panels).
+  if (m <= 2) return uneven || uneven_short ? 5 : 1;
+  if (m <= 8) {
+    if (P < 2 * 256 && J * x_step_bytes(fmt, m) <= kSliceBudget) return 3;
+    if (P >= 8 * 256 && P <= 16 * 256 &&
+        std::max(round_fill((P + 7) / 8), round_fill((P + 4) / 5)) < 0.82)
+      return 14;
+    return 2;
+  }
+  return 3;  // 9-16 rows (prefill-sized calls with a 16-row tile)
 }
 
 bool gemm_plan_info(int id, GemmPlan* out) {

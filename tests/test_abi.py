@@ -111,12 +111,15 @@ def test_gemm_plan(qpn):
     # 2176 panels (436 five-panel workgroups, 85%) keep the five-panel plan
     pl = qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 8, 34816, 5120)
     assert (pl.workgroups, pl.panels_per_workgroup) == (436, 5)
-    # FP8 at 3-4 rows over 384 panels and 80 k-steps: two panels per workgroup;
-    # at 1-2 rows, or with 1088 panels, one panel per workgroup
-    for m in (3, 4):
+    # FP8 at 3-8 rows over 384 panels and 80 k-steps (slice fits): two panels
+    # per workgroup; at 1-2 rows one; with 1088 panels, or a slice that must
+    # be split (5120x17408), five; 3072 panels, sixteen
+    for m in (3, 4, 8):
         assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 6144, 5120).panels_per_workgroup == 2
+        assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 17408, 5120).panels_per_workgroup == 5
+        assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 5120, 17408).panels_per_workgroup == 5
+        assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 49152, 5120).panels_per_workgroup == 16
     assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 2, 6144, 5120).panels_per_workgroup == 1
-    assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 4, 17408, 5120).panels_per_workgroup == 1
     # NVFP4 at 3-8 rows over fewer than 512 panels whose whole slice fits the
     # LDS budget: two panels per workgroup; 4352x8192 at 8 rows would need a
     # split slice and keeps five

@@ -1,19 +1,22 @@
 """Every branch of the automatic launch-plan choice, on a shape that selects
 it, against the oracle (every output element).
 
-The branches: one panel per workgroup below 256 panels at any m; the
-remainder split (256 to 767 panels with a remainder of 16 or more) over a
-long K (64 or more k-steps; eight wavefronts per panel for NVFP4, four for
-FP8) and over a short K with 512 or more panels and a remainder of 64 or
-more (four wavefronts); whole panels for a short K otherwise; five NVFP4
-panels or two FP8 panels per workgroup above 2 (NVFP4) or 4 (FP8) rows,
-two NVFP4 panels up to 8 rows over fewer than 512 panels when the whole
-activation slice fits the LDS budget, and for FP8 at 3-4 rows
-with fewer than 768 panels and 64 or more k-steps (with twice the K splits the
-LDS budget forces when those still fit 256 workgroups); eight NVFP4 panels per
-workgroup for 2048 or more panels when they fill whole rounds of 256 CUs;
-one workgroup per CU with all its 8-16 panels (one wavefront each) when
-neither the eight- nor the five-panel workgroups fill 82% of their rounds.
+The branches, both formats unless named:
+- one panel per workgroup below 256 panels, at any m;
+- at 1-2 rows (up to 256-767 panels with a remainder of 16 or more): the
+  remainder split in K over a long K (64 or more k-steps; eight wavefronts
+  per panel for NVFP4, four for FP8), and over a short K with 512 or more
+  panels and a remainder of 64 or more (four wavefronts); whole panels for
+  a short K otherwise;
+- at 3-8 rows: two panels per workgroup over fewer than 512 panels when the
+  whole activation slice fits the LDS budget; else five panels per
+  workgroup (with twice the K splits the LDS budget forces when those still
+  fit 256 workgroups); eight NVFP4 panels per workgroup for 2048 or more
+  panels when they fill whole rounds of 256 CUs; one workgroup per CU with
+  all its 8-16 panels (one wavefront each) when neither the eight- nor the
+  five-panel workgroups fill 82% of their rounds;
+- NVFP4 at 2 rows: the eight- and sixteen-panel plans as at 3-8 rows;
+- FP8 at 9-16 rows (the 16-row prefill tile): two panels per workgroup.
 The plan fields reported through the C ABI are asserted first, so each case
 covers the branch it names.
 """
@@ -42,6 +45,8 @@ CASES = [
     ("nvfp4", 4100, 10368, 4, 3, 5, False, "five panels per workgroup, LDS-forced K splits doubled"),
     ("fp8", 4100, 2048, 6, 4, 2, False, "two FP8 panels per workgroup"),
     ("fp8", 4100, 4096, 4, 4, 2, False, "two FP8 panels per workgroup, 4 rows, long K"),
+    ("fp8", 8704, 1024, 8, 3, 5, False, "five FP8 panels per workgroup, 512 or more panels"),
+    ("fp8", 49152, 256, 4, 1, 16, False, "sixteen FP8 panels per workgroup"),
     ("nvfp4", 32768, 512, 2, 2, 8, False, "eight panels per workgroup, 2 rows"),
     ("nvfp4", 32768, 512, 8, 2, 8, False, "eight panels per workgroup, 8 rows"),
     ("nvfp4", 49152, 256, 2, 1, 16, False, "sixteen panels per workgroup, 2 rows"),
