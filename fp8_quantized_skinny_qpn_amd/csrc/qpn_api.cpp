@@ -169,7 +169,7 @@ int plan_query(int op, int plan, int m, int64_t n, int64_t k, PlanInfo* o) {
     if (plan != 0) return QPN_ERR_SHAPE;
     if (m < 0 || m > kMaxPrefillM) return QPN_ERR_SHAPE;
     if (!(fmt == kFmtNvfp4 ? nv_shape_ok(n, k) : f8_shape_ok(n, k))) return QPN_ERR_SHAPE;
-    if (m <= kPrefillSkinnyRows) {  // the skinny kernel (a 16-row tile above 8 rows)
+    if (prefill_on_skinny(fmt, m, n, k)) {  // the skinny kernel (a 16-row tile above 8 rows)
       GemmLaunch g;
       if (gemm_launch_for(fmt, m > 0 ? m : 1, n, k, 0, (size_t)-1, 0, &g) != kGemmLaunchOk)
         return QPN_ERR_SHAPE;
@@ -331,7 +331,7 @@ int prefill_entry(uint32_t fmt, const void* packed, const uint16_t* x, uint16_t*
   int rc = device_check();
   if (rc != QPN_OK) return rc;
   GemmArgs a{packed, x, y, m, n, k, nullptr, workspace, stream};
-  if (m <= kPrefillSkinnyRows) {
+  if (prefill_on_skinny(fmt, m, n, k)) {
     // the skinny kernel with a 16-row tile, when the workspace holds the K
     // splits it needs; otherwise the tiled kernel below (which runs with any)
     GemmLaunch g;

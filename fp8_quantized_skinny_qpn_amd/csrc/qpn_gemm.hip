@@ -739,15 +739,18 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
   // 11.2 / 12.3 us, 17408x5120 19.3 / 23.1 -> 17.6 / 18.6, 5120x17408 23.3 /
   // 25.5 -> 20.2 / 20.9, 37984x5120 38.1 / 40.6 -> 32.4 / 34.0, 49152x5120
   // 43.3 / 47.5 -> 39.9 / 41.1 (sixteen panels).
+  // At 9-16 rows (prefill-sized calls with a 16-row tile) two panels per
+  // workgroup stay best below 512 panels, whether or not the slice fits; from
+  // 512 the five- or sixteen-panel plans (M = 9 / 16: 17408x5120 29.2 / 33.3
+  // -> 23.0 / 24.9 us, 34816x5120 52.2 / 58.9 -> 42.1 / 45.7, 10240x17408
+  // 58.5 / 64.2 -> 46.0 / 49.1).
   if (m <= 2) return uneven || uneven_short ? 5 : 1;
-  if (m <= 8) {
-    if (P < 2 * 256 && J * x_step_bytes(fmt, m) <= kSliceBudget) return 3;
-    if (P >= 8 * 256 && P <= 16 * 256 &&
-        std::max(round_fill((P + 7) / 8), round_fill((P + 4) / 5)) < 0.82)
-      return 14;
-    return 2;
-  }
-  return 3;  // 9-16 rows (prefill-sized calls with a 16-row tile)
+  if (m <= 8 && P < 2 * 256 && J * x_step_bytes(fmt, m) <= kSliceBudget) return 3;
+  if (m > 8 && P < 2 * 256) return 3;
+  if (P >= 8 * 256 && P <= 16 * 256 &&
+      std::max(round_fill((P + 7) / 8), round_fill((P + 4) / 5)) < 0.82)
+    return 14;
+  return 2;
 }
 
 bool gemm_plan_info(int id, GemmPlan* out) {

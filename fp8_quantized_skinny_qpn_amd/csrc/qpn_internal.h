@@ -96,11 +96,11 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 // Prefill-sized activation blocks (9 <= m <= 256): one launch of the tiled
 // MFMA kernel, 128 output channels by 32 mt activation rows per workgroup up
 // to 128 rows, 256 channels by 128-row blocks above (and by 32 or 64 rows
-// for NVFP4 blocks of 17-64 rows when that fills half the CUs).
+// for NVFP4 blocks of up to 64 rows when that fills half the CUs).
 // Calls of up to kPrefillSkinnyRows rows run the skinny kernel instead, with
 // a 16-row activation tile that fills the MFMA's B operand exactly (the
-// weights stream once, as at m <= 8), unless the workspace given is too
-// small for the K splits its LDS budget needs.
+// weights stream once, as at m <= 8), where prefill_on_skinny says so and
+// the workspace given holds the K splits its LDS budget needs.
 constexpr int kMaxPrefillM = 256;
 constexpr int kPrefillSkinnyRows = 16;
 constexpr int64_t kPrefillWorkgroups = 256;  // one per CU of an MI355X
@@ -125,6 +125,9 @@ struct PrefillLaunch {
   size_t ws_needed;
 };
 int prefill_tiles(int m);
+// Whether a prefill-sized call of m <= kPrefillSkinnyRows rows runs the
+// skinny kernel (else the tiled one).  A pure function of its arguments.
+bool prefill_on_skinny(uint32_t fmt, int m, int64_t n, int64_t k);
 // A pure function of its arguments; fewer K splits when ws_bytes is short.
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out);

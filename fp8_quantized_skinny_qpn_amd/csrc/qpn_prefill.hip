@@ -21,8 +21,8 @@
 // feeds 2.  A CU pulls only ~25-30 GB/s from L2 and beyond on MI355X, so the
 // bytes a workgroup fetches per k-step set the pace, and the wide tile
 // fetches half the activation bytes per channel: it runs above 128 rows
-// (two row blocks from 129 rows) and, for NVFP4, from 17 to 64 rows when it
-// still gives half the CUs a workgroup (launch choice below).  The
+// (two row blocks from 129 rows) and, for NVFP4, up to 64 rows when it still
+// gives half the CUs a workgroup (launch choice below).  The
 // activation slice of a k-step reaches LDS through loads of whole 128-byte
 // lines, swizzled so that the MFMA operand reads are free of bank conflicts
 // (see issue_x).
@@ -662,8 +662,9 @@ int prefill_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : m <= 128 ? 4 : 8; 
 // whole tiles on 136 CUs, which lost to 256 equal ranges (45.4 against 50.9
 // us at 128 rows).
 //
-// The wide tile at 17-64 NVFP4 rows.  Fewer, larger tiles: taken when that
-// launch still has at least 128 workgroups.  A/B: 17408x5120 at 32 / 64 rows
+// The wide tile at up to 64 NVFP4 rows (from 9 rows where the call runs the
+// tiled kernel).  Fewer, larger tiles: taken when that launch still has at
+// least 128 workgroups.  A/B: 17408x5120 at 32 / 64 rows
 // 25.9 -> 22.2 / 34.8 -> 32.4 us; 5120x17408 at 64 rows 37.4 -> 37.0.  At
 // 5120x17408 and 32 rows it would have 60 workgroups (three pieces of each
 // of 20 tiles, the most its 32-row shares stage holds) and took 37 against
@@ -765,12 +766,34 @@ PfShape prefill_shape(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes
 
 }  // namespace
 
+// 9-16 rows: the skinny kernel stages a 16-row slice per workgroup and must
+// split K to fit it in LDS; the tiled kernel streams the slice through
+// stages and splits K only to fill the CUs.  The tiled kernel (a 32-row tile,
+// half of it zeros) measured faster on large calls, the skinny kernel on the
+// rest (M = 9 / 16, us, skinny -> tiled): NVFP4 25600x5120 24.9 / 28.3 ->
+// 22.3 / 22.9, 65536x5120 46.0 / 51.1 -> 41.2 / 37.4, 20480x17408 63.7 / 66.9
+// -> 52.8 / 51.3; FP8 5120x17408 33.0 / 36.1 -> 28.9 / 29.2, 10240x17408 46.0
+// / 49.1 -> 43.1 / 43.1, 65536x5120 74.1 / 79.5 -> 68.5 / 66.7; but NVFP4
+// 17408x5120 16.7 / 19.2 against 19.3 / 19.1, 5120x17408 19.0 / 21.3 against
+// 25.3 / 25.0, FP8 34816x5120 42.1 / 45.7 against 56.3 / 58.0.
+bool prefill_on_skinny(uint32_t fmt, int m, int64_t n, int64_t k) {
+  if (m > kPrefillSkinnyRows) return false;
+  if (m <= kMaxM) return true;
+  const int64_t P = panels_of(n);
+  if (fmt == kFmtNvfp4) {
+    const int64_t J = nv_ksteps_of(k);
+    return !(P >= 1536 || (P >= 1024 && J >= 64));
+  }
+  const int64_t J = f8_ksteps_of(k);
+  return !(J >= 128 || P >= 3072);
+}
+
 int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes,
                        PrefillLaunch* out) {
   PfShape sh = prefill_shape(fmt, m, n, k, ws_bytes, m > 128);
-  // NVFP4 blocks of 17 to 64 rows: the 256-channel tile when it still fills
+  // NVFP4 blocks of up to 64 rows: the 256-channel tile when it still fills
   // half the CUs or more
-  if (fmt == kFmtNvfp4 && m > kPrefillSkinnyRows && m <= 64) {
+  if (fmt == kFmtNvfp4 && m <= 64) {
     const PfShape w = prefill_shape(fmt, m, n, k, ws_bytes, true);
     if (w.G >= kPrefillWorkgroups / 2) sh = w;
   }

@@ -129,11 +129,12 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * split_workgroups, the workgroups that work on K ranges (split_workgroups
  * / splits panel groups of the last panels, dispatched first).  The other
  * workgroups - 0 unless the plan balances whole panels per CU - each take
- * panels_per_workgroup whole panels.  For the prefill ops above 16 rows a
- * workgroup covers either 8 panels (waves_per_panel 2: a wavefront per half
- * of the activation rows) or 16 panels (waves_per_panel 1; above 128 rows,
- * and for NVFP4 at 17-64 rows when that launch still has 128 workgroups or
- * more) by activation_rows = 32, 64 or 128 rows (the fewest that hold m, at
+ * panels_per_workgroup whole panels.  For the prefill ops on the tiled
+ * kernel (above 16 rows, and at 9-16 rows of large calls: see
+ * qpn_gemm_prefill_nvfp4) a workgroup covers either 8 panels
+ * (waves_per_panel 2: a wavefront per half of the activation rows) or 16
+ * panels (waves_per_panel 1; above 128 rows, and for NVFP4 up to 64 rows
+ * when that launch still has 128 workgroups or more) by activation_rows = 32, 64 or 128 rows (the fewest that hold m, at
  * most 128; more rows are further row blocks, as separate workgroups).  The
  * workgroups cut the (tile, k-step) pairs into contiguous ranges: equal
  * ones, or, where the partial tiles are summed in shares (128 rows or 16
@@ -231,7 +232,9 @@ QPN_API int qpn_gemm_fp8(const void *packed, const uint16_t *x, uint16_t *y, int
  * sum_k X[m, k] * W[n, k]), FP32 accumulation, weights decoded in registers,
  * no dequantised copy.  Up to 16 rows it runs the skinny kernel of
  * qpn_gemm_nvfp4 / qpn_gemm_fp8 with a 16-row activation tile (the weights
- * stream once); from 17 rows, or when the workspace given cannot hold the K
+ * stream once); from 17 rows, at 9-16 rows of large calls (NVFP4: 1536 or
+ * more 16-row panels, or 1024 or more with k > 8064; FP8: k > 8128, or
+ * 3072 or more panels), or when the workspace given cannot hold the K
  * splits the skinny kernel needs, a tiled MFMA kernel.  Both reach the same
  * parity bar.  x: [m, k] FP16, 16-byte aligned; y: [m, n] FP16.
  * workspace: zero-filled device memory, 16-byte aligned, of

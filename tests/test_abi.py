@@ -320,11 +320,22 @@ def test_prefill_queries(qpn):
                         (32, 5120, 17408), (64, 17408, 5120), (128, 5120, 17408), (128, 6144, 5120),
                         (128, 5120, 4096), (256, 17408, 5120), (256, 5120, 17408), (130, 200, 1024),
                         (1, 16, 64), (256, 6144, 5120), (256, 5120, 5120), (100, 40000, 1024),
-                        (32, 6144, 5120), (40, 300, 9008), (40, 300, 20000), (64, 5120, 4096)]:
+                        (32, 6144, 5120), (40, 300, 9008), (40, 300, 20000), (64, 5120, 4096),
+                        (16, 25600, 5120), (9, 20480, 17408), (12, 65536, 5120), (16, 16384, 1024),
+                        (16, 24576, 512), (9, 1024, 8192), (8, 65536, 5120), (16, 34816, 5120)]:
             pl = qpn.gemm_plan(op, m, n, k)
             ws = qpn.workspace_bytes(op, m, n, k)
-            if m <= 16:
-                # up to 16 rows run the skinny kernel (a 16-row tile above 8 rows)
+            P = -(-n // 16)
+            if op == qpn.OP_PREFILL_NVFP4:
+                J = -(-k // 128)
+                tiled = P >= 1536 or (P >= 1024 and J >= 64)
+            else:
+                J = -(-k // 64)
+                tiled = J >= 128 or P >= 3072
+            if m <= 8 or (m <= 16 and not tiled):
+                # the skinny kernel (a 16-row tile above 8 rows): up to 8 rows,
+                # and at 9-16 rows unless the call is large (many panels, or a
+                # long K: with 1024 or more panels for NVFP4)
                 assert pl.activation_rows in (1, 2, 4, 8, 16)
                 assert m <= pl.activation_rows < 2 * max(m, 1)
                 assert pl.split_workgroups % pl.splits == 0 and pl.split_workgroups <= pl.workgroups
@@ -364,7 +375,7 @@ def test_prefill_queries(qpn):
                 return chans, tiles, G, pieces_of(G)
             wide = m > 128
             if op == qpn.OP_PREFILL_NVFP4 and m <= 64 and launch(True)[2] >= 128:
-                wide = True   # 17-64 NVFP4 rows: 256 channels when that still fills half the CUs
+                wide = True   # up to 64 NVFP4 rows: 256 channels when that still fills half the CUs
             chans, tiles, G, pieces = launch(wide)
             assert (pl.waves_per_panel, pl.panels_per_workgroup) == ((1, 16) if wide else (2, 8))
             assert pl.activation_rows == rows
@@ -392,6 +403,22 @@ def test_prefill_queries(qpn):
     # FP8 5120x5120 at 64 rows: 40 tiles in four whole pieces of 1280 K
     pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, 64, 5120, 5120)
     assert (pl.workgroups, pl.splits) == (160, 4)
+    # 9-16 rows: the skinny kernel on the decoder shapes, the tiled one on
+    # large calls
+    for m in (9, 16):
+        assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, 17408, 5120).activation_rows == 16
+        assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, 5120, 17408).activation_rows == 16
+        pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, 25600, 5120)
+        assert (pl.activation_rows, pl.panels_per_workgroup) == (32, 16)
+        assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, m, 20480, 17408).activation_rows == 32
+        assert qpn.gemm_plan(qpn.OP_PREFILL_FP8, m, 5120, 17408).activation_rows == 32
+        assert qpn.gemm_plan(qpn.OP_PREFILL_FP8, m, 65536, 5120).activation_rows == 32
+        # FP8 on the skinny kernel: two panels per workgroup below 512
+        # panels, five from 512
+        pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, m, 6144, 5120)
+        assert (pl.activation_rows, pl.panels_per_workgroup) == (16, 2)
+        pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, m, 34816, 5120)
+        assert (pl.activation_rows, pl.panels_per_workgroup) == (16, 5)
 
 
 def test_prefill_argument_errors(qpn):

@@ -1,8 +1,9 @@
 """Prefill-sized activation blocks (9 <= m <= 256) against the oracle.
 
 Up to 16 rows the call runs the skinny kernel with a 16-row activation tile
-(the tiled kernel when no workspace is given and K needs splitting); from 17
-rows the tiled MFMA kernel.  Both paths are covered below.
+(the tiled kernel for large calls at 9-16 rows, and when no workspace is
+given and K needs splitting); from 17 rows the tiled MFMA kernel.  Both
+paths are covered below.
 
 The same parity bar as the skinny GEMM: per element |err| <= 1e-2 rms(ref)
 + 1e-3 and relative Frobenius error <= 2e-3 against the FP64 oracle product
@@ -59,10 +60,11 @@ def test_prefill_small(fmt, n, k):
 
 
 @pytest.mark.parametrize("fmt,n,k,ppw,splits", [("nvfp4", 4100, 1280, 5, 1), ("nvfp4", 4100, 3328, 5, 4),
-                                               ("fp8", 4100, 3328, 2, 2), ("nvfp4", 65536, 256, 8, 1)])
+                                               ("fp8", 4100, 3328, 2, 2), ("fp8", 8704, 1024, 5, 1),
+                                               ("fp8", 48000, 256, 16, 1)])
 def test_prefill_16_rows_multi_panel(fmt, n, k, ppw, splits):
-    """9-16 rows through the skinny kernel's shared-slice plans (five and
-    eight NVFP4 panels or two FP8 panels per workgroup, the 16-row staging
+    """9-16 rows through the skinny kernel's shared-slice plans (five NVFP4
+    panels; two, five or sixteen FP8 panels per workgroup; the 16-row staging
     order, with and without K splits), ragged N, every output checked."""
     qpn = need_gpu()
     w = synth.weights(n, k, seed=n + 3 * k)
@@ -93,6 +95,24 @@ def test_prefill_full_size_sampled(fmt, n, k):
         parity(y[:, rows], ref(x[:m], rows), f"prefill full {fmt} {n}x{k} m={m}")
     y = host(_prefill_one_range(qpn, pw, dev(x[:128])))
     parity(y[:, rows], ref(x[:128], rows), f"prefill full {fmt} {n}x{k} m=128 one K range")
+
+
+@pytest.mark.parametrize("fmt,n,k,ppw", [("nvfp4", 24576, 1024, 16), ("fp8", 1000, 8192, 8)])
+def test_prefill_9_16_rows_tiled(fmt, n, k, ppw):
+    """9-16 rows of a large call (NVFP4 with 1536 or more panels, FP8 with
+    128 or more k-steps of 64) on the tiled kernel, a 32-row tile half of which
+    reads zero rows: the 256-channel tile for NVFP4, the 128-channel tile
+    for FP8 (ragged N), every output checked."""
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=n + 5 * k)
+    x = synth.activations(16, k, seed=n + 5 * k, m_max=16)
+    pw, ref = _pack(qpn, fmt, w)
+    op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+    for m in (9, 12, 16):
+        pl = qpn.gemm_plan(op, m, n, k)
+        assert (pl.activation_rows, pl.panels_per_workgroup) == (32, ppw), (m, pl)
+        log(f"prefill tiled {fmt} {n}x{k} m={m}: {pl.workgroups} workgroups, {pl.splits} per tile")
+        parity(host(qpn.prefill(pw, dev(x[:m]))), ref(x[:m]), f"prefill tiled {fmt} {n}x{k} m={m}")
 
 
 def test_prefill_wide_tile_small_blocks():
