@@ -61,7 +61,7 @@ def test_prefill_small(fmt, n, k):
 
 @pytest.mark.parametrize("fmt,n,k,ppw,splits", [("nvfp4", 4100, 1280, 5, 1), ("nvfp4", 4100, 3328, 5, 4),
                                                ("fp8", 4100, 3328, 2, 2), ("fp8", 8704, 1024, 5, 1),
-                                               ("fp8", 48000, 256, 16, 1)])
+                                               ("fp8", 8200, 3328, 5, 2), ("fp8", 48000, 256, 16, 1)])
 def test_prefill_16_rows_multi_panel(fmt, n, k, ppw, splits):
     """9-16 rows through the skinny kernel's shared-slice plans (five NVFP4
     panels; two, five or sixteen FP8 panels per workgroup; the 16-row staging
