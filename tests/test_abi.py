@@ -322,7 +322,9 @@ def test_prefill_queries(qpn):
                         (1, 16, 64), (256, 6144, 5120), (256, 5120, 5120), (100, 40000, 1024),
                         (32, 6144, 5120), (40, 300, 9008), (40, 300, 20000), (64, 5120, 4096),
                         (16, 25600, 5120), (9, 20480, 17408), (12, 65536, 5120), (16, 16384, 1024),
-                        (16, 24576, 512), (9, 1024, 8192), (8, 65536, 5120), (16, 34816, 5120)]:
+                        (16, 24576, 512), (9, 1024, 8192), (8, 65536, 5120), (16, 34816, 5120),
+                        (128, 34816, 5120), (256, 34816, 5120), (128, 151936, 5120), (32, 33000, 1024),
+                        (100, 33000, 512), (200, 102400, 64), (128, 65536, 5120)]:
             pl = qpn.gemm_plan(op, m, n, k)
             ws = qpn.workspace_bytes(op, m, n, k)
             P = -(-n // 16)
@@ -357,8 +359,12 @@ def test_prefill_queries(qpn):
                     return max(owner(t * J + J - 1) - owner(t * J) + 1 for t in range(tiles)) if g != tiles else 1
                 # stream-K: the (tile, k-step) units cut into equal contiguous
                 # ranges, one per workgroup, at least 512 of K each, up to 256
-                # workgroups; from 256 tiles on, whole tiles
+                # workgroups; from 256 tiles on, whole tiles, unless their
+                # rounds of 256 are less than 85% full: then one round of 256
                 G = tiles if (J == 0 or tiles >= 256) else max(tiles, min(256, U // (512 // ks)))
+                rounds = -(-tiles // 256)
+                if J > 0 and tiles > 256 and tiles % 256 and U // 256 >= 512 // ks and tiles < 0.85 * 256 * rounds:
+                    G = 256
                 shares = False
                 if J > 0 and tiles < 256:
                     # tiles summed in shares go through 1 KiB-per-contributor LDS
@@ -403,6 +409,15 @@ def test_prefill_queries(qpn):
     # FP8 5120x5120 at 64 rows: 40 tiles in four whole pieces of 1280 K
     pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, 64, 5120, 5120)
     assert (pl.workgroups, pl.splits) == (160, 4)
+    # more tiles than CUs: 34816x5120 at 128 rows (272 tiles) in one round of
+    # 256 equal ranges; 151936x5120 (1187 tiles, rounds 93% full) and
+    # 65536x5120 (512) in whole tiles
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 34816, 5120)
+    assert (pl.workgroups, pl.splits) == (256, 2)
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 151936, 5120)
+    assert (pl.workgroups, pl.splits) == (1187, 1)
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 65536, 5120)
+    assert (pl.workgroups, pl.splits) == (512, 1)
     # 9-16 rows: the skinny kernel on the decoder shapes, the tiled one on
     # large calls
     for m in (9, 16):

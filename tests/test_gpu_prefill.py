@@ -115,6 +115,28 @@ def test_prefill_9_16_rows_tiled(fmt, n, k, ppw):
         parity(host(qpn.prefill(pw, dev(x[:m]))), ref(x[:m]), f"prefill tiled {fmt} {n}x{k} m={m}")
 
 
+@pytest.mark.parametrize("fmt,n,k,m", [("fp8", 33000, 1024, 32), ("nvfp4", 33000, 512, 100)])
+def test_prefill_many_tiles_one_round(fmt, n, k, m):
+    """More output tiles than CUs (258) whose whole-tile rounds would be half
+    empty: one round of 256 equal ranges, every tile but a few cut between
+    two workgroups and summed up the pairwise tree; 1024 sampled output
+    channels (the last included) against the oracle, and the call without a
+    workspace (whole tiles) as well."""
+    qpn = need_gpu()
+    w = synth.weights(n, k, seed=n + 7 * k)
+    x = synth.activations(m, k, seed=n + 7 * k, m_max=m)
+    pw, ref = _pack(qpn, fmt, w)
+    op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+    pl = qpn.gemm_plan(op, m, n, k)
+    assert (pl.workgroups, pl.splits, pl.panels_per_workgroup) == (256, 2, 8), pl
+    rows = np.sort(np.concatenate([np.random.default_rng(n).choice(n - 1, 1023, replace=False), [n - 1]]))
+    y_ref = ref(x, rows)
+    log(f"prefill many tiles {fmt} {n}x{k} m={m}")
+    parity(host(qpn.prefill(pw, dev(x)))[:, rows], y_ref, f"prefill many tiles {fmt} {n}x{k} m={m}")
+    parity(host(_prefill_one_range(qpn, pw, dev(x)))[:, rows], y_ref,
+           f"prefill many tiles {fmt} {n}x{k} m={m} whole tiles")
+
+
 def test_prefill_wide_tile_small_blocks():
     """17-64 NVFP4 rows on the 256-channel tile (32- and 64-row tiles, taken
     when the call still fills half the CUs): ragged N (33 blocks, the last

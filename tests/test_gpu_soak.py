@@ -7,7 +7,8 @@ whose automatic plans split K 2, 3, 4, 5, 6, 7, 10, 13 and 18 ways; the
 balanced hybrid launches (whole panels plus a K-split remainder, four and
 six splits); lm_head calls with split K; the 16-row skinny prefill tile and
 the tiled prefill kernel with tiles cut between workgroups (narrow and
-wide tiles, summed up the pairwise tree and in shares); and the no-allocation GEMM on the
+wide tiles, summed up the pairwise tree and in shares, and more tiles than
+CUs in one round of 256 ranges); and the no-allocation GEMM on the
 library's own scratch.  Every 40 calls the outputs are compared bit for bit
 with the first result of their call, stopping at the first mismatch.  The
 first result of each call is checked against the oracle on sampled rows, and
@@ -39,6 +40,7 @@ CASES = [
     ("prefill", "nvfp4", 16, 300, 9008, 7), ("prefill", "fp8", 9, 300, 4096, 7),
     ("prefill", "nvfp4", 40, 300, 9008, 8), ("prefill", "nvfp4", 200, 1500, 4096, 4),
     ("prefill", "fp8", 128, 1000, 6144, 6), ("prefill", "fp8", 40, 300, 20000, 39),
+    ("prefill", "fp8", 32, 33000, 1024, 2),
     ("noalloc", "nvfp4", 8, 300, 8192, 7),
 ]
 
