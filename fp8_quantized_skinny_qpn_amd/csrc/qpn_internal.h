@@ -96,7 +96,8 @@ hipError_t launch_argmax_finalize(uint64_t* keys, int m, int32_t* argmax, const 
 // Prefill-sized activation blocks (9 <= m <= 256): one launch of the tiled
 // MFMA kernel, 128 output channels by 32 mt activation rows per workgroup up
 // to 128 rows, 256 channels by 128-row blocks above (and by 32 or 64 rows
-// for NVFP4 blocks of up to 64 rows when that fills half the CUs).
+// for NVFP4 blocks of up to 64 rows when that fills half the CUs, and by
+// 128 rows at 65-128 rows of large calls).
 // Calls of up to kPrefillSkinnyRows rows run the skinny kernel instead, with
 // a 16-row activation tile that fills the MFMA's B operand exactly (the
 // weights stream once, as at m <= 8), where prefill_on_skinny says so and

@@ -21,8 +21,9 @@
 // feeds 2.  A CU pulls only ~25-30 GB/s from L2 and beyond on MI355X, so the
 // bytes a workgroup fetches per k-step set the pace, and the wide tile
 // fetches half the activation bytes per channel: it runs above 128 rows
-// (two row blocks from 129 rows) and, for NVFP4, up to 64 rows when it still
-// gives half the CUs a workgroup (launch choice below).  The
+// (two row blocks from 129 rows), at 65-128 rows on large calls and, for
+// NVFP4, up to 64 rows when it still gives half the CUs a workgroup (launch
+// choice below).  The
 // activation slice of a k-step reaches LDS through loads of whole 128-byte
 // lines, swizzled so that the MFMA operand reads are free of bank conflicts
 // (see issue_x).
@@ -803,10 +804,19 @@ int prefill_launch_for(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_byte
                        PrefillLaunch* out) {
   PfShape sh = prefill_shape(fmt, m, n, k, ws_bytes, m > 128);
   // NVFP4 blocks of up to 64 rows: the 256-channel tile when it still fills
-  // half the CUs or more
+  // half the CUs or more.  65-128 rows: the 256-channel tile when there are
+  // more than 128 tiles of 128 channels and it still gives three quarters of
+  // the CUs a workgroup (half the activation fetches per channel):
+  // 37984x5120 at 128 rows 86 -> 78 us, 49152x5120 99 -> 87, 65536x5120 125
+  // -> 106, 151936x5120 279 -> 231, 20480x17408 134 -> 125, FP8 34816x5120
+  // at 80 / 128 rows 74 / 72 -> 70 / 68; with fewer tiles it lost
+  // (5120x17408 45.7 against 43.5 us), and at 136 tiles (17408x5120) it ties.
   if (fmt == kFmtNvfp4 && m <= 64) {
     const PfShape w = prefill_shape(fmt, m, n, k, ws_bytes, true);
     if (w.G >= kPrefillWorkgroups / 2) sh = w;
+  } else if (m > 64 && m <= 128 && sh.tiles > kPrefillWorkgroups / 2) {
+    const PfShape w = prefill_shape(fmt, m, n, k, ws_bytes, true);
+    if (w.G >= 3 * kPrefillWorkgroups / 4) sh = w;
   }
   // the partial area is addressed with 32-bit offsets
   if (sh.need >= ((size_t)1 << 31)) return kGemmNoWorkspace;

@@ -133,8 +133,10 @@ QPN_API size_t qpn_workspace_bytes(int op, int m, int64_t n, int64_t k);
  * kernel (above 16 rows, and at 9-16 rows of large calls: see
  * qpn_gemm_prefill_nvfp4) a workgroup covers either 8 panels
  * (waves_per_panel 2: a wavefront per half of the activation rows) or 16
- * panels (waves_per_panel 1; above 128 rows, and for NVFP4 up to 64 rows
- * when that launch still has 128 workgroups or more) by activation_rows = 32, 64 or 128 rows (the fewest that hold m, at
+ * panels (waves_per_panel 1; above 128 rows; at 65-128 rows when there
+ * are more than 128 tiles of 128 channels and the 256-channel launch has
+ * 192 workgroups or more; and for NVFP4 up to 64 rows when that launch
+ * still has 128 workgroups or more) by activation_rows = 32, 64 or 128 rows (the fewest that hold m, at
  * most 128; more rows are further row blocks, as separate workgroups).  The
  * workgroups cut the (tile, k-step) pairs into contiguous ranges: equal
  * ones, or, where the partial tiles are summed in shares (128 rows or 16

@@ -324,7 +324,8 @@ def test_prefill_queries(qpn):
                         (16, 25600, 5120), (9, 20480, 17408), (12, 65536, 5120), (16, 16384, 1024),
                         (16, 24576, 512), (9, 1024, 8192), (8, 65536, 5120), (16, 34816, 5120),
                         (128, 34816, 5120), (256, 34816, 5120), (128, 151936, 5120), (32, 33000, 1024),
-                        (100, 33000, 512), (200, 102400, 64), (128, 65536, 5120)]:
+                        (100, 33000, 512), (200, 102400, 64), (128, 65536, 5120), (80, 16400, 1024),
+                        (128, 16384, 1024), (100, 37984, 5120)]:
             pl = qpn.gemm_plan(op, m, n, k)
             ws = qpn.workspace_bytes(op, m, n, k)
             P = -(-n // 16)
@@ -382,6 +383,8 @@ def test_prefill_queries(qpn):
             wide = m > 128
             if op == qpn.OP_PREFILL_NVFP4 and m <= 64 and launch(True)[2] >= 128:
                 wide = True   # up to 64 NVFP4 rows: 256 channels when that still fills half the CUs
+            if 64 < m <= 128 and launch(False)[1] > 128 and launch(True)[2] >= 192:
+                wide = True   # 65-128 rows: 256 channels with more than 128 narrow tiles, on 192+ workgroups
             chans, tiles, G, pieces = launch(wide)
             assert (pl.waves_per_panel, pl.panels_per_workgroup) == ((1, 16) if wide else (2, 8))
             assert pl.activation_rows == rows
@@ -409,15 +412,23 @@ def test_prefill_queries(qpn):
     # FP8 5120x5120 at 64 rows: 40 tiles in four whole pieces of 1280 K
     pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, 64, 5120, 5120)
     assert (pl.workgroups, pl.splits) == (160, 4)
-    # more tiles than CUs: 34816x5120 at 128 rows (272 tiles) in one round of
-    # 256 equal ranges; 151936x5120 (1187 tiles, rounds 93% full) and
-    # 65536x5120 (512) in whole tiles
-    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 34816, 5120)
+    # more tiles than CUs: 34816x5120 at 256 rows (272 tiles) in one round of
+    # 256 equal ranges; 151936x5120 at 256 rows (1188 tiles, rounds 93% full)
+    # in whole tiles
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 34816, 5120)
     assert (pl.workgroups, pl.splits) == (256, 2)
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 256, 151936, 5120)
+    assert (pl.workgroups, pl.splits) == (1188, 1)
+    # 65-128 rows with more than 128 narrow tiles: the 256-channel tile
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 34816, 5120)
+    assert (pl.panels_per_workgroup, pl.workgroups, pl.splits) == (16, 256, 3)
+    assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 17408, 5120).panels_per_workgroup == 16
+    assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 5120, 17408).panels_per_workgroup == 8
+    assert qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 16400, 1024).panels_per_workgroup == 8  # 130 wide workgroups
     pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 151936, 5120)
-    assert (pl.workgroups, pl.splits) == (1187, 1)
+    assert (pl.panels_per_workgroup, pl.workgroups, pl.splits) == (16, 256, 2)
     pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 128, 65536, 5120)
-    assert (pl.workgroups, pl.splits) == (512, 1)
+    assert (pl.panels_per_workgroup, pl.workgroups, pl.splits) == (16, 256, 1)
     # 9-16 rows: the skinny kernel on the decoder shapes, the tiled one on
     # large calls
     for m in (9, 16):

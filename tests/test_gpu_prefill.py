@@ -137,6 +137,27 @@ def test_prefill_many_tiles_one_round(fmt, n, k, m):
            f"prefill many tiles {fmt} {n}x{k} m={m} whole tiles")
 
 
+@pytest.mark.parametrize("fmt,m", [("nvfp4", 100), ("fp8", 80)])
+def test_prefill_wide_tile_65_128_rows(fmt, m):
+    """65-128 rows of a call with more than 128 tiles of 128 channels on the
+    256-channel tile (129 tiles of one 128-row block, equal ranges over 256
+    workgroups, ragged N and M): 1024 sampled output channels, the last
+    included, against the oracle, with and without a workspace."""
+    qpn = need_gpu()
+    n, k = 33000, 1024
+    w = synth.weights(n, k, seed=n + m)
+    x = synth.activations(m, k, seed=n + m, m_max=m)
+    pw, ref = _pack(qpn, fmt, w)
+    op = qpn.OP_PREFILL_NVFP4 if fmt == "nvfp4" else qpn.OP_PREFILL_FP8
+    pl = qpn.gemm_plan(op, m, n, k)
+    assert (pl.panels_per_workgroup, pl.activation_rows, pl.workgroups) == (16, 128, 256), pl
+    rows = np.sort(np.concatenate([np.random.default_rng(m).choice(n - 1, 1023, replace=False), [n - 1]]))
+    y_ref = ref(x, rows)
+    log(f"prefill wide 65-128 {fmt} {n}x{k} m={m}: {pl.splits} per tile")
+    parity(host(qpn.prefill(pw, dev(x)))[:, rows], y_ref, f"prefill wide {fmt} {n}x{k} m={m}")
+    parity(host(_prefill_one_range(qpn, pw, dev(x)))[:, rows], y_ref, f"prefill wide {fmt} {n}x{k} m={m} one K range")
+
+
 def test_prefill_wide_tile_small_blocks():
     """17-64 NVFP4 rows on the 256-channel tile (32- and 64-row tiles, taken
     when the call still fills half the CUs): ragged N (33 blocks, the last
