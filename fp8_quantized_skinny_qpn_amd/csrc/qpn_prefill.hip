@@ -741,7 +741,15 @@ PfShape prefill_shape(uint32_t fmt, int m, int64_t n, int64_t k, size_t ws_bytes
     // straddles two tiles leaves two partial tiles to write and sum and
     // restarts the pipeline.  Unless that leaves pieces longer than
     // kPrefillMaxPieceK of K: then equal ranges over all the CUs.
-    const int64_t c = std::min<int64_t>(std::min<int64_t>(target / tiles, stage_kib),
+    // 32-row tiles of 128 channels take at most three pieces, summed up the
+    // pairwise tree (their small partial tiles make the fix-up latency-bound,
+    // and fewer pieces mean fewer round trips): FP8 7168x5120 at 20 / 32 rows
+    // 19.3 / 19.8 -> 17.8 / 18.1 us, 6144x5120 18.2 / 18.9 -> 17.0 / 18.1,
+    // 5120x4096 at 32 rows 17.1 -> 15.8; NVFP4 5120x4096 and 6144x5120 at 32
+    // rows 15.0 / 17.0 -> 13.6 / 15.8.  Two pieces lost (FP8 6144x5120 at 32
+    // rows 20.4 us), and at 33-64 rows the cap made no difference or lost.
+    const int64_t cmax = !wide && mt == 1 ? std::min<int64_t>(stage_kib, 3) : stage_kib;
+    const int64_t c = std::min<int64_t>(std::min<int64_t>(target / tiles, cmax),
                                         std::max<int64_t>(1, J * ks / kPrefillPieceK));
     if (c >= 2 && J * ks <= c * kPrefillMaxPieceK) {
       G = tiles * c;

@@ -379,7 +379,9 @@ def test_prefill_queries(qpn):
                     waves = 4 if (op == qpn.OP_PREFILL_FP8 and not wide and rows == 32) else 8
                     stage_kib = (4 if op == qpn.OP_PREFILL_NVFP4 else 2) * rows // 16 // (waves // 4)
                     # whole pieces: a multiple of the tiles, each piece 1024 to 4096 of K
-                    c = min(256 // tiles, stage_kib, max(1, J * ks // 1024))
+                    # (32-row tiles of 128 channels: at most three pieces)
+                    c = min(256 // tiles, stage_kib if wide or rows > 32 else min(stage_kib, 3),
+                            max(1, J * ks // 1024))
                     if c >= 2 and J * ks <= c * 4096:
                         G, shares = tiles * c, True
                     elif (wide or rows == 128) and pieces_of(G) > stage_kib:
@@ -414,6 +416,9 @@ def test_prefill_queries(qpn):
     # whole pieces of 4352 K each are too long: equal ranges over 256 workgroups
     pl = qpn.gemm_plan(qpn.OP_PREFILL_NVFP4, 32, 5120, 17408)
     assert (pl.workgroups, pl.panels_per_workgroup) == (256, 8)
+    # FP8 7168x5120 at 32 rows: 56 tiles of 32 rows in three whole pieces
+    pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, 32, 7168, 5120)
+    assert (pl.workgroups, pl.splits) == (168, 3)
     # FP8 5120x5120 at 64 rows: 40 tiles in four whole pieces of 1280 K
     pl = qpn.gemm_plan(qpn.OP_PREFILL_FP8, 64, 5120, 5120)
     assert (pl.workgroups, pl.splits) == (160, 4)
