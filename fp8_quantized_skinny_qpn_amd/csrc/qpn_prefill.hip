@@ -40,8 +40,10 @@
 //
 // Work split (stream-K).  The (tile, k-step) pairs are cut into contiguous
 // ranges, one per workgroup (up to 256, one per CU, when the tiles are
-// fewer), so every CU streams about the same bytes in a single wave.  A
-// workgroup runs its range as pieces, one per tile it touches.  The partial
+// fewer, and 256 when whole tiles would leave their last round of 256 part
+// empty), so every CU streams about the same bytes in a single wave.  A
+// workgroup runs its range as pieces, one per tile it touches; where the
+// ranges can be whole pieces of one tile each, they are.  The partial
 // tiles of a tile cut between workgroups are summed deterministically, up
 // a fixed pairwise tree or in shares (see the kernel).
 #include <algorithm>
