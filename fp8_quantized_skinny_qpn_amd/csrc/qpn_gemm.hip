@@ -721,11 +721,6 @@ int gemm_auto_plan(uint32_t fmt, int m, int64_t n, int64_t k) {
       return 14;
     if (m >= 2 && P >= 8 * 256 && round_fill((P + 7) / 8) >= round_fill((P + 4) / 5) - 0.02)
       return 13;
-    // At 2 rows with 768 or more panels, five-panel workgroups that fill
-    // their rounds of 256 CUs to 80% or more: 17408x5120 11.73 -> 11.19 us,
-    // 34816x5120 19.35 -> 18.73, 37984x5120 20.78 -> 19.64 (at 1 row they
-    // tie or lose; with rounds 60% full, 25600x5120 and 12288x5120, they lose)
-    if (m == 2 && P >= 3 * 256 && round_fill((P + 4) / 5) >= 0.8) return 2;
     if (m <= 2) return uneven ? 4 : uneven_short ? 5 : 1;
     // Up to 8 rows over 1-2 panels per CU whose whole activation slice fits
     // the LDS budget: two panels per workgroup, four wavefronts each, six

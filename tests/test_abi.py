@@ -120,11 +120,10 @@ def test_gemm_plan(qpn):
         assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 5120, 17408).panels_per_workgroup == 5
         assert qpn.gemm_plan(qpn.OP_GEMM_FP8, m, 49152, 5120).panels_per_workgroup == 16
     assert qpn.gemm_plan(qpn.OP_GEMM_FP8, 2, 6144, 5120).panels_per_workgroup == 1
-    # NVFP4 at 2 rows: five panels per workgroup where they fill 80% of their
-    # rounds (17408x5120: 218 of 256), one panel otherwise (25600x5120: 320 of 512)
-    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 2, 17408, 5120).panels_per_workgroup == 5
-    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 2, 25600, 5120).panels_per_workgroup == 1
-    assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, 1, 17408, 5120).panels_per_workgroup == 1
+    # NVFP4 at 1-2 rows over 768 or more panels: one panel per workgroup
+    for m in (1, 2):
+        assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, 17408, 5120).panels_per_workgroup == 1
+        assert qpn.gemm_plan(qpn.OP_GEMM_NVFP4, m, 37984, 5120).panels_per_workgroup == 1
     # NVFP4 at 3-8 rows over fewer than 512 panels whose whole slice fits the
     # LDS budget: two panels per workgroup; 4352x8192 at 8 rows would need a
     # split slice and keeps five

@@ -15,9 +15,7 @@ The branches, both formats unless named:
   panels when they fill whole rounds of 256 CUs; one workgroup per CU with
   all its 8-16 panels (one wavefront each) when neither the eight- nor the
   five-panel workgroups fill 82% of their rounds;
-- NVFP4 at 2 rows: the eight- and sixteen-panel plans as at 3-8 rows, and
-  five panels per workgroup from 768 panels when those workgroups fill
-  their rounds of 256 CUs to 80% or more;
+- NVFP4 at 2 rows: the eight- and sixteen-panel plans as at 3-8 rows;
 - FP8 at 9-16 rows (the 16-row prefill tile): two panels per workgroup.
 The plan fields reported through the C ABI are asserted first, so each case
 covers the branch it names.
@@ -49,7 +47,7 @@ CASES = [
     ("fp8", 4100, 4096, 4, 4, 2, False, "two FP8 panels per workgroup, 4 rows, long K"),
     ("fp8", 8704, 1024, 8, 3, 5, False, "five FP8 panels per workgroup, 512 or more panels"),
     ("fp8", 49152, 256, 4, 1, 16, False, "sixteen FP8 panels per workgroup"),
-    ("nvfp4", 17400, 512, 2, 3, 5, False, "five panels per workgroup, 2 rows, rounds 80% full or more"),
+    ("nvfp4", 17400, 512, 2, 4, 1, False, "one panel per workgroup, 2 rows, 768 or more panels"),
     ("nvfp4", 32768, 512, 2, 2, 8, False, "eight panels per workgroup, 2 rows"),
     ("nvfp4", 32768, 512, 8, 2, 8, False, "eight panels per workgroup, 8 rows"),
     ("nvfp4", 49152, 256, 2, 1, 16, False, "sixteen panels per workgroup, 2 rows"),
